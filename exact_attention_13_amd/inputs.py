@@ -1,0 +1,102 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the smoke check.
+
+This module holds no attention arithmetic: it only draws random numbers and
+rounds them to the storage dtype.  Both the GPU library's callers and the CPU
+oracle's callers take their inputs from here, so the two sides see the same
+bits.
+
+Recipe (one per workload, all tensors contiguous [B, H, N, d]):
+  * ``numpy.random.default_rng(seed)`` (PCG64), drawn in the order Q, K, V;
+  * ``normal``: Q, K, V = standard_normal(float32);
+  * ``large_logit``: Q, K = 3 * standard_normal(float32) (scores with a
+    standard deviation near 9, so the running max moves a lot and rescaling is
+    exercised), V = 2 * random(float32) - 1, i.e. uniform on [-1, 1);
+  * the float32 draws are rounded to the workload dtype with round-to-nearest-
+    even (torch CPU ``.to``), and those rounded values are the inputs.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+import numpy as np
+import torch
+
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str          # "f32" | "bf16" | "f16"
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    seed: int
+    dist: str = "normal"
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(d), as the fp32 number the library receives."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def flops(self) -> float:
+        """Metric FLOPs: 4*B*H*N^2*d, halved when causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2.0 if self.causal else f
+
+    @property
+    def visible_pairs(self) -> int:
+        per_head = self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
+        return self.B * self.H * per_head
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workloads (plus the ragged variant of the second) that the parity
+# tests and the benchmark use.
+WORKLOADS = {
+    "C1": Workload("C1", "f32", 1, 1, 512, 64, False, 0),
+    "C2": Workload("C2", "f32", 4, 8, 2048, 64, False, 1),
+    "C2r": Workload("C2r", "f32", 4, 8, 2000, 64, False, 1),
+    "C3": Workload("C3", "bf16", 8, 16, 4096, 128, True, 2),
+    "C4": Workload("C4", "bf16", 1, 16, 16384, 64, False, 3),
+    "C5": Workload("C5", "f16", 2, 32, 8191, 128, True, 4, "large_logit"),
+}
+
+
+def make_inputs(w: Workload):
+    """Return (q, k, v) as CPU torch tensors of the workload's dtype."""
+    rng = np.random.default_rng(w.seed)
+    shape = (w.B, w.H, w.N, w.d)
+    if w.dist == "normal":
+        q = rng.standard_normal(shape, dtype=np.float32)
+        k = rng.standard_normal(shape, dtype=np.float32)
+        v = rng.standard_normal(shape, dtype=np.float32)
+    elif w.dist == "large_logit":
+        q = 3.0 * rng.standard_normal(shape, dtype=np.float32)
+        k = 3.0 * rng.standard_normal(shape, dtype=np.float32)
+        v = rng.random(shape, dtype=np.float32) * 2.0 - 1.0
+    else:
+        raise ValueError(f"unknown distribution {w.dist!r}")
+    tdt = TORCH_DTYPES[w.dtype]
+    return tuple(torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(tdt)
+                 for x in (q, k, v))
+
+
+def sample_rows(w: Workload, count: int, seed: int = 12345) -> np.ndarray:
+    """Deterministic sample of flat row indices (b*H + h)*N + i.
+
+    Always includes the first and last row of the first and last head (the
+    causal corner cases and the ragged tail) plus uniformly drawn rows.
+    """
+    total = w.B * w.H * w.N
+    fixed = {0, w.N - 1, total - w.N, total - 1}
+    rng = np.random.default_rng(seed)
+    drawn = rng.choice(total, size=min(count, total), replace=False)
+    rows = np.array(sorted(fixed.union(int(r) for r in drawn)), dtype=np.int64)
+    return rows

@@ -1,0 +1,204 @@
+/*
+ * fa_oracle.c -- plain, slow, fp64 reference for exact softmax attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library
+ * and its Python binding) may link, load or call this file; only the tests,
+ * the smoke check and the benchmark's CPU-baseline leg use it.  It shares
+ * no code, header, table or conversion routine with the GPU path.
+ *
+ * What it computes (per batch b, head h, query row i):
+ *   s_ij = scale * sum_k q_ik * k_jk                for every visible key j
+ *   m_i  = max_j s_ij                                (pass 1)
+ *   l_i  = sum_j exp(s_ij - m_i)                     (pass 2)
+ *   o_i  = sum_j exp(s_ij - m_i) / l_i * v_j         (pass 3)
+ *   lse_i = m_i + ln(l_i)
+ * This is the "standard attention" definition the pages give: the scaled
+ * dot products, a numerically safe softmax computed in three passes over a
+ * row (max, sum of exponentials, normalise), and the weighted sum of value
+ * rows.  Sources:
+ *   - "FlashAttention dissected" (leren.llmnet.nl), section "The mathematical
+ *     breakthrough": the softmax of a row, and the pseudocode's score
+ *     S = Q K^T / sqrt(d);
+ *   - "How Did I Write My First FlashAttention Kernel in CUDA?", the passage
+ *     on why softmax normally needs three passes over the data;
+ *   - "CUDA Flash Attention: Online Softmax with Shared Memory Tiling"
+ *     (GitHub README), section "Kernel 1 -- Naive Attention": one score per
+ *     (i, j), a row-wise max / exp / normalise, then O_i = sum_j P_ij V_j.
+ * The visible set is every key j in [0, N), or j <= i when causal (key j > i
+ * masked, the causal convention of the workload definitions; the pages
+ * themselves do not define a causal mask).  A row with no visible key gets
+ * o_i = 0 and lse_i = -inf.
+ *
+ * Inputs are read in their stored type and widened exactly to double:
+ *   fp32  by a C cast;
+ *   bf16  by placing the 16 stored bits above 16 zero bits of an fp32;
+ *   fp16  by decoding sign / 5-bit exponent / 10-bit fraction (IEEE-754
+ *         binary16) here, including subnormals, infinities and NaN.
+ * All arithmetic after widening is double.  The N x N score matrix is never
+ * formed: one row of scores (at most N doubles) lives per worker thread.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2 };
+
+/* ---- exact widening of the stored element types ------------------------- */
+
+static double widen_bf16(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double widen_f16(uint16_t bits) {
+  int sign = (bits >> 15) & 1;
+  int expo = (bits >> 10) & 0x1f;
+  int frac = bits & 0x3ff;
+  double mag;
+  if (expo == 0) {
+    mag = ldexp((double)frac, -24); /* subnormal: frac * 2^-14 * 2^-10 */
+  } else if (expo == 31) {
+    mag = frac ? NAN : INFINITY;
+  } else {
+    mag = ldexp(1.0 + (double)frac / 1024.0, expo - 15);
+  }
+  return sign ? -mag : mag;
+}
+
+static double load_elem(const void* base, int dtype, int64_t idx) {
+  switch (dtype) {
+    case ORACLE_F32: return (double)((const float*)base)[idx];
+    case ORACLE_BF16: return widen_bf16(((const uint16_t*)base)[idx]);
+    default: return widen_f16(((const uint16_t*)base)[idx]);
+  }
+}
+
+/* Exposed so that the tests can check the widening against independent
+ * library conversions over every 16-bit pattern. */
+double oracle_widen(int dtype, uint32_t bits) {
+  if (dtype == ORACLE_BF16) return widen_bf16((uint16_t)bits);
+  if (dtype == ORACLE_F16) return widen_f16((uint16_t)bits);
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* ---- one query row, three passes ---------------------------------------- */
+
+typedef struct {
+  const void *q, *k, *v;
+  int dtype;
+  int64_t H, N, d;
+  double scale;
+  int causal;
+  const int64_t* rows; /* flat (b*H + h)*N + i indices, or NULL for all */
+  int64_t nrows;
+  double *o, *lse;     /* o: [nrows, d], lse: [nrows] */
+  int64_t first, last; /* this worker's slice of [0, nrows) */
+} job_t;
+
+static void one_row(const job_t* J, int64_t flat, double* o_out, double* lse_out,
+                    double* s /* scratch, N doubles */) {
+  const int64_t N = J->N, d = J->d;
+  const int64_t bh = flat / N, i = flat % N;
+  const int64_t head = bh * N * d; /* element offset of this (b, h) */
+  const int64_t nvis = J->causal ? i + 1 : N;
+
+  int64_t c;
+  for (c = 0; c < d; ++c) o_out[c] = 0.0;
+  if (nvis <= 0) {
+    *lse_out = -INFINITY;
+    return;
+  }
+
+  /* pass 1: scaled scores and their maximum */
+  double m = -INFINITY;
+  for (int64_t j = 0; j < nvis; ++j) {
+    double dot = 0.0;
+    for (c = 0; c < d; ++c)
+      dot += load_elem(J->q, J->dtype, head + i * d + c) *
+             load_elem(J->k, J->dtype, head + j * d + c);
+    s[j] = J->scale * dot;
+    if (s[j] > m) m = s[j];
+  }
+
+  /* pass 2: sum of exponentials shifted by the maximum */
+  double l = 0.0;
+  for (int64_t j = 0; j < nvis; ++j) l += exp(s[j] - m);
+
+  /* pass 3: normalised weights times value rows */
+  for (int64_t j = 0; j < nvis; ++j) {
+    double p = exp(s[j] - m) / l;
+    for (c = 0; c < d; ++c) o_out[c] += p * load_elem(J->v, J->dtype, head + j * d + c);
+  }
+  *lse_out = m + log(l);
+}
+
+static void* worker(void* arg) {
+  const job_t* J = (const job_t*)arg;
+  double* s = (double*)malloc(sizeof(double) * (size_t)(J->N > 0 ? J->N : 1));
+  if (!s) return (void*)1;
+  for (int64_t r = J->first; r < J->last; ++r) {
+    int64_t flat = J->rows ? J->rows[r] : r;
+    one_row(J, flat, J->o + r * J->d, J->lse + r, s);
+  }
+  free(s);
+  return NULL;
+}
+
+/*
+ * oracle_fwd_f64 -- q, k, v: contiguous [B, H, N, d] arrays of `dtype`.
+ * rows: optional list of flat row indices ((b*H + h)*N + i); NULL means all
+ * B*H*N rows in order.  o: [nrows, d] doubles, lse: [nrows] doubles.
+ * Returns 0 on success, -1 on a bad argument, -2 when out of memory.
+ */
+int oracle_fwd_f64(const void* q, const void* k, const void* v, int dtype, int64_t B,
+                   int64_t H, int64_t N, int64_t d, double scale, int causal,
+                   const int64_t* rows, int64_t nrows, double* o, double* lse,
+                   int nthreads) {
+  if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return -1;
+  if (B < 0 || H < 0 || N < 0 || d <= 0 || nrows < 0) return -1;
+  if (!rows) nrows = B * H * N;
+  if (nrows == 0) return 0;
+  if (!q || !k || !v || !o || !lse) return -1;
+  if (rows) {
+    for (int64_t r = 0; r < nrows; ++r)
+      if (rows[r] < 0 || rows[r] >= B * H * N) return -1;
+  }
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > nrows) nthreads = (int)nrows;
+
+  job_t* jobs = (job_t*)calloc((size_t)nthreads, sizeof(job_t));
+  pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  if (!jobs || !tids) {
+    free(jobs);
+    free(tids);
+    return -2;
+  }
+  int rc = 0, started = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    job_t* J = &jobs[t];
+    J->q = q; J->k = k; J->v = v; J->dtype = dtype;
+    J->H = H; J->N = N; J->d = d; J->scale = scale; J->causal = causal;
+    J->rows = rows; J->nrows = nrows; J->o = o; J->lse = lse;
+    J->first = nrows * t / nthreads;
+    J->last = nrows * (t + 1) / nthreads;
+    if (pthread_create(&tids[t], NULL, worker, J) != 0) {
+      if (worker(J)) rc = -2; /* no thread: run this slice inline */
+      continue;
+    }
+    tids[started++] = tids[t];
+  }
+  for (int t = 0; t < started; ++t) {
+    void* ret = NULL;
+    pthread_join(tids[t], &ret);
+    if (ret) rc = -2;
+  }
+  free(jobs);
+  free(tids);
+  return rc;
+}

@@ -1,0 +1,55 @@
+"""The oracle's pins catch plausible slips: each mutant fails at least one pin.
+
+Every case below plants one mistake in a temporary copy of ``fa_oracle.c``
+(on the CPU, never on a GPU), builds it, and runs ``test_oracle_pins.py``
+against that build.  A mutant that passes every pin would mean the pins leave
+that part of the oracle unchecked.
+"""
+import os
+import shutil
+import subprocess
+import sys
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+SRC = ROOT / "oracle" / "fa_oracle.c"
+
+MUTANTS = {
+    "causal_off_by_one": ("J->causal ? i + 1 : N", "J->causal ? i : N"),
+    "dropped_scale": ("s[j] = J->scale * dot;", "s[j] = dot;"),
+    "key_row_index": ("load_elem(J->k, J->dtype, head + j * d + c)",
+                      "load_elem(J->k, J->dtype, head + i * d + c)"),
+    "value_row_index": ("load_elem(J->v, J->dtype, head + j * d + c)",
+                        "load_elem(J->v, J->dtype, head + i * d + c)"),
+    "transposed_query": ("load_elem(J->q, J->dtype, head + i * d + c)",
+                         "load_elem(J->q, J->dtype, head + c * N + i)"),
+    "dropped_normalisation": ("double p = exp(s[j] - m) / l;", "double p = exp(s[j] - m);"),
+    "lse_sign": ("*lse_out = m + log(l);", "*lse_out = m - log(l);"),
+    "lse_dropped_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
+    "head_offset": ("const int64_t head = bh * N * d;", "const int64_t head = bh * d;"),
+    "max_not_subtracted_in_sum": ("l += exp(s[j] - m);", "l += exp(s[j]);"),
+    "f16_bias": ("expo - 15);", "expo - 16);"),
+    "f16_subnormal": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    "bf16_shift": ("(uint32_t)bits << 16;", "(uint32_t)bits << 15;"),
+    "max_uses_min": ("if (s[j] > m) m = s[j];", "if (s[j] < m || m == -INFINITY) m = s[j];"),
+}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    text = SRC.read_text()
+    assert text.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    src = tmp_path / "fa_oracle_mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-pthread", "-o",
+                    str(lib), str(src), "-lm"], check=True)
+    env = dict(os.environ, FA_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        str(ROOT / "tests" / "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"

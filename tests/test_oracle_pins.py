@@ -1,0 +1,281 @@
+"""Pins of the fp64 oracle to facts fixed outside the oracle itself.
+
+Each test ties the three-pass oracle (``oracle/fa_oracle.c``) to something it
+does not compute itself: a closed form, an invariant of softmax attention, an
+independent library routine, exhaustive conversion tables, or the tile-by-tile
+online recurrence that the pages describe.  They are chosen so that a plausible
+slip anywhere in the oracle (a dropped term, a wrong sign or index, a
+transposed operand, an off-by-one causal bound, a wrong head offset, a wrong
+16-bit decode) fails at least one of them.  CPU only.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import online_ref
+
+RNG = np.random.default_rng(2024)
+
+
+def _rand(shape, dtype=torch.float32, scale=1.0, seed=0):
+    g = np.random.default_rng(seed)
+    x = (scale * g.standard_normal(shape)).astype(np.float32)
+    return torch.from_numpy(x).to(dtype)
+
+
+def _f64(t):
+    return t.to(torch.float64).numpy()
+
+
+# --------------------------------------------------------------------------
+# Exact widening of stored elements (the oracle's own bf16/fp16 decoders)
+# --------------------------------------------------------------------------
+
+def test_widen_f16_exhaustive_against_numpy(oracle_lib):
+    bits = np.arange(65536, dtype=np.uint32)
+    ref = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    got = np.array([oracle.widen("f16", int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_widen_bf16_exhaustive_against_torch(oracle_lib):
+    bits = np.arange(65536, dtype=np.uint32)
+    ref = torch.from_numpy(bits.astype(np.uint16).view(np.int16)).view(torch.bfloat16)
+    ref = ref.to(torch.float64).numpy()
+    got = np.array([oracle.widen("bf16", int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+# --------------------------------------------------------------------------
+# Closed forms
+# --------------------------------------------------------------------------
+
+def test_two_key_closed_form(oracle_lib):
+    # d = 1, N = 2, scale = 1: query 0 sees scores (0, 1) -> weights
+    # 1/(1+e) and e/(1+e); LSE = ln(1 + e).  Causal row 0 sees key 0 only.
+    q = torch.tensor([[[[1.0], [1.0]]]])
+    k = torch.tensor([[[[0.0], [1.0]]]])
+    v = torch.tensor([[[[3.0], [-5.0]]]])
+    o, lse = oracle.fwd(q, k, v, 1.0, False)
+    e = math.e
+    assert o[0, 0, 0, 0] == pytest.approx((3.0 - 5.0 * e) / (1.0 + e), rel=1e-15)
+    assert lse[0, 0, 0] == pytest.approx(math.log1p(e), rel=1e-15)
+    o, lse = oracle.fwd(q, k, v, 1.0, True)
+    assert o[0, 0, 0, 0] == 3.0 and lse[0, 0, 0] == 0.0
+    assert o[0, 0, 1, 0] == pytest.approx((3.0 - 5.0 * e) / (1.0 + e), rel=1e-15)
+
+
+def test_score_range_beyond_exp_range_stays_finite(oracle_lib):
+    # Scores -800, 0, 800 (scale 1, d = 1): exp(1600) overflows a double, so
+    # only a softmax that subtracts the row maximum (the "safe" form whose
+    # three passes the pages describe) returns the one-hot answer here:
+    # O = V[2], LSE = 800.  Causal row 1 sees scores -800, 0 -> O = V[1].
+    q = torch.ones((1, 1, 3, 1))
+    k = torch.tensor([[[[-800.0], [0.0], [800.0]]]])
+    v = torch.tensor([[[[1.0], [2.0], [4.0]]]])
+    o, lse = oracle.fwd(q, k, v, 1.0, False)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    np.testing.assert_array_equal(o[0, 0, :, 0], [4.0, 4.0, 4.0])
+    np.testing.assert_array_equal(lse[0, 0], [800.0, 800.0, 800.0])
+    o, lse = oracle.fwd(q, k, v, 1.0, True)
+    np.testing.assert_array_equal(o[0, 0, :, 0], [1.0, 2.0, 4.0])
+    np.testing.assert_array_equal(lse[0, 0], [-800.0, 0.0, 800.0])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_sum_to_one(oracle_lib, dtype, causal):
+    # V = 1 everywhere: every output is the sum of the softmax weights.
+    B, H, N, d = 2, 3, 37, 16
+    q = _rand((B, H, N, d), dtype, seed=1)
+    k = _rand((B, H, N, d), dtype, seed=2)
+    v = torch.ones((B, H, N, d), dtype=dtype)
+    o, lse = oracle.fwd(q, k, v, 1.0 / math.sqrt(d), causal)
+    assert np.max(np.abs(o - 1.0)) <= 1e-14
+    # and LSE normalises the same scores: sum_j exp(s_ij - lse_i) = 1
+    s = (1.0 / math.sqrt(d)) * np.einsum("bhid,bhjd->bhij", _f64(q), _f64(k))
+    if causal:
+        s = np.where(np.triu(np.ones((N, N), bool), 1), -np.inf, s)
+    tot = np.exp(s - lse[..., None]).sum(-1)
+    assert np.max(np.abs(tot - 1.0)) <= 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_gives_column_mean(oracle_lib, causal):
+    # Q = 0 makes every score 0: O_i is the plain mean of the visible V rows
+    # and LSE_i = ln(#visible).
+    B, H, N, d = 1, 2, 50, 8
+    q = torch.zeros((B, H, N, d))
+    k = _rand((B, H, N, d), seed=3)
+    v = _rand((B, H, N, d), seed=4)
+    o, lse = oracle.fwd(q, k, v, 0.35, causal)
+    vv = _f64(v)
+    if causal:
+        ref = np.cumsum(vv, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+        ref_lse = np.log(np.arange(1, N + 1, dtype=np.float64))[None, None, :]
+    else:
+        ref = np.broadcast_to(vv.mean(axis=2, keepdims=True), vv.shape)
+        ref_lse = np.full((B, H, N), math.log(N))
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, np.broadcast_to(ref_lse, lse.shape), rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("jstar", [0, 5, 31])
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_dominant_logit_returns_that_value_row(oracle_lib, jstar, causal):
+    # Key j* = t*u with q_i = u: its score beats every other by > 60, so the
+    # softmax is one-hot to far below 1e-20 and O_i = V_j*, LSE_i = s_ij*.
+    N, d = 32, 8
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    k = _rand((1, 1, N, d), scale=0.5, seed=5)
+    u = torch.zeros(d)
+    u[2] = 1.0
+    t = 256.0
+    k[0, 0, jstar] = t * u
+    q = u.expand(1, 1, N, d).contiguous()
+    v = _rand((1, 1, N, d), seed=6)
+    o, lse = oracle.fwd(q, k, v, scale, causal)
+    rows = range(jstar, N) if causal else range(N)
+    others = [j for j in range(N) if j != jstar]
+    gap = scale * t - scale * float(k[0, 0, others, 2].abs().max())
+    assert gap > 60
+    for i in rows:
+        np.testing.assert_allclose(o[0, 0, i], _f64(v[0, 0, jstar]), rtol=0, atol=1e-20)
+        assert lse[0, 0, i] == pytest.approx(scale * t, rel=1e-15)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_causal_row_zero_is_first_value_row(oracle_lib, dtype):
+    B, H, N, d = 2, 2, 19, 8
+    q, k, v = (_rand((B, H, N, d), dtype, seed=s) for s in (7, 8, 9))
+    scale = 0.25
+    o, lse = oracle.fwd(q, k, v, scale, True)
+    np.testing.assert_array_equal(o[:, :, 0], _f64(v[:, :, 0]))
+    dot0 = (_f64(q[:, :, 0]) * _f64(k[:, :, 0])).sum(-1)
+    np.testing.assert_allclose(lse[:, :, 0], scale * dot0, rtol=1e-15, atol=1e-15)
+    # a single key (N = 1) returns V[0] whatever the query, causal or not
+    o1, _ = oracle.fwd(q[:, :, :1].contiguous(), k[:, :, :1].contiguous(),
+                       v[:, :, :1].contiguous(), scale, False)
+    np.testing.assert_array_equal(o1[:, :, 0], _f64(v[:, :, 0]))
+
+
+# --------------------------------------------------------------------------
+# The method: tile-by-tile online softmax equals three-pass, by brute force
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [1, 4, 8])
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_recurrence_equals_three_pass(oracle_lib, d, causal):
+    worst = 0.0
+    for seed in range(5):
+        for n in range(1, 17):
+            q, k, v = (_rand((1, 1, n, d), scale=2.0, seed=100 * seed + 10 * n + j)
+                       for j in range(3))
+            scale = 1.0 / math.sqrt(d)
+            o_ref, lse_ref = oracle.fwd(q, k, v, scale, causal)
+            qq, kk, vv = (_f64(t[0, 0]) for t in (q, k, v))
+            sc = float(np.float32(scale))
+            for bc in range(1, n + 1):
+                for br in sorted({1, n}):
+                    for form in (online_ref.deferred, online_ref.normalised):
+                        o, lse = form(qq, kk, vv, sc, causal, br=br, bc=bc)
+                        err = np.max(np.abs(o - o_ref[0, 0])) / max(1.0, np.max(np.abs(o_ref)))
+                        err_l = np.max(np.abs(lse - lse_ref[0, 0]) / np.maximum(1.0, np.abs(lse_ref[0, 0])))
+                        worst = max(worst, err, err_l)
+    assert worst <= 1e-13, worst
+
+
+# --------------------------------------------------------------------------
+# Independent library routines on small shapes
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,d", [(1, 8), (7, 8), (33, 64), (64, 16)])
+def test_matches_torch_sdpa_fp64(oracle_lib, dtype, causal, N, d):
+    B, H = 2, 3
+    q, k, v = (_rand((B, H, N, d), dtype, scale=1.5, seed=s) for s in (11, 12, 13))
+    scale = 1.0 / math.sqrt(d)
+    sc = float(np.float32(scale))
+    o, lse = oracle.fwd(q, k, v, scale, causal)
+    q64, k64, v64 = (t.to(torch.float64) for t in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q64, k64, v64, is_causal=causal, scale=sc).numpy()
+    logits = sc * torch.matmul(q64, k64.transpose(-1, -2).contiguous())
+    if causal:
+        logits = logits.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    ref_lse = torch.logsumexp(logits, dim=-1).numpy()
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_matches_scipy_softmax(oracle_lib):
+    from scipy.special import softmax
+    N, d = 40, 24
+    q, k, v = (_rand((1, 1, N, d), seed=s) for s in (21, 22, 23))
+    scale = 0.3
+    o, _ = oracle.fwd(q, k, v, scale, False)
+    s = float(np.float32(scale)) * (_f64(q[0, 0]) @ _f64(k[0, 0]).T)
+    ref = softmax(s, axis=1) @ _f64(v[0, 0])
+    np.testing.assert_allclose(o[0, 0], ref, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Invariants
+# --------------------------------------------------------------------------
+
+def _int_valued(shape, seed, lo=-4, hi=5):
+    g = np.random.default_rng(seed)
+    return torch.from_numpy((g.integers(lo, hi, size=shape) / 4.0).astype(np.float32))
+
+
+def test_joint_key_value_permutation_leaves_output(oracle_lib):
+    B, H, N, d = 1, 2, 29, 8
+    q, k, v = (_rand((B, H, N, d), seed=s) for s in (31, 32, 33))
+    perm = torch.from_numpy(np.random.default_rng(34).permutation(N))
+    o1, l1 = oracle.fwd(q, k, v, 0.4, False)
+    o2, l2 = oracle.fwd(q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(), 0.4, False)
+    np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=1e-14, atol=1e-14)
+
+
+def test_query_permutation_permutes_rows(oracle_lib):
+    B, H, N, d = 2, 1, 23, 8
+    q, k, v = (_rand((B, H, N, d), seed=s) for s in (41, 42, 43))
+    perm = np.random.default_rng(44).permutation(N)
+    o1, l1 = oracle.fwd(q, k, v, 0.4, False)
+    o2, l2 = oracle.fwd(q[:, :, torch.from_numpy(perm)].contiguous(), k, v, 0.4, False)
+    np.testing.assert_array_equal(o1[:, :, perm], o2)
+    np.testing.assert_array_equal(l1[:, :, perm], l2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_common_key_shift_moves_only_lse(oracle_lib, causal):
+    # K' = K + w (exact: small multiples of 1/4) shifts row i's scores by
+    # scale*q_i.w, so O is unchanged and LSE_i grows by exactly that.
+    B, H, N, d = 1, 2, 31, 8
+    q, k, v = _int_valued((B, H, N, d), 51), _int_valued((B, H, N, d), 52), _rand((B, H, N, d), seed=53)
+    w = _int_valued((d,), 54)
+    scale = 0.5
+    o1, l1 = oracle.fwd(q, k, v, scale, causal)
+    o2, l2 = oracle.fwd(q, (k + w).contiguous(), v, scale, causal)
+    shift = scale * (_f64(q) @ _f64(w))
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l2, l1 + shift, rtol=1e-13, atol=1e-12)
+
+
+def test_row_subset_equals_full_rows(oracle_lib):
+    B, H, N, d = 2, 3, 45, 16
+    q, k, v = (_rand((B, H, N, d), seed=s) for s in (61, 62, 63))
+    o, l = oracle.fwd(q, k, v, 0.25, True)
+    rows = np.array([0, 44, 45, 100, B * H * N - 1])
+    os_, ls_ = oracle.fwd(q, k, v, 0.25, True, rows=rows)
+    np.testing.assert_array_equal(os_, o.reshape(-1, d)[rows])
+    np.testing.assert_array_equal(ls_, l.reshape(-1)[rows])
