@@ -1,0 +1,182 @@
+"""Throughput of the libfa forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C4]
+
+One step is one call of the whole forward pass (``fa_fwd``: one kernel) over
+the workload's inputs, which are resident in HBM before timing starts.  The
+default workload is the bf16 long-sequence shape B=1 H=16 N=16384 d=64,
+non-causal.  Prints ONE JSON line with:
+
+  value / ms_per_step   whole-job throughput (metric FLOPs 4*B*H*N^2*d, halved
+                        when causal) from a wall clock around K steps,
+                        bracketed by stream synchronisation;
+  roofline              the kernel's own average duration from HIP events
+                        recorded on the launch stream around every timed
+                        launch, against the MI355X dense MFMA peak of the
+                        input dtype; ``traffic`` is the HBM bytes per launch
+                        from the committed rocprofv3 counter summary when it
+                        was taken on the current kernel source, else null;
+  cpu_baseline          the fp64 oracle timed on the host cores on a bounded
+                        row sample of the same workload (reported baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "fwd attention TFLOP/s & % MFMA peak, bf16 B=1 H=16 N=16384 d=64 (1 GPU)"
+# MI355X published dense peaks (TFLOP/s) per input dtype.
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+KERNEL_SOURCES = ["fa_device.hpp", "fa_fwd_h16.hip", "fa_fwd_f32.hip", "fa_api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update((ROOT / "exact_attention_13_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None."""
+    path = ROOT / "profiles" / f"fa_fwd_{workload}_hbm_traffic.txt"
+    if not path.exists():
+        return None
+    fields = {}
+    for line in path.read_text().splitlines():
+        m = re.match(r"^([a-z_]+):\s*(\S+)", line)
+        if m:
+            fields[m.group(1)] = m.group(2)
+    if fields.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, target_s: float):
+    """fp64 oracle on a bounded row sample, scaled to TFLOP/s."""
+    import numpy as np
+    import oracle
+    from oracle.reference import default_threads
+
+    threads = default_threads()
+    pair_flops = 4.0 * w.d
+
+    def rows_flops(rows):
+        n = w.N
+        vis = (rows % n + 1) if w.causal else np.full(rows.shape, n)
+        return float(vis.sum()) * pair_flops
+
+    rng = np.random.default_rng(99)
+    total = w.B * w.H * w.N
+    calib = np.sort(rng.choice(total, size=min(256, total), replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, w.scale, w.causal, rows=calib, threads=threads)
+    dt = max(time.perf_counter() - t0, 1e-3)
+    rate = rows_flops(calib) / dt
+    want = int(min(total, max(256, target_s * rate / (pair_flops * (w.N if not w.causal else w.N / 2)))))
+    rows = np.sort(rng.choice(total, size=want, replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, w.scale, w.causal, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    fl = rows_flops(rows)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{want} of {total} query rows (uniform, seed 99) of the same workload, "
+                      f"{fl:.3e} FLOPs in {dt:.1f} s, fp64 three-pass, {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="C4")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the forward pass has no multi-GPU path "
+              "in this library (heads shard across GPUs with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from exact_attention_13_amd import binding
+    from exact_attention_13_amd.inputs import WORKLOADS, make_inputs
+
+    binding.load()  # fails loudly when libfa.so is missing
+    w = WORKLOADS[args.workload]
+    q, k, v = make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        binding.fwd(qd, kd, vd, w.scale, w.causal, out=o, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+
+    # Kernel duration: events on the launch stream around every launch.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        binding.fwd(qd, kd, vd, w.scale, w.causal, out=o, lse=lse, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    avg_kernel_ms = sum(kernel_ms) / len(kernel_ms)
+    ms_per_step = wall * 1e3 / args.steps
+
+    flops = w.flops
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = read_traffic(w.name)
+
+    out = {
+        "metric": METRIC if w.name == "C4" else f"fwd attention TFLOP/s, workload {w.name}",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": f"synthetic: seeded ({w.dist}, numpy PCG64 seed {w.seed}) Q/K/V rounded to {w.dtype}",
+        "config": {"workload": f"{w.name}: {w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} "
+                               f"{'causal' if w.causal else 'non-causal'}",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "flops_per_step": flops, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic,
+                     "kernel_ms_avg": round(avg_kernel_ms, 5),
+                     "kernel_ms_min": round(kernel_ms[0], 5),
+                     "kernel_ms_median": round(kernel_ms[len(kernel_ms) // 2], 5)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,88 @@
+// fa_device.hpp -- device helpers shared by the libfa forward kernels (gfx950).
+//
+// Everything here is CDNA4-specific: wave64, 32x32 MFMA tiles, the
+// permlane32 swap between the two halves of a wave, and the XCD layout of
+// MI355X (eight accelerator dies, workgroups dealt round-robin across them).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa_impl {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309417f;
+
+// Arguments common to every forward kernel.  Pointers are the caller's
+// [B, H, N, d] buffers; `bh` = B*H independent heads.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;      // may be null
+  int bh;          // B*H
+  int n;           // sequence length
+  float scale;     // multiplier of q.k
+  float scale_log2;  // scale * log2(e): scores enter exp2 in this unit
+};
+
+// ---------------------------------------------------------------------------
+// Workgroup -> tile mapping.
+//
+// The dispatcher deals workgroup w to XCD (w mod 8).  Re-indexing makes each
+// XCD take one contiguous range of logical tiles, so the workgroups that a
+// die runs at the same time mostly belong to one head and read the same K/V
+// tiles through that die's L2.  The map is a bijection of [0, total).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  constexpr int kXcds = 8;
+  const int per = total / kXcds, extra = total % kXcds;
+  const int x = w % kXcds, i = w / kXcds;
+  const int base = x * per + (x < extra ? x : extra);
+  return base + i;
+}
+
+// Reduce a value with the lane that differs in bit 5 (the other half-wave).
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Key position inside a 16-key chunk of the transposed V tile: bits 2 and 3
+// swapped.  The 32x32 score accumulator gives lane half g the keys
+// {4g..4g+3, 8+4g..8+4g+3} of each 16-key chunk; storing key kk at
+// swap23(kk) puts exactly those eight keys at positions 8g..8g+7, so one
+// 16-byte LDS read yields a lane's whole A operand for the P.V product.
+__host__ __device__ constexpr int swap23(int kk) {
+  return (kk & ~0xC) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+}
+
+// Host-side launchers (one per element-type family).
+hipError_t launch_fwd_h16(bool bf16, int d, bool causal, const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(int d, bool causal, const FwdArgs& a, hipStream_t s);
+
+// Workgroup count of a launch (the host checks it fits the grid limit).
+int64_t h16_grid_blocks(int64_t bh, int64_t n);
+int64_t f32_grid_blocks(int64_t bh, int64_t n);
+
+}  // namespace fa_impl

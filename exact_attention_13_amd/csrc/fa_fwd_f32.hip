@@ -1,0 +1,264 @@
+// fa_fwd_f32.hip -- FlashAttention forward, fp32 in / fp32 MFMA / fp32 out,
+// for MI355X (gfx950).
+//
+// Same schedule as the bf16/fp16 kernel (one workgroup per (batch*head,
+// 128-query tile), four wave64s of 32 queries, K/V tiles of 64 keys double
+// buffered in LDS, S^T = K Q^T so that each lane holds one query's scores,
+// online softmax with exp2, one division by l at the end), with fp32 data:
+//   * both products run on v_mfma_f32_32x32x2_f32 (2-deep contraction per
+//     instruction);
+//   * the contraction order is permuted so each lane's operands come from
+//     16-byte reads: lane half g feeds columns 8j + 4g .. 8j + 4g + 3 of K
+//     and Q to four consecutive instructions; for P.V the score register r
+//     of the S^T accumulator is, unchanged, the B operand of instruction r;
+//   * V is stored transposed in LDS ([d][key], four keys per 16-byte word
+//     group), a register-level 4x4 transpose on the way in;
+//   * P stays fp32 and l is a plain fp32 sum.
+// Sources as for the bf16/fp16 kernel: "FlashAttention dissected",
+// "Algorithmic core in pseudocode" (the recurrence and final division),
+// the GitHub README "CUDA Flash Attention..." (padded shared rows, K/V loads
+// by all warps, tile masking, NaN guard, size_t indexing) and the course
+// lesson "FlashAttention Inner Loop Implementation" (Q held in registers).
+#include "fa_device.hpp"
+
+namespace fa_impl {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kQPerWave = 32;
+constexpr int kBM = 128;
+constexpr int kBN = 64;
+
+template <int D>
+struct Tile {
+  static constexpr int kKStride = D + 4;    // floats per K row in LDS (+16 B)
+  static constexpr int kVStride = kBN + 4;  // floats per transposed-V row (+16 B)
+  static constexpr int kKStage = kBN * kKStride;
+  static constexpr int kVStage = D * kVStride;
+  static constexpr int kLdsFloats = 2 * (kKStage + kVStage);
+  static constexpr int kKChunks = kBN * D / 4 / kThreads;         // float4 K chunks per thread
+  static constexpr int kVUnits = (kBN / 4) * (D / 4) / kThreads;  // (4 keys, 4 columns) per thread
+  static_assert(kKChunks * kThreads * 4 == kBN * D, "K tile split");
+  static_assert(kVUnits * kThreads * 16 == kBN * D, "V tile split");
+};
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, int total) {
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(16))) float lds[T::kLdsFloats];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, grp = lane >> 5;
+  const int N = a.n;
+
+  const int L = xcd_remap(blockIdx.x, total);
+  const int bh = L / n_qt;
+  int qt = L - bh * n_qt;
+  if (CAUSAL) qt = n_qt - 1 - qt;
+
+  const int64_t head = (int64_t)bh * N * D;
+  const float* __restrict__ qg = (const float*)a.q + head;
+  const float* __restrict__ kg = (const float*)a.k + head;
+  const float* __restrict__ vg = (const float*)a.v + head;
+
+  const int q0 = qt * kBM;
+  const int qw0 = q0 + wave * kQPerWave;
+  const int my_q = qw0 + col;
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // Q fragment: lane (col, grp) holds Q[my_q][8j + 4grp + e], e = 0..3.
+  f32x4 qf[D / 8];
+  {
+    const int r = my_q < N ? my_q : N - 1;
+    const float* p = qg + (int64_t)r * D + grp * 4;
+#pragma unroll
+    for (int j = 0; j < D / 8; ++j) {
+      const f32x4 x = *(const f32x4*)(p + j * 8);
+      qf[j] = my_q < N ? x : zero4;
+    }
+  }
+
+  const int kv_end = CAUSAL ? min(q0 + kBM, N) : N;
+  const int n_kv = (kv_end + kBN - 1) / kBN;
+  const int wave_kv_end = CAUSAL ? min(qw0 + kQPerWave, N) : N;
+
+  f32x4 kst[T::kKChunks];
+  f32x4 vst[T::kVUnits][4];
+
+  auto load_tile = [&](int t) {
+    const int k0 = t * kBN;
+#pragma unroll
+    for (int i = 0; i < T::kKChunks; ++i) {
+      const int u = tid + i * kThreads;
+      const int row = u / (D / 4), cc = u % (D / 4);
+      const int key = k0 + row;
+      const int kr = key < N ? key : N - 1;
+      const f32x4 x = *(const f32x4*)(kg + (int64_t)kr * D + cc * 4);
+      kst[i] = key < N ? x : zero4;
+    }
+#pragma unroll
+    for (int i = 0; i < T::kVUnits; ++i) {
+      const int u = tid + i * kThreads;
+      const int kq = u % (kBN / 4), cc = u / (kBN / 4);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int key = k0 + 4 * kq + h;
+        const int kr = key < N ? key : N - 1;
+        const f32x4 x = *(const f32x4*)(vg + (int64_t)kr * D + cc * 4);
+        vst[i][h] = key < N ? x : zero4;
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    float* ks = lds + buf * T::kKStage;
+    float* vs = lds + 2 * T::kKStage + buf * T::kVStage;
+#pragma unroll
+    for (int i = 0; i < T::kKChunks; ++i) {
+      const int u = tid + i * kThreads;
+      const int row = u / (D / 4), cc = u % (D / 4);
+      *(f32x4*)(ks + row * T::kKStride + cc * 4) = kst[i];
+    }
+#pragma unroll
+    for (int i = 0; i < T::kVUnits; ++i) {
+      const int u = tid + i * kThreads;
+      const int kq = u % (kBN / 4), cc = u / (kBN / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x4 w = {vst[i][0][e], vst[i][1][e], vst[i][2][e], vst[i][3][e]};
+        *(f32x4*)(vs + (cc * 4 + e) * T::kVStride + kq * 4) = w;
+      }
+    }
+  };
+
+  const float c = a.scale_log2;
+  float m_run = kNegInf;
+  float l_run = 0.f;
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = (f32x16){};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_kv; ++t) {
+    const int k0 = t * kBN;
+    const bool more = t + 1 < n_kv;
+    if (more) load_tile(t + 1);
+
+    if (k0 < wave_kv_end) {
+      const float* ks = lds + (t & 1) * T::kKStage;
+      const float* vs = lds + 2 * T::kKStage + (t & 1) * T::kVStage;
+
+      f32x16 s[kBN / 32];
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb) s[kb] = (f32x16){};
+#pragma unroll
+      for (int j = 0; j < D / 8; ++j)
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb) {
+          const f32x4 ka = *(const f32x4*)(ks + (kb * 32 + col) * T::kKStride + j * 8 + grp * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[kb] = mfma_f32(ka[e], qf[j][e], s[kb]);
+        }
+
+      const bool ragged = k0 + kBN > N;
+      const bool diag = CAUSAL && (k0 + kBN - 1 > qw0);
+      if (ragged || diag) {
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
+            const bool masked = key >= N || (CAUSAL && key > my_q);
+            s[kb][r] = masked ? kNegInf : s[kb][r];
+          }
+      }
+
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = half_swap_max(mx);
+
+      const float m_new = fmaxf(m_run, mx);
+      if (__any(m_new > m_run)) {
+        const float alpha = m_new > m_run ? fast_exp2((m_run - m_new) * c) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        m_run = m_new;
+      }
+      const float nmc = m_run == kNegInf ? 0.f : -m_run * c;
+
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s[kb][r], c, nmc));
+          s[kb][r] = p;
+          l_run += p;
+        }
+
+      // O^T += V^T P^T: instruction r of key block kb takes score register r.
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const f32x4 va =
+                *(const f32x4*)(vs + (db * 32 + col) * T::kVStride + kb * 32 + g4 * 8 + grp * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oacc[db] = mfma_f32(va[e], s[kb][g4 * 4 + e], oacc[db]);
+          }
+    }
+
+    if (more) store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+
+  const float l_tot = half_swap_sum(l_run);
+  const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+  if (my_q < N) {
+    float* og = (float*)a.o + head + (int64_t)my_q * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 w = {oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv,
+                         oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv};
+        *(f32x4*)(og + db * 32 + 8 * j + 4 * grp) = w;
+      }
+    if (grp == 0 && a.lse)
+      a.lse[(int64_t)bh * N + my_q] =
+          l_tot > 0.f ? (m_run * c + fast_log2(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const FwdArgs& a, hipStream_t s) {
+  int n_qt = (a.n + kBM - 1) / kBM;
+  int total = (int)((int64_t)n_qt * a.bh);
+  FwdArgs args = a;
+  void* params[] = {&args, &n_qt, &total};
+  return hipLaunchKernel((const void*)&fwd_f32_kernel<D, CAUSAL>, dim3(total), dim3(kThreads),
+                         params, 0, s);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(int d, bool causal, const FwdArgs& a, hipStream_t s) {
+  if (d == 64) return causal ? launch<64, true>(a, s) : launch<64, false>(a, s);
+  return causal ? launch<128, true>(a, s) : launch<128, false>(a, s);
+}
+
+int64_t f32_grid_blocks(int64_t bh, int64_t n) { return (n + kBM - 1) / kBM * bh; }
+
+}  // namespace fa_impl

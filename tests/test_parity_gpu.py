@@ -1,0 +1,223 @@
+"""Parity of the HIP forward pass with the fp64 oracle (MI355X only).
+
+Every case runs the library through its C ABI (``binding.fwd`` -> ``fa_fwd``)
+on seeded synthetic inputs and compares O and LSE element by element with the
+three-pass fp64 oracle on the same bits.
+
+Tolerances (fixed by the task for the forward output):
+  * fp32 inputs: max |O - O_ref| <= 1e-4 and max |LSE - LSE_ref| <= 1e-4;
+  * bf16/fp16 inputs: max |O - O_ref| <= 2e-2 and
+    ||O - O_ref||_2 / ||O_ref||_2 <= 5e-3, max |LSE - LSE_ref| <= 2e-2.
+At full workload sizes the oracle recomputes a sample of rows (corners of the
+first and last head, the ragged tail and uniformly drawn rows); the rel-L2 is
+then taken over those rows.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_13_amd import binding
+from exact_attention_13_amd.inputs import WORKLOADS, Workload, make_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(q, k, v, scale, causal, stream=None):
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o, lse = binding.fwd(qd, kd, vd, scale, causal, stream=stream)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what=""):
+    o = o_gpu.to(torch.float64).numpy().reshape(o_ref.shape)
+    l = lse_gpu.to(torch.float64).numpy().reshape(lse_ref.shape)
+    assert np.all(np.isfinite(o)), f"{what}: non-finite O"
+    err = float(np.max(np.abs(o - o_ref))) if o.size else 0.0
+    lerr = float(np.max(np.abs(l - lse_ref))) if l.size else 0.0
+    if dtype == "f32":
+        assert err <= 1e-4, f"{what}: max|dO| = {err:.3e}"
+        assert lerr <= 1e-4, f"{what}: max|dLSE| = {lerr:.3e}"
+    else:
+        rel = float(np.linalg.norm(o - o_ref) / max(np.linalg.norm(o_ref), 1e-300))
+        assert err <= 2e-2, f"{what}: max|dO| = {err:.3e}"
+        assert rel <= 5e-3, f"{what}: rel-L2 = {rel:.3e}"
+        assert lerr <= 2e-2, f"{what}: max|dLSE| = {lerr:.3e}"
+    return err, lerr
+
+
+def small_case(dtype, B, H, N, d, causal, seed, dist="normal"):
+    w = Workload("case", dtype, B, H, N, d, causal, seed, dist)
+    return w, make_inputs(w)
+
+
+# --------------------------------------------------------------------------
+# Small shapes: full oracle, several tiles plus ragged tails
+# --------------------------------------------------------------------------
+
+SMALL_N = [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 383, 513]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_shapes(dtype, d, causal):
+    for i, n in enumerate(SMALL_N):
+        B, H = (1, 2) if i % 2 else (2, 3)
+        w, (q, k, v) = small_case(dtype, B, H, n, d, causal, seed=1000 + i)
+        _note(f"small {dtype} d={d} causal={causal} B={B} H={H} N={n}")
+        o, lse = run_gpu(q, k, v, w.scale, causal)
+        o_ref, lse_ref = oracle.fwd(q, k, v, w.scale, causal)
+        assert_close(o, lse, o_ref, lse_ref, dtype, f"N={n}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_logits_small(dtype, causal):
+    # scores with std ~ 9: the running max moves often, rescaling is exercised
+    w, (q, k, v) = small_case(dtype, 2, 2, 777, 128, causal, seed=77, dist="large_logit")
+    _note(f"large-logit {dtype} causal={causal}")
+    o, lse = run_gpu(q, k, v, w.scale, causal)
+    o_ref, lse_ref = oracle.fwd(q, k, v, w.scale, causal)
+    assert_close(o, lse, o_ref, lse_ref, dtype)
+
+
+# --------------------------------------------------------------------------
+# The workloads at full size
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C2r"])
+def test_workload_full_oracle(name):
+    w = WORKLOADS[name]
+    q, k, v = make_inputs(w)
+    _note(f"workload {name} full")
+    o, lse = run_gpu(q, k, v, w.scale, w.causal)
+    o_ref, lse_ref = oracle.fwd(q, k, v, w.scale, w.causal)
+    assert_close(o, lse, o_ref, lse_ref, w.dtype, name)
+
+
+@pytest.mark.parametrize("name", ["C3", "C4", "C5"])
+def test_workload_sampled_rows(name):
+    w = WORKLOADS[name]
+    q, k, v = make_inputs(w)
+    _note(f"workload {name} sampled")
+    o, lse = run_gpu(q, k, v, w.scale, w.causal)
+    rows = sample_rows(w, 768)
+    o_ref, lse_ref = oracle.fwd(q, k, v, w.scale, w.causal, rows=rows)
+    o_s = o.reshape(-1, w.d)[torch.from_numpy(rows)]
+    l_s = lse.reshape(-1)[torch.from_numpy(rows)]
+    assert_close(o_s, l_s, o_ref, lse_ref, w.dtype, name)
+    # properties at every row: finite outputs, |O| bounded by max|V| (O is a
+    # convex combination of value rows), LSE >= the row's own-score bound
+    vmax = float(v.abs().max())
+    assert torch.isfinite(lse).all()
+    assert float(o.float().abs().max()) <= vmax * (1 + 1e-2)
+
+
+# --------------------------------------------------------------------------
+# Edge cases of the boundary
+# --------------------------------------------------------------------------
+
+def test_null_lse_gives_same_output():
+    w, (q, k, v) = small_case("bf16", 1, 2, 300, 64, True, seed=5)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o1 = torch.empty_like(qd)
+    o2 = torch.empty_like(qd)
+    lse = torch.empty((1, 2, 300), dtype=torch.float32, device=DEV)
+    st = torch.cuda.current_stream().cuda_stream
+    B, H, N, d = q.shape
+    assert binding.fa_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o1.data_ptr(),
+                          lse.data_ptr(), B, H, N, d, w.scale, 1, binding.FA_BF16, st) == 0
+    assert binding.fa_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o2.data_ptr(),
+                          None, B, H, N, d, w.scale, 1, binding.FA_BF16, st) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_canaries_untouched_and_not_read(dtype):
+    # Every buffer sits at the front of a larger allocation whose tail is NaN.
+    # Outputs must leave the tail alone; inputs must not read it (a read would
+    # put NaN into O).
+    B, H, N, d = 2, 3, 333, 128
+    w, (q, k, v) = small_case(dtype, B, H, N, d, True, seed=9)
+    tdt = TORCH[dtype]
+    pad = 4096
+    n = q.numel()
+
+    def poisoned(src):
+        buf = torch.full((n + pad,), float("nan"), dtype=tdt, device=DEV)
+        buf[:n] = src.reshape(-1).to(DEV)
+        return buf, buf[:n].view(B, H, N, d)
+
+    (qb, qd), (kb, kd), (vb, vd) = poisoned(q), poisoned(k), poisoned(v)
+    ob = torch.full((n + pad,), float("nan"), dtype=tdt, device=DEV)
+    lb = torch.full((B * H * N + pad,), float("nan"), dtype=torch.float32, device=DEV)
+    o, lse = ob[:n].view(B, H, N, d), lb[:B * H * N].view(B, H, N)
+    binding.fwd(qd, kd, vd, w.scale, True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(ob[n:]).all() and torch.isnan(lb[B * H * N:]).all()
+    o_ref, lse_ref = oracle.fwd(q, k, v, w.scale, True)
+    assert_close(o.cpu(), lse.cpu(), o_ref, lse_ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_deterministic_bitwise(dtype):
+    w, (q, k, v) = small_case(dtype, 1, 4, 1000, 64, False, seed=11)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o1, l1 = binding.fwd(qd, kd, vd, w.scale, False)
+    o2, l2 = binding.fwd(qd, kd, vd, w.scale, False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_side_stream():
+    w, (q, k, v) = small_case("f16", 1, 2, 260, 128, False, seed=13)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+        o, lse = binding.fwd(qd, kd, vd, w.scale, False, stream=s)
+    s.synchronize()
+    o_ref, lse_ref = oracle.fwd(q, k, v, w.scale, False)
+    assert_close(o.cpu(), lse.cpu(), o_ref, lse_ref, "f16")
+
+
+def test_nondefault_scale_and_self_attention():
+    # q = k = v (one buffer), scale not 1/sqrt(d)
+    w, (q, _, _) = small_case("bf16", 1, 1, 190, 64, True, seed=15)
+    qd = q.to(DEV)
+    o, lse = binding.fwd(qd, qd, qd, 0.37, True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.fwd(q, q, q, 0.37, True)
+    assert_close(o.cpu(), lse.cpu(), o_ref, lse_ref, "bf16")
+
+
+def test_long_sequence_single_head():
+    # one head, 131072 keys: the longest row in the suite (causal, d = 128)
+    w = Workload("long", "bf16", 1, 1, 131072, 128, True, 17)
+    q, k, v = make_inputs(w)
+    _note("long single head N=131072")
+    o, lse = run_gpu(q, k, v, w.scale, True)
+    rows = sample_rows(w, 48)
+    o_ref, lse_ref = oracle.fwd(q, k, v, w.scale, True, rows=rows)
+    idx = torch.from_numpy(rows)
+    assert_close(o.reshape(-1, 128)[idx], lse.reshape(-1)[idx], o_ref, lse_ref, "bf16")
+
+
+def test_library_is_the_hip_build():
+    binding.load()
+    with open("/proc/self/maps") as f:
+        maps = f.read()
+    assert str(binding.library_path()) in maps
