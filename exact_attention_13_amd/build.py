@@ -28,6 +28,8 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # keep MFMA operands and accumulators in ordinary VGPRs (no AGPR copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

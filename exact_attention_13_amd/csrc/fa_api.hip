@@ -47,6 +47,8 @@ extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o
   const int64_t elem = dtype == FA_F32 ? 4 : 2;
   if (bh > INT64_MAX / N || bh * N > INT64_MAX / (d * elem)) return FA_ERR_SHAPE;
   const int64_t rows = bh * N;
+  // one head's rows are addressed with 32-bit byte offsets (buffer loads)
+  if ((N + 256) * d * elem > INT32_MAX) return FA_ERR_SHAPE;
   const int64_t grid = dtype == FA_F32 ? fa_impl::f32_grid_blocks(bh, N)
                                        : fa_impl::h16_grid_blocks(bh, N);
   if (grid > INT32_MAX) return FA_ERR_SHAPE;

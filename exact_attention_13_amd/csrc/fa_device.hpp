@@ -22,6 +22,13 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309417f;
 
+// Lazy rescaling: the reference maximum of a row only moves when a new score
+// exceeds it by more than kRescaleLog2 in exp2 units, so most tiles skip the
+// rescale of O and l.  Every exp2 argument stays <= kRescaleLog2, i.e. each
+// weight is <= 256: no overflow in fp32, bf16 or fp16.  Softmax does not
+// depend on the shift, so the result is the same up to rounding.
+constexpr float kRescaleLog2 = 8.0f;
+
 // Arguments common to every forward kernel.  Pointers are the caller's
 // [B, H, N, d] buffers; `bh` = B*H independent heads.
 struct FwdArgs {
@@ -50,6 +57,18 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
   const int x = w % kXcds, i = w / kXcds;
   const int base = x * per + (x < extra ? x : extra);
   return base + i;
+}
+
+// Buffer resource over `bytes` bytes from `base` (raw, no stride).  Loads
+// whose offset lies past the end return zeros instead of touching memory:
+// rows past the end of a sequence read as zero without a branch or a wait.
+// 0x00020000 is the resource word 3 that gfx9-family parts expect.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
 // Reduce a value with the lane that differs in bit 5 (the other half-wave).

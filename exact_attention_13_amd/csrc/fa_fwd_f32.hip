@@ -61,26 +61,21 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
   if (CAUSAL) qt = n_qt - 1 - qt;
 
   const int64_t head = (int64_t)bh * N * D;
-  const float* __restrict__ qg = (const float*)a.q + head;
-  const float* __restrict__ kg = (const float*)a.k + head;
-  const float* __restrict__ vg = (const float*)a.v + head;
+  const int head_bytes = N * D * 4;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const float*)a.q + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const float*)a.k + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const float*)a.v + head, head_bytes);
 
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * kQPerWave;
   const int my_q = qw0 + col;
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  // Q fragment: lane (col, grp) holds Q[my_q][8j + 4grp + e], e = 0..3.
+  // Q fragment: lane (col, grp) holds Q[my_q][8j + 4grp + e], e = 0..3; rows
+  // past the end read as zero.
   f32x4 qf[D / 8];
-  {
-    const int r = my_q < N ? my_q : N - 1;
-    const float* p = qg + (int64_t)r * D + grp * 4;
 #pragma unroll
-    for (int j = 0; j < D / 8; ++j) {
-      const f32x4 x = *(const f32x4*)(p + j * 8);
-      qf[j] = my_q < N ? x : zero4;
-    }
-  }
+  for (int j = 0; j < D / 8; ++j)
+    qf[j] = __builtin_bit_cast(f32x4, buf_load16(qr, (my_q * D + j * 8 + grp * 4) * 4));
 
   const int kv_end = CAUSAL ? min(q0 + kBM, N) : N;
   const int n_kv = (kv_end + kBN - 1) / kBN;
@@ -89,28 +84,22 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
   f32x4 kst[T::kKChunks];
   f32x4 vst[T::kVUnits][4];
 
+  // HBM -> registers for tile t; keys >= N read as zeros (buffer range check).
   auto load_tile = [&](int t) {
     const int k0 = t * kBN;
 #pragma unroll
     for (int i = 0; i < T::kKChunks; ++i) {
       const int u = tid + i * kThreads;
       const int row = u / (D / 4), cc = u % (D / 4);
-      const int key = k0 + row;
-      const int kr = key < N ? key : N - 1;
-      const f32x4 x = *(const f32x4*)(kg + (int64_t)kr * D + cc * 4);
-      kst[i] = key < N ? x : zero4;
+      kst[i] = __builtin_bit_cast(f32x4, buf_load16(kr, ((k0 + row) * D + cc * 4) * 4));
     }
 #pragma unroll
     for (int i = 0; i < T::kVUnits; ++i) {
       const int u = tid + i * kThreads;
       const int kq = u % (kBN / 4), cc = u / (kBN / 4);
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int key = k0 + 4 * kq + h;
-        const int kr = key < N ? key : N - 1;
-        const f32x4 x = *(const f32x4*)(vg + (int64_t)kr * D + cc * 4);
-        vst[i][h] = key < N ? x : zero4;
-      }
+      for (int h = 0; h < 4; ++h)
+        vst[i][h] = __builtin_bit_cast(f32x4, buf_load16(vr, ((k0 + 4 * kq + h) * D + cc * 4) * 4));
     }
   };
 
@@ -144,6 +133,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
 
   load_tile(0);
   store_tile(0);
+  // Everything loaded so far (Q included) has landed: the loop below then
+  // never waits on a prefetch before its own LDS store.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < n_kv; ++t) {
@@ -187,13 +179,14 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = half_swap_max(mx);
 
-      const float m_new = fmaxf(m_run, mx);
-      if (__any(m_new > m_run)) {
-        const float alpha = m_new > m_run ? fast_exp2((m_run - m_new) * c) : 1.f;
+      // Lazy reference max, as in the bf16/fp16 kernel.
+      const bool grow = (mx - m_run) * c > kRescaleLog2;
+      if (__any(grow)) {
+        const float alpha = grow ? fast_exp2((m_run - mx) * c) : 1.f;
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-        m_run = m_new;
+        m_run = grow ? mx : m_run;
       }
       const float nmc = m_run == kNegInf ? 0.f : -m_run * c;
 

@@ -23,8 +23,9 @@
 //     pseudocode"): running max m and sum l per query row, in registers; the
 //     scores enter exp2 with the scale folded into one FMA,
 //     p = exp2(s * scale*log2e - m * scale*log2e); when the max grows, O and
-//     l are rescaled by exp2((m_old - m_new) * scale*log2e).  The rescale is
-//     skipped, wave-uniformly, when no row of the wave changed its max.
+//     l are rescaled by exp2((m_old - m_new) * scale*log2e).  The reference
+//     max only moves when a score beats it by more than 2^8 in exp2 units,
+//     so the rescale is skipped, wave-uniformly, on almost every tile.
 //     A row whose max is still -inf (no visible key yet) uses a shift of 0,
 //     so -inf - (-inf) never forms a NaN (GitHub README, "NaN guard").
 //   * P is rounded to bf16/fp16 (nearest-even) and is, unchanged, the
@@ -110,26 +111,20 @@ __global__ __launch_bounds__(kThreads) void fwd_h16_kernel(FwdArgs a, int n_qt, 
   if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
 
   const int64_t head = (int64_t)bh * N * D;
-  const uint16_t* __restrict__ qg = (const uint16_t*)a.q + head;
-  const uint16_t* __restrict__ kg = (const uint16_t*)a.k + head;
-  const uint16_t* __restrict__ vg = (const uint16_t*)a.v + head;
+  const int head_bytes = N * D * 2;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint16_t*)a.q + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.v + head, head_bytes);
 
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * kQPerWave;
   const int my_q = qw0 + col;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  // Q fragment: lane (col, grp) holds Q[my_q][16*kc + 8*grp .. +8).
+  // Q fragment: lane (col, grp) holds Q[my_q][16*kc + 8*grp .. +8); rows past
+  // the end read as zero.
   u32x4 qf[D / 16];
-  {
-    const int r = my_q < N ? my_q : N - 1;
-    const uint16_t* p = qg + (int64_t)r * D + grp * 8;
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-      const u32x4 x = *(const u32x4*)(p + kc * 16);
-      qf[kc] = my_q < N ? x : zero4;
-    }
-  }
+  for (int kc = 0; kc < D / 16; ++kc) qf[kc] = buf_load16(qr, (my_q * D + kc * 16 + grp * 8) * 2);
 
   const int kv_end = CAUSAL ? min(q0 + kBM, N) : N;
   const int n_kv = (kv_end + kBN - 1) / kBN;
@@ -138,30 +133,23 @@ __global__ __launch_bounds__(kThreads) void fwd_h16_kernel(FwdArgs a, int n_qt, 
   u32x4 kst[T::kKChunks];
   u32x4 vst[T::kVUnits][2];
 
-  // HBM -> registers for tile t.  Keys >= N read as zeros (their scores are
-  // masked, and zero V rows keep 0 * V finite).
+  // HBM -> registers for tile t.  Keys >= N read as zeros through the
+  // buffer range check (their scores are masked, and zero V rows keep 0 * V
+  // finite); nothing waits on these loads until the tile is stored to LDS.
   auto load_tile = [&](int t) {
     const int k0 = t * kBN;
 #pragma unroll
     for (int i = 0; i < T::kKChunks; ++i) {
       const int u = tid + i * kThreads;
       const int row = u / (D / 8), cc = u % (D / 8);
-      const int key = k0 + row;
-      const int kr = key < N ? key : N - 1;
-      const u32x4 x = *(const u32x4*)(kg + (int64_t)kr * D + cc * 8);
-      kst[i] = key < N ? x : zero4;
+      kst[i] = buf_load16(kr, ((k0 + row) * D + cc * 8) * 2);
     }
 #pragma unroll
     for (int i = 0; i < T::kVUnits; ++i) {
       const int u = tid + i * kThreads;
       const int pr = u % (kBN / 2), cc = u / (kBN / 2);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int key = k0 + 2 * pr + h;
-        const int kr = key < N ? key : N - 1;
-        const u32x4 x = *(const u32x4*)(vg + (int64_t)kr * D + cc * 8);
-        vst[i][h] = key < N ? x : zero4;
-      }
+      for (int h = 0; h < 2; ++h) vst[i][h] = buf_load16(vr, ((k0 + 2 * pr + h) * D + cc * 8) * 2);
     }
   };
 
@@ -185,8 +173,9 @@ __global__ __launch_bounds__(kThreads) void fwd_h16_kernel(FwdArgs a, int n_qt, 
       const u32x4 x = vst[i][0], y = vst[i][1];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = (x[j] & 0xffffu) | (y[j] << 16);
-        const uint32_t hi = (x[j] >> 16) | (y[j] & 0xffff0000u);
+        // lo = (x.lo16, y.lo16), hi = (x.hi16, y.hi16)
+        const uint32_t lo = __builtin_amdgcn_perm(y[j], x[j], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(y[j], x[j], 0x07060302u);
         *(uint32_t*)(vs + (cc * 8 + 2 * j) * T::kVStride + pos) = lo;
         *(uint32_t*)(vs + (cc * 8 + 2 * j + 1) * T::kVStride + pos) = hi;
       }
@@ -202,6 +191,9 @@ __global__ __launch_bounds__(kThreads) void fwd_h16_kernel(FwdArgs a, int n_qt, 
 
   load_tile(0);
   store_tile(0);
+  // Everything loaded so far (Q included) has landed: the loop below then
+  // never waits on a prefetch before its own LDS store.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < n_kv; ++t) {
@@ -246,13 +238,16 @@ __global__ __launch_bounds__(kThreads) void fwd_h16_kernel(FwdArgs a, int n_qt, 
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = half_swap_max(mx);
 
-      const float m_new = fmaxf(m_run, mx);
-      if (__any(m_new > m_run)) {
-        const float alpha = m_new > m_run ? fast_exp2((m_run - m_new) * c) : 1.f;
+      // Move the reference max only when the tile's max beats it by more
+      // than 2^kRescaleLog2 (always on a row's first visible key, since
+      // m_run = -inf there); a row still without a visible key keeps -inf.
+      const bool grow = (mx - m_run) * c > kRescaleLog2;
+      if (__any(grow)) {
+        const float alpha = grow ? fast_exp2((m_run - mx) * c) : 1.f;
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-        m_run = m_new;
+        m_run = grow ? mx : m_run;
       }
       const float nmc = m_run == kNegInf ? 0.f : -m_run * c;
 

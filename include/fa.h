@@ -48,7 +48,7 @@ typedef enum {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,     /* q, k, v or o is NULL                                  */
-  FA_ERR_SHAPE = 2,    /* B, H or N negative, or the launch grid would overflow */
+  FA_ERR_SHAPE = 2,    /* B, H or N negative, or the problem is too large       */
   FA_ERR_HEAD_DIM = 3, /* d is not one of the supported head sizes (64, 128)    */
   FA_ERR_DTYPE = 4,    /* dtype is not an fa_dtype value                        */
   FA_ERR_SCALE = 5,    /* scale is not finite or not > 0                        */
@@ -70,6 +70,9 @@ typedef enum {
  *          log; a row with no visible key would get O_i = 0, LSE_i = -inf.
  * B, H, N  batch, heads, sequence length (queries = keys = N).  Any of them
  *          zero is a valid empty problem and returns FA_OK with no launch.
+ *          Limits (else FA_ERR_SHAPE): B*H <= 2^31-1, one head's N x d
+ *          array (plus 256 rows) below 2^31 bytes, and the launch grid
+ *          (B*H*ceil(N/128) workgroups) below 2^31.
  * d        head dimension: 64 or 128.
  * scale    multiplier of the dot products (usually 1/sqrt(d)); finite, > 0.
  * causal   nonzero: key j is masked for query i when j > i.
