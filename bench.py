@@ -36,7 +36,8 @@ sys.path.insert(0, str(ROOT))
 METRIC = "fwd attention TFLOP/s & % MFMA peak, bf16 B=1 H=16 N=16384 d=64 (1 GPU)"
 # MI355X published dense peaks (TFLOP/s) per input dtype.
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
-KERNEL_SOURCES = ["fa_device.hpp", "fa_fwd_h16.hip", "fa_fwd_f32.hip", "fa_api.hip"]
+KERNEL_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_fwd_h16.hip", "fa_fwd_f32.hip",
+                  "fa_api.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -104,6 +105,9 @@ def main():
     ap.add_argument("--workload", default="C4")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of attention, run a plain device copy of this many bytes "
+                         "(calibrates the HBM traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -114,6 +118,16 @@ def main():
     import torch
     from exact_attention_13_amd import binding
     from exact_attention_13_amd.inputs import WORKLOADS, make_inputs
+
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.rand(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "launches": max(1, args.steps)}), flush=True)
+        return
 
     binding.load()  # fails loudly when libfa.so is missing
     w = WORKLOADS[args.workload]

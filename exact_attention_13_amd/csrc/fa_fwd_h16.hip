@@ -29,77 +29,46 @@
 //     A row whose max is still -inf (no visible key yet) uses a shift of 0,
 //     so -inf - (-inf) never forms a NaN (GitHub README, "NaN guard").
 //   * P is rounded to bf16/fp16 (nearest-even) and is, unchanged, the
-//     B operand of O^T = V^T P^T; the row sum l adds the same rounded values
-//     (v_dot2 with (1, 1)), so the weights that multiply V sum to one.
+//     B operand of O^T = V^T P^T; the row sum l adds the fp32 values with
+//     plain VALU adds.  (v_dot2 would add the rounded pairs in one
+//     instruction, but it runs in the matrix pipe and cannot overlap the
+//     MFMAs of the other waves.)
 //   * Causal and ragged masking (-inf) is applied only on tiles that cross
 //     the diagonal or the end of the sequence; tiles wholly above the
 //     diagonal are never loaded.
 //   * Epilogue ("FlashAttention dissected", pseudocode's final step): one
 //     division of O by l, rounding to the I/O type, and LSE = scale*m + ln l.
-#include "fa_device.hpp"
+#include "fa_h16.hpp"
 
 namespace fa_impl {
 namespace {
 
-constexpr int kThreads = 256;    // four wave64s
-constexpr int kQPerWave = 32;    // one 32-wide MFMA column block per wave
-constexpr int kBM = 128;         // queries per workgroup
-constexpr int kBN = 64;          // keys per K/V tile
-
-template <bool BF16>
-struct Half;
-
-template <>
-struct Half<true> {
-  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack(float x, float y) {
-    const bf16x2 t = {(__bf16)x, (__bf16)y};
-    return __builtin_bit_cast(uint32_t, t);
-  }
-  // acc + lo(p) + hi(p), fp32 accumulate
-  static __device__ __forceinline__ float add_pair(uint32_t p, float acc) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
-  }
-};
-
-template <>
-struct Half<false> {
-  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack(float x, float y) {
-    const f16x2 t = {(_Float16)x, (_Float16)y};
-    return __builtin_bit_cast(uint32_t, t);
-  }
-  static __device__ __forceinline__ float add_pair(uint32_t p, float acc) {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), one, acc, false);
-  }
-};
-
-template <int D>
-struct Tile {
-  static constexpr int kKStride = D + 8;    // elements per K row in LDS (+16 B)
-  static constexpr int kVStride = kBN + 8;  // elements per transposed-V row (+16 B)
-  static constexpr int kKStage = kBN * kKStride;
+// Tile configuration: NW wave64s per workgroup, each owning QB blocks of 32
+// query rows; K/V tiles of BN keys.  The instance table below picks one
+// configuration per (dtype, d, causal).
+template <int D_, int QB_, int BN_, int NW_>
+struct Cfg {
+  static constexpr int D = D_, QB = QB_, BN = BN_, NW = NW_;
+  static constexpr int kThreads = NW * 64;
+  static constexpr int kQPerWave = 32 * QB;
+  static constexpr int kBM = NW * kQPerWave;        // queries per workgroup
+  static constexpr int kKStride = D + 8;            // elements per K row in LDS (+16 B)
+  static constexpr int kVStride = BN + 8;           // elements per transposed-V row (+16 B)
+  static constexpr int kKStage = BN * kKStride;
   static constexpr int kVStage = D * kVStride;
   static constexpr int kLdsElems = 2 * (kKStage + kVStage);
-  static constexpr int kKChunks = kBN * D / 8 / kThreads;          // 16 B K chunks per thread
-  static constexpr int kVUnits = (kBN / 2) * (D / 8) / kThreads;   // (key pair, 8 columns) per thread
-  static_assert(kKChunks * kThreads * 8 == kBN * D, "K tile split");
-  static_assert(kVUnits * kThreads * 16 == kBN * D, "V tile split");
+  static constexpr int kKUnits = BN * D / 8;        // 16-byte K chunks per tile
+  static constexpr int kVUnits = (BN / 2) * (D / 8);  // (key pair, 8 columns) per tile
+  static constexpr int kKPer = (kKUnits + kThreads - 1) / kThreads;
+  static constexpr int kVPer = (kVUnits + kThreads - 1) / kThreads;
+  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
 };
 
-template <bool BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fwd_h16_kernel(FwdArgs a, int n_qt, int total) {
-  using T = Tile<D>;
+template <bool BF16, bool CAUSAL, class C>
+__global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_qt, int total) {
   using HH = Half<BF16>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[T::kLdsElems];
+  constexpr int D = C::D, QB = C::QB, BN = C::BN;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLdsElems];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, grp = lane >> 5;
@@ -116,78 +85,94 @@ __global__ __launch_bounds__(kThreads) void fwd_h16_kernel(FwdArgs a, int n_qt, 
   const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + head, head_bytes);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.v + head, head_bytes);
 
-  const int q0 = qt * kBM;
-  const int qw0 = q0 + wave * kQPerWave;
-  const int my_q = qw0 + col;
+  const int q0 = qt * C::kBM;
+  const int qw0 = q0 + wave * C::kQPerWave;  // first query of this wave
 
-  // Q fragment: lane (col, grp) holds Q[my_q][16*kc + 8*grp .. +8); rows past
-  // the end read as zero.
-  u32x4 qf[D / 16];
+  // Q fragments: block qb, lane (col, grp) holds Q[qw0 + 32qb + col][16kc + 8grp .. +8);
+  // rows past the end read as zero.
+  u32x4 qf[QB][D / 16];
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) qf[kc] = buf_load16(qr, (my_q * D + kc * 16 + grp * 8) * 2);
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc)
+      qf[qb][kc] = buf_load16(qr, ((qw0 + 32 * qb + col) * D + kc * 16 + grp * 8) * 2);
 
-  const int kv_end = CAUSAL ? min(q0 + kBM, N) : N;
-  const int n_kv = (kv_end + kBN - 1) / kBN;
-  const int wave_kv_end = CAUSAL ? min(qw0 + kQPerWave, N) : N;
+  const int kv_end = CAUSAL ? min(q0 + C::kBM, N) : N;
+  const int n_kv = (kv_end + BN - 1) / BN;
+  const int wave_kv_end = CAUSAL ? min(qw0 + C::kQPerWave, N) : N;
 
-  u32x4 kst[T::kKChunks];
-  u32x4 vst[T::kVUnits][2];
+  u32x4 kst[C::kKPer];
+  u32x4 vst[C::kVPer][2];
 
   // HBM -> registers for tile t.  Keys >= N read as zeros through the
   // buffer range check (their scores are masked, and zero V rows keep 0 * V
   // finite); nothing waits on these loads until the tile is stored to LDS.
   auto load_tile = [&](int t) {
-    const int k0 = t * kBN;
+    const int k0 = t * BN;
 #pragma unroll
-    for (int i = 0; i < T::kKChunks; ++i) {
-      const int u = tid + i * kThreads;
-      const int row = u / (D / 8), cc = u % (D / 8);
-      kst[i] = buf_load16(kr, ((k0 + row) * D + cc * 8) * 2);
+    for (int i = 0; i < C::kKPer; ++i) {
+      const int u = tid + i * C::kThreads;
+      if (C::kKUnits % C::kThreads == 0 || u < C::kKUnits) {
+        const int row = u / (D / 8), cc = u % (D / 8);
+        kst[i] = buf_load16(kr, ((k0 + row) * D + cc * 8) * 2);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < T::kVUnits; ++i) {
-      const int u = tid + i * kThreads;
-      const int pr = u % (kBN / 2), cc = u / (kBN / 2);
+    for (int i = 0; i < C::kVPer; ++i) {
+      const int u = tid + i * C::kThreads;
+      if (C::kVUnits % C::kThreads == 0 || u < C::kVUnits) {
+        const int pr = u % (BN / 2), cc = u / (BN / 2);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) vst[i][h] = buf_load16(vr, ((k0 + 2 * pr + h) * D + cc * 8) * 2);
+        for (int h = 0; h < 2; ++h)
+          vst[i][h] = buf_load16(vr, ((k0 + 2 * pr + h) * D + cc * 8) * 2);
+      }
     }
   };
 
   // registers -> LDS buffer `buf`: K row-major (padded), V transposed with
   // keys interleaved in pairs: one 32-bit word holds (V[kk][c], V[kk+1][c]).
   auto store_tile = [&](int buf) {
-    uint16_t* ks = lds + buf * T::kKStage;
-    uint16_t* vs = lds + 2 * T::kKStage + buf * T::kVStage;
+    uint16_t* ks = lds + buf * C::kKStage;
+    uint16_t* vs = lds + 2 * C::kKStage + buf * C::kVStage;
 #pragma unroll
-    for (int i = 0; i < T::kKChunks; ++i) {
-      const int u = tid + i * kThreads;
-      const int row = u / (D / 8), cc = u % (D / 8);
-      *(u32x4*)(ks + row * T::kKStride + cc * 8) = kst[i];
+    for (int i = 0; i < C::kKPer; ++i) {
+      const int u = tid + i * C::kThreads;
+      if (C::kKUnits % C::kThreads == 0 || u < C::kKUnits) {
+        const int row = u / (D / 8), cc = u % (D / 8);
+        *(u32x4*)(ks + row * C::kKStride + cc * 8) = kst[i];
+      }
     }
 #pragma unroll
-    for (int i = 0; i < T::kVUnits; ++i) {
-      const int u = tid + i * kThreads;
-      const int pr = u % (kBN / 2), cc = u / (kBN / 2);
-      const int kk = 2 * pr;
-      const int pos = (kk & ~15) | swap23(kk & 15);
-      const u32x4 x = vst[i][0], y = vst[i][1];
+    for (int i = 0; i < C::kVPer; ++i) {
+      const int u = tid + i * C::kThreads;
+      if (C::kVUnits % C::kThreads == 0 || u < C::kVUnits) {
+        const int pr = u % (BN / 2), cc = u / (BN / 2);
+        const int kk = 2 * pr;
+        const int pos = (kk & ~15) | swap23(kk & 15);
+        const u32x4 x = vst[i][0], y = vst[i][1];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // lo = (x.lo16, y.lo16), hi = (x.hi16, y.hi16)
-        const uint32_t lo = __builtin_amdgcn_perm(y[j], x[j], 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(y[j], x[j], 0x07060302u);
-        *(uint32_t*)(vs + (cc * 8 + 2 * j) * T::kVStride + pos) = lo;
-        *(uint32_t*)(vs + (cc * 8 + 2 * j + 1) * T::kVStride + pos) = hi;
+        for (int j = 0; j < 4; ++j) {
+          // lo = (x.lo16, y.lo16), hi = (x.hi16, y.hi16)
+          const uint32_t lo = __builtin_amdgcn_perm(y[j], x[j], 0x05040100u);
+          const uint32_t hi = __builtin_amdgcn_perm(y[j], x[j], 0x07060302u);
+          *(uint32_t*)(vs + (cc * 8 + 2 * j) * C::kVStride + pos) = lo;
+          *(uint32_t*)(vs + (cc * 8 + 2 * j + 1) * C::kVStride + pos) = hi;
+        }
       }
     }
   };
 
   const float c = a.scale_log2;
-  float m_run = kNegInf;  // running max of raw scores q.k for query my_q
-  float l_run = 0.f;      // this lane's share of the running sum of exp2 terms
-  f32x16 oacc[D / 32];
+  float m_run[QB];  // running reference max of raw scores q.k, per query row
+  float l_run[QB];  // this lane's share of the running sum of exp2 terms
+  f32x16 oacc[QB][D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = (f32x16){};
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = kNegInf;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[qb][db] = (f32x16){};
+  }
 
   load_tile(0);
   store_tile(0);
@@ -197,81 +182,91 @@ __global__ __launch_bounds__(kThreads) void fwd_h16_kernel(FwdArgs a, int n_qt, 
   __syncthreads();
 
   for (int t = 0; t < n_kv; ++t) {
-    const int k0 = t * kBN;
+    const int k0 = t * BN;
     const bool more = t + 1 < n_kv;
     if (more) load_tile(t + 1);
 
     if (k0 < wave_kv_end) {
-      const uint16_t* ks = lds + (t & 1) * T::kKStage;
-      const uint16_t* vs = lds + 2 * T::kKStage + (t & 1) * T::kVStage;
+      const uint16_t* ks = lds + (t & 1) * C::kKStage;
+      const uint16_t* vs = lds + 2 * C::kKStage + (t & 1) * C::kVStage;
 
-      // S^T = K Q^T: lane holds keys k0 + 32*kb + 8*(r/4) + 4*grp + r%4.
-      f32x16 s[kBN / 32];
+      // S^T = K Q^T: lane holds keys k0 + 32*kb + 8*(r/4) + 4*grp + r%4 of
+      // query qw0 + 32*qb + col.
+      f32x16 s[QB][BN / 32];
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) {
-        s[kb] = (f32x16){};
+      for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = (f32x16){};
 #pragma unroll
         for (int kc = 0; kc < D / 16; ++kc) {
           const u32x4 ka =
-              *(const u32x4*)(ks + (kb * 32 + col) * T::kKStride + kc * 16 + grp * 8);
-          s[kb] = HH::mfma(ka, qf[kc], s[kb]);
+              *(const u32x4*)(ks + (kb * 32 + col) * C::kKStride + kc * 16 + grp * 8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = HH::mfma(ka, qf[qb][kc], s[qb][kb]);
         }
       }
 
-      const bool ragged = k0 + kBN > N;
-      const bool diag = CAUSAL && (k0 + kBN - 1 > qw0);
+      const bool ragged = k0 + BN > N;
+      const bool diag = CAUSAL && (k0 + BN - 1 > qw0);
       if (ragged || diag) {
 #pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
-            const bool masked = key >= N || (CAUSAL && key > my_q);
-            s[kb][r] = masked ? kNegInf : s[kb][r];
-          }
+          for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
+              const bool masked = key >= N || (CAUSAL && key > qw0 + 32 * qb + col);
+              s[qb][kb][r] = masked ? kNegInf : s[qb][kb][r];
+            }
       }
 
-      float mx = kNegInf;
+      uint32_t pk[QB][BN / 32][8];
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = half_swap_max(mx);
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = tree_max<BN / 32>(s[qb]);
+        mx = half_swap_max(mx);
 
-      // Move the reference max only when the tile's max beats it by more
-      // than 2^kRescaleLog2 (always on a row's first visible key, since
-      // m_run = -inf there); a row still without a visible key keeps -inf.
-      const bool grow = (mx - m_run) * c > kRescaleLog2;
-      if (__any(grow)) {
-        const float alpha = grow ? fast_exp2((m_run - mx) * c) : 1.f;
-        l_run *= alpha;
+        // Move the reference max only when the tile's max beats it by more
+        // than 2^kRescaleLog2 (always on a row's first visible key, since
+        // m_run = -inf there); a row still without a visible key keeps -inf.
+        const bool grow = (mx - m_run[qb]) * c > kRescaleLog2;
+        if (__any(grow)) {
+          const float alpha = grow ? fast_exp2((m_run[qb] - mx) * c) : 1.f;
+          l_run[qb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-        m_run = grow ? mx : m_run;
-      }
-      const float nmc = m_run == kNegInf ? 0.f : -m_run * c;
-
-      uint32_t pk[kBN / 32][8];
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p0 = fast_exp2(fmaf(s[kb][2 * j], c, nmc));
-          const float p1 = fast_exp2(fmaf(s[kb][2 * j + 1], c, nmc));
-          pk[kb][j] = HH::pack(p0, p1);
-          l_run = HH::add_pair(pk[kb][j], l_run);
+          for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
+          m_run[qb] = grow ? mx : m_run[qb];
         }
+        const float nmc = m_run[qb] == kNegInf ? 0.f : -m_run[qb] * c;
+
+        float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // independent row-sum chains
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float p0 = fast_exp2(fmaf(s[qb][kb][2 * j], c, nmc));
+            const float p1 = fast_exp2(fmaf(s[qb][kb][2 * j + 1], c, nmc));
+            pk[qb][kb][j] = HH::pack(p0, p1);
+            lsum[j & 3] += p0 + p1;
+          }
+        l_run[qb] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+      }
 
       // O^T += V^T P^T over 16-key chunks.
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int pc = 0; pc < kBN / 16; ++pc) {
+        for (int pc = 0; pc < BN / 16; ++pc) {
           const u32x4 va =
-              *(const u32x4*)(vs + (db * 32 + col) * T::kVStride + pc * 16 + grp * 8);
+              *(const u32x4*)(vs + (db * 32 + col) * C::kVStride + pc * 16 + grp * 8);
           const int kb = pc >> 1, h = (pc & 1) * 4;
-          const u32x4 pb = {pk[kb][h], pk[kb][h + 1], pk[kb][h + 2], pk[kb][h + 3]};
-          oacc[db] = HH::mfma(va, pb, oacc[db]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const u32x4 pb = {pk[qb][kb][h], pk[qb][kb][h + 1], pk[qb][kb][h + 2],
+                              pk[qb][kb][h + 3]};
+            oacc[qb][db] = HH::mfma(va, pb, oacc[qb][db]);
+          }
         }
     }
 
@@ -280,47 +275,68 @@ __global__ __launch_bounds__(kThreads) void fwd_h16_kernel(FwdArgs a, int n_qt, 
   }
 
   // Epilogue: l over both half-waves, O / l, LSE.
-  const float l_tot = half_swap_sum(l_run);
-  const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
-  if (my_q < N) {
-    uint16_t* og = (uint16_t*)a.o + head + (int64_t)my_q * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = qw0 + 32 * qb + col;
+    const float l_tot = half_swap_sum(l_run[qb]);
+    const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+    if (q < N) {
+      uint16_t* og = (uint16_t*)a.o + head + (int64_t)q * D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = db * 32 + 8 * j + 4 * grp;
-        const u32x2 w = {HH::pack(oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv),
-                         HH::pack(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv)};
-        *(u32x2*)(og + d0) = w;
-      }
-    if (grp == 0 && a.lse)
-      a.lse[(int64_t)bh * N + my_q] =
-          l_tot > 0.f ? (m_run * c + fast_log2(l_tot)) * kLn2 : kNegInf;
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d0 = db * 32 + 8 * j + 4 * grp;
+          const u32x2 w = {HH::pack(oacc[qb][db][4 * j] * inv, oacc[qb][db][4 * j + 1] * inv),
+                           HH::pack(oacc[qb][db][4 * j + 2] * inv, oacc[qb][db][4 * j + 3] * inv)};
+          *(u32x2*)(og + d0) = w;
+        }
+      if (grp == 0 && a.lse)
+        a.lse[(int64_t)bh * N + q] =
+            l_tot > 0.f ? (m_run[qb] * c + fast_log2(l_tot)) * kLn2 : kNegInf;
+    }
   }
 }
 
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, bool CAUSAL, class C>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
-  int n_qt = (a.n + kBM - 1) / kBM;
+  int n_qt = (a.n + C::kBM - 1) / C::kBM;
   int total = (int)((int64_t)n_qt * a.bh);
   FwdArgs args = a;
   void* params[] = {&args, &n_qt, &total};
-  return hipLaunchKernel((const void*)&fwd_h16_kernel<BF16, D, CAUSAL>, dim3(total),
-                         dim3(kThreads), params, 0, s);
+  return hipLaunchKernel((const void*)&fwd_h16_kernel<BF16, CAUSAL, C>, dim3(total),
+                         dim3(C::kThreads), params, 0, s);
 }
 
-template <bool BF16, int D>
+// Instance table: one tile configuration per head size (measured on MI355X:
+// d = 64 is VALU-heavy, so eight waves of 64 query rows each halve the LDS
+// reads per MFMA; d = 128 prefers four waves of 32 rows with 32-key tiles).
+// Overridable at build time (FA_H16_D64_CFG / FA_H16_D128_CFG = QB, BN, NW).
+#ifndef FA_H16_D64_CFG
+#define FA_H16_D64_CFG 2, 64, 8
+#endif
+#ifndef FA_H16_D128_CFG
+#define FA_H16_D128_CFG 1, 32, 4
+#endif
+using CfgD64 = Cfg<64, FA_H16_D64_CFG>;
+using CfgD128 = Cfg<128, FA_H16_D128_CFG>;
+
+template <bool BF16, class C>
 hipError_t launch_c(bool causal, const FwdArgs& a, hipStream_t s) {
-  return causal ? launch<BF16, D, true>(a, s) : launch<BF16, D, false>(a, s);
+  return causal ? launch<BF16, true, C>(a, s) : launch<BF16, false, C>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_h16(bool bf16, int d, bool causal, const FwdArgs& a, hipStream_t s) {
-  if (bf16) return d == 64 ? launch_c<true, 64>(causal, a, s) : launch_c<true, 128>(causal, a, s);
-  return d == 64 ? launch_c<false, 64>(causal, a, s) : launch_c<false, 128>(causal, a, s);
+  if (bf16)
+    return d == 64 ? launch_c<true, CfgD64>(causal, a, s) : launch_c<true, CfgD128>(causal, a, s);
+  return d == 64 ? launch_c<false, CfgD64>(causal, a, s) : launch_c<false, CfgD128>(causal, a, s);
 }
 
-int64_t h16_grid_blocks(int64_t bh, int64_t n) { return (n + kBM - 1) / kBM * bh; }
+int64_t h16_grid_blocks(int64_t bh, int64_t n) {
+  const int64_t bm = CfgD64::kBM < CfgD128::kBM ? CfgD64::kBM : CfgD128::kBM;
+  return (n + bm - 1) / bm * bh;
+}
 
 }  // namespace fa_impl

@@ -1,0 +1,57 @@
+// fa_h16.hpp -- helpers shared by the bf16/fp16 forward kernels (gfx950).
+#pragma once
+
+#include "fa_device.hpp"
+
+namespace fa_impl {
+
+// MFMA, rounding of P and the element type of one 16-bit input family.
+template <bool BF16>
+struct Half;
+
+template <>
+struct Half<true> {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float x, float y) {
+    const bf16x2 t = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, t);
+  }
+};
+
+template <>
+struct Half<false> {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float x, float y) {
+    const f16x2 t = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, t);
+  }
+};
+
+// Maximum of the KB x 16 scores held by a lane, as a tree of v_max3.
+template <int KB>
+__device__ __forceinline__ float tree_max(const f32x16 (&s)[KB]) {
+  float m[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const float a = __builtin_fmaxf(__builtin_fmaxf(s[kb][0], s[kb][1]), s[kb][2]);
+    const float b = __builtin_fmaxf(__builtin_fmaxf(s[kb][3], s[kb][4]), s[kb][5]);
+    const float c = __builtin_fmaxf(__builtin_fmaxf(s[kb][6], s[kb][7]), s[kb][8]);
+    const float d = __builtin_fmaxf(__builtin_fmaxf(s[kb][9], s[kb][10]), s[kb][11]);
+    const float e = __builtin_fmaxf(__builtin_fmaxf(s[kb][12], s[kb][13]), s[kb][14]);
+    const float f = __builtin_fmaxf(__builtin_fmaxf(a, b), c);
+    const float g = __builtin_fmaxf(__builtin_fmaxf(d, e), s[kb][15]);
+    m[kb] = __builtin_fmaxf(f, g);
+  }
+  float r = m[0];
+#pragma unroll
+  for (int kb = 1; kb < KB; ++kb) r = __builtin_fmaxf(r, m[kb]);
+  return r;
+}
+
+}  // namespace fa_impl

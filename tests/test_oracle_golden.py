@@ -1,0 +1,20 @@
+"""The oracle reproduces its stored outputs (regression guard, not a pin)."""
+import json
+from pathlib import Path
+
+import numpy as np
+
+import oracle
+from exact_attention_13_amd.inputs import Workload, make_inputs
+
+GOLDEN = Path(__file__).resolve().parent / "golden" / "oracle_small.json"
+
+
+def test_oracle_matches_stored_outputs(oracle_lib):
+    for case in json.loads(GOLDEN.read_text()):
+        dtype, B, H, N, d, causal, seed, dist = case["workload"]
+        w = Workload(case["name"], dtype, B, H, N, d, causal, seed, dist)
+        q, k, v = make_inputs(w)
+        o, lse = oracle.fwd(q, k, v, w.scale, w.causal)
+        np.testing.assert_allclose(o.ravel(), case["o"], rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(lse.ravel(), case["lse"], rtol=1e-14, atol=1e-15)
