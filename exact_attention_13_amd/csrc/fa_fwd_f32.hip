@@ -51,7 +51,10 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
   using T = Tile<D>;
   __shared__ __attribute__((aligned(16))) float lds[T::kLdsFloats];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform across a wave: keep it (and every branch on
+  // it) scalar instead of exec-masked
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, grp = lane >> 5;
   const int N = a.n;
 
