@@ -20,19 +20,20 @@
 //     that query sit in the lane 32 positions away.  Row statistics are thus
 //     an in-lane reduction plus one permlane32 swap.
 //   * Online softmax ("FlashAttention dissected", "Algorithmic core in
-//     pseudocode"): running max m and sum l per query row, in registers; the
-//     scores enter exp2 with the scale folded into one FMA,
-//     p = exp2(s * scale*log2e - m * scale*log2e); when the max grows, O and
-//     l are rescaled by exp2((m_old - m_new) * scale*log2e).  The reference
-//     max only moves when a score beats it by more than 2^8 in exp2 units,
-//     so the rescale is skipped, wave-uniformly, on almost every tile.
-//     A row whose max is still -inf (no visible key yet) uses a shift of 0,
-//     so -inf - (-inf) never forms a NaN (GitHub README, "NaN guard").
+//     pseudocode"): running reference max m and sum l per query row, in
+//     registers; the scores enter exp2 with the scale folded into one FMA,
+//     p = exp2(s * scale*log2e - m * scale*log2e).  Most tiles take a fast
+//     path with no row max at all: the lane's partial row sum bounds every
+//     weight, and only when it exceeds 2^15 (or the row has no m yet) does
+//     the tile take the exact max, rescale O and l by
+//     exp2((m_old - m_new) * scale*log2e) and recompute P.  A row whose max
+//     is still -inf (no visible key yet) uses a shift of 0, so
+//     -inf - (-inf) never forms a NaN (GitHub README, "NaN guard").
 //   * P is rounded to bf16/fp16 (nearest-even) and is, unchanged, the
-//     B operand of O^T = V^T P^T; the row sum l adds the fp32 values with
-//     plain VALU adds.  (v_dot2 would add the rounded pairs in one
-//     instruction, but it runs in the matrix pipe and cannot overlap the
-//     MFMAs of the other waves.)
+//     B operand of O^T = V^T P^T; the row sum l adds the same rounded pairs
+//     with v_dot2c, which runs in the matrix pipe: on gfx950 plain VALU work
+//     and MFMAs compete for the same issue resources, while the matrix pipe
+//     has room to spare.
 //   * Causal and ragged masking (-inf) is applied only on tiles that cross
 //     the diagonal or the end of the sequence; tiles wholly above the
 //     diagonal are never loaded.
@@ -42,6 +43,9 @@
 
 namespace fa_impl {
 namespace {
+
+// Largest lane partial row sum accepted without an exact max (see the softmax).
+constexpr float kFastSumLimit = 32768.f;
 
 // Tile configuration: NW wave64s per workgroup, each owning QB blocks of 32
 // query rows; K/V tiles of BN keys.  The instance table below picks one
@@ -227,33 +231,40 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
       uint32_t pk[QB][BN / 32][8];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float mx = tree_max<BN / 32>(s[qb]);
-        mx = half_swap_max(mx);
-
-        // Move the reference max only when the tile's max beats it by more
-        // than 2^kRescaleLog2 (always on a row's first visible key, since
-        // m_run = -inf there); a row still without a visible key keeps -inf.
-        const bool grow = (mx - m_run[qb]) * c > kRescaleLog2;
-        if (__any(grow)) {
-          const float alpha = grow ? fast_exp2((m_run[qb] - mx) * c) : 1.f;
+        // P = exp2(S c - m c), rounded; the row sum adds the rounded pairs,
+        // so the weights that multiply V sum exactly to l.
+        auto exp_row = [&](float nmc) {
+          float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent sum chains
+#pragma unroll
+          for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float p0 = fast_exp2(fmaf(s[qb][kb][2 * j], c, nmc));
+              const float p1 = fast_exp2(fmaf(s[qb][kb][2 * j + 1], c, nmc));
+              pk[qb][kb][j] = HH::pack(p0, p1);
+              ls[j & 3] = HH::dot2(pk[qb][kb][j], ls[j & 3]);
+            }
+          return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        };
+        // Fast path: no row max.  P is formed against the current reference
+        // max m, and the lane's partial sum bounds every weight it added; a
+        // sum <= 2^15 means no weight can overflow fp16/bf16.  Otherwise (a
+        // score rose well above m, or the row has no m yet: the shift is
+        // +inf and the sum inf/NaN) take the exact max over both half-waves,
+        // rescale O and l by exp2((m_old - m_new) c) and recompute P.
+        float lt = exp_row(m_run[qb] == kNegInf ? __builtin_inff() : -m_run[qb] * c);
+        if (__any(!(lt <= kFastSumLimit))) {
+          float mx = tree_max<BN / 32>(s[qb]);
+          mx = half_swap_max(mx);
+          const float m_new = fmaxf(m_run[qb], mx);
+          const float alpha = m_new > m_run[qb] ? fast_exp2((m_run[qb] - m_new) * c) : 1.f;
           l_run[qb] *= alpha;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
-          m_run[qb] = grow ? mx : m_run[qb];
+          m_run[qb] = m_new;
+          lt = exp_row(m_run[qb] == kNegInf ? 0.f : -m_run[qb] * c);
         }
-        const float nmc = m_run[qb] == kNegInf ? 0.f : -m_run[qb] * c;
-
-        float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // independent row-sum chains
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float p0 = fast_exp2(fmaf(s[qb][kb][2 * j], c, nmc));
-            const float p1 = fast_exp2(fmaf(s[qb][kb][2 * j + 1], c, nmc));
-            pk[qb][kb][j] = HH::pack(p0, p1);
-            lsum[j & 3] += p0 + p1;
-          }
-        l_run[qb] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+        l_run[qb] += lt;
       }
 
       // O^T += V^T P^T over 16-key chunks.

@@ -19,6 +19,12 @@ struct Half<true> {
     const bf16x2 t = {(__bf16)x, (__bf16)y};
     return __builtin_bit_cast(uint32_t, t);
   }
+  // acc + lo(p) + hi(p): sums a pair of rounded weights in one instruction
+  // (v_dot2c runs in the matrix pipe, leaving the VALU to the softmax)
+  static __device__ __forceinline__ float dot2(uint32_t p, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
+  }
 };
 
 template <>
@@ -30,6 +36,10 @@ struct Half<false> {
   static __device__ __forceinline__ uint32_t pack(float x, float y) {
     const f16x2 t = {(_Float16)x, (_Float16)y};
     return __builtin_bit_cast(uint32_t, t);
+  }
+  static __device__ __forceinline__ float dot2(uint32_t p, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), one, acc, false);
   }
 };
 
