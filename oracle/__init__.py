@@ -8,10 +8,13 @@ and the two share no code.
 Contents:
   * ``reference.fwd``       -- three-pass fp64 attention (C, ``fa_oracle.c``),
                                the plain definition of what the method computes;
+  * ``reference.fwd_gqa``   -- the same with grouped K/V heads and separate
+                               query / key lengths (decoding);
+  * ``reference.combine``   -- fp64 merge of results over disjoint key ranges;
   * ``online_ref``          -- the tile-by-tile online-softmax recurrence in
                                numpy fp64, in the deferred-normalisation form and
                                in the per-step-normalised form, used only to pin
                                the method's claim that it equals the plain
                                definition.
 """
-from .reference import build, fwd, widen, FLAT_ROWS_ALL  # noqa: F401
+from .reference import build, fwd, fwd_gqa, combine, widen, FLAT_ROWS_ALL  # noqa: F401

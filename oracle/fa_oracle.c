@@ -29,6 +29,20 @@
  * themselves do not define a causal mask).  A row with no visible key gets
  * o_i = 0 and lse_i = -inf.
  *
+ * The general entry point also takes separate query and key lengths and
+ * grouped K/V heads ("FlashAttention dissected", section "Interaction with
+ * the KV cache during inference": a decoding step has N_q = 1 query against
+ * N_kv cached keys, and several query heads may share one K/V head).  Query
+ * head h reads K/V head h / (H / H_kv).  The pages fix no causal alignment
+ * for N_q != N_kv; the reading taken is that query row i stands at key
+ * position N_kv - N_q + i (the rows are the newest tokens), so key j is
+ * visible when j <= i + N_kv - N_q.  For N_q = N_kv this is the mask above.
+ *
+ * oracle_combine_f64 merges results computed over disjoint key ranges,
+ * following the normalised update of "How Did I Write My First
+ * FlashAttention Kernel in CUDA?", pseudo-algorithm steps 4 and 5, applied
+ * to whole ranges (see that function).
+ *
  * Inputs are read in their stored type and widened exactly to double:
  *   fp32  by a C cast;
  *   bf16  by placing the 16 stored bits above 16 zero bits of an fp32;
@@ -92,21 +106,25 @@ double oracle_widen(int dtype, uint32_t bits) {
 typedef struct {
   const void *q, *k, *v;
   int dtype;
-  int64_t H, N, d;
+  int64_t H, Hkv, Nq, Nk, d;
   double scale;
   int causal;
-  const int64_t* rows; /* flat (b*H + h)*N + i indices, or NULL for all */
+  const int64_t* rows; /* flat (b*H + h)*Nq + i indices, or NULL for all */
   int64_t nrows;
   double *o, *lse;     /* o: [nrows, d], lse: [nrows] */
   int64_t first, last; /* this worker's slice of [0, nrows) */
 } job_t;
 
 static void one_row(const job_t* J, int64_t flat, double* o_out, double* lse_out,
-                    double* s /* scratch, N doubles */) {
-  const int64_t N = J->N, d = J->d;
-  const int64_t bh = flat / N, i = flat % N;
-  const int64_t head = bh * N * d; /* element offset of this (b, h) */
-  const int64_t nvis = J->causal ? i + 1 : N;
+                    double* s /* scratch, Nk doubles */) {
+  const int64_t Nq = J->Nq, Nk = J->Nk, d = J->d;
+  const int64_t bh = flat / Nq, i = flat % Nq;
+  const int64_t b = bh / J->H, h = bh % J->H;
+  const int64_t kvh = h / (J->H / J->Hkv);            /* K/V head of query head h */
+  const int64_t qhead = bh * Nq * d;                  /* element offset of this (b, h) */
+  const int64_t kvhead = (b * J->Hkv + kvh) * Nk * d; /* ... and of its K/V head */
+  int64_t nvis = J->causal ? i + 1 + (Nk - Nq) : Nk;
+  if (nvis < 0) nvis = 0;
 
   int64_t c;
   for (c = 0; c < d; ++c) o_out[c] = 0.0;
@@ -120,8 +138,8 @@ static void one_row(const job_t* J, int64_t flat, double* o_out, double* lse_out
   for (int64_t j = 0; j < nvis; ++j) {
     double dot = 0.0;
     for (c = 0; c < d; ++c)
-      dot += load_elem(J->q, J->dtype, head + i * d + c) *
-             load_elem(J->k, J->dtype, head + j * d + c);
+      dot += load_elem(J->q, J->dtype, qhead + i * d + c) *
+             load_elem(J->k, J->dtype, kvhead + j * d + c);
     s[j] = J->scale * dot;
     if (s[j] > m) m = s[j];
   }
@@ -133,14 +151,14 @@ static void one_row(const job_t* J, int64_t flat, double* o_out, double* lse_out
   /* pass 3: normalised weights times value rows */
   for (int64_t j = 0; j < nvis; ++j) {
     double p = exp(s[j] - m) / l;
-    for (c = 0; c < d; ++c) o_out[c] += p * load_elem(J->v, J->dtype, head + j * d + c);
+    for (c = 0; c < d; ++c) o_out[c] += p * load_elem(J->v, J->dtype, kvhead + j * d + c);
   }
   *lse_out = m + log(l);
 }
 
 static void* worker(void* arg) {
   const job_t* J = (const job_t*)arg;
-  double* s = (double*)malloc(sizeof(double) * (size_t)(J->N > 0 ? J->N : 1));
+  double* s = (double*)malloc(sizeof(double) * (size_t)(J->Nk > 0 ? J->Nk : 1));
   if (!s) return (void*)1;
   for (int64_t r = J->first; r < J->last; ++r) {
     int64_t flat = J->rows ? J->rows[r] : r;
@@ -151,23 +169,25 @@ static void* worker(void* arg) {
 }
 
 /*
- * oracle_fwd_f64 -- q, k, v: contiguous [B, H, N, d] arrays of `dtype`.
- * rows: optional list of flat row indices ((b*H + h)*N + i); NULL means all
- * B*H*N rows in order.  o: [nrows, d] doubles, lse: [nrows] doubles.
+ * oracle_fwd_gqa_f64 -- q: contiguous [B, H, Nq, d], k and v: contiguous
+ * [B, Hkv, Nk, d], all of `dtype`; Hkv divides H.
+ * rows: optional list of flat row indices ((b*H + h)*Nq + i); NULL means all
+ * B*H*Nq rows in order.  o: [nrows, d] doubles, lse: [nrows] doubles.
  * Returns 0 on success, -1 on a bad argument, -2 when out of memory.
  */
-int oracle_fwd_f64(const void* q, const void* k, const void* v, int dtype, int64_t B,
-                   int64_t H, int64_t N, int64_t d, double scale, int causal,
-                   const int64_t* rows, int64_t nrows, double* o, double* lse,
-                   int nthreads) {
+int oracle_fwd_gqa_f64(const void* q, const void* k, const void* v, int dtype, int64_t B,
+                       int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, double scale,
+                       int causal, const int64_t* rows, int64_t nrows, double* o, double* lse,
+                       int nthreads) {
   if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return -1;
-  if (B < 0 || H < 0 || N < 0 || d <= 0 || nrows < 0) return -1;
-  if (!rows) nrows = B * H * N;
+  if (B < 0 || H < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d <= 0 || nrows < 0) return -1;
+  if (Hkv == 0 ? H != 0 : H % Hkv != 0) return -1;
+  if (!rows) nrows = B * H * Nq;
   if (nrows == 0) return 0;
-  if (!q || !k || !v || !o || !lse) return -1;
+  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return -1;
   if (rows) {
     for (int64_t r = 0; r < nrows; ++r)
-      if (rows[r] < 0 || rows[r] >= B * H * N) return -1;
+      if (rows[r] < 0 || rows[r] >= B * H * Nq) return -1;
   }
   if (nthreads < 1) nthreads = 1;
   if (nthreads > nrows) nthreads = (int)nrows;
@@ -183,7 +203,8 @@ int oracle_fwd_f64(const void* q, const void* k, const void* v, int dtype, int64
   for (int t = 0; t < nthreads; ++t) {
     job_t* J = &jobs[t];
     J->q = q; J->k = k; J->v = v; J->dtype = dtype;
-    J->H = H; J->N = N; J->d = d; J->scale = scale; J->causal = causal;
+    J->H = H; J->Hkv = Hkv; J->Nq = Nq; J->Nk = Nk; J->d = d;
+    J->scale = scale; J->causal = causal;
     J->rows = rows; J->nrows = nrows; J->o = o; J->lse = lse;
     J->first = nrows * t / nthreads;
     J->last = nrows * (t + 1) / nthreads;
@@ -201,4 +222,62 @@ int oracle_fwd_f64(const void* q, const void* k, const void* v, int dtype, int64
   free(jobs);
   free(tids);
   return rc;
+}
+
+/*
+ * oracle_fwd_f64 -- the square multi-head case: q, k, v all contiguous
+ * [B, H, N, d]; rows index ((b*H + h)*N + i).  Same returns.
+ */
+int oracle_fwd_f64(const void* q, const void* k, const void* v, int dtype, int64_t B,
+                   int64_t H, int64_t N, int64_t d, double scale, int causal,
+                   const int64_t* rows, int64_t nrows, double* o, double* lse,
+                   int nthreads) {
+  return oracle_fwd_gqa_f64(q, k, v, dtype, B, H, H, N, N, d, scale, causal, rows, nrows, o,
+                            lse, nthreads);
+}
+
+/*
+ * oracle_combine_f64 -- merge S results over disjoint key ranges.
+ *
+ * o_parts [S, rows, d]: range s's output for each row, already divided by
+ * the range's own sum of exponentials; lse_parts [S, rows]: the natural log
+ * of that sum (-inf for a range with no visible key).  Output: o [rows, d],
+ * lse [rows].
+ *
+ * A range is the "new block" of the normalised online update (pseudo-algorithm
+ * steps 4-5 of "How Did I Write My First FlashAttention Kernel in CUDA?"): a
+ * block with local maximum m~, local sum l~ and normalised output O~ = P~V/l~
+ * merges into the running (m, l, O) by
+ *     m_new = max(m, m~)
+ *     l_new = exp(m - m_new) l + exp(m~ - m_new) l~
+ *     O     = (l exp(m - m_new) O + l~ exp(m~ - m_new) O~) / l_new.
+ * The update only uses m~ and l~ through m~ + ln l~, so a range enters with
+ * m~ = LSE_s and l~ = 1.  The running state starts empty (m = -inf, l = 0,
+ * O = 0); a range with LSE_s = -inf has no keys and is skipped, so no
+ * -inf - (-inf) is ever formed.  At the end lse = m + ln l (-inf if l = 0).
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_combine_f64(const double* o_parts, const double* lse_parts, int64_t S, int64_t rows,
+                       int64_t d, double* o, double* lse) {
+  if (S < 1 || rows < 0 || d <= 0) return -1;
+  if (rows == 0) return 0;
+  if (!o_parts || !lse_parts || !o || !lse) return -1;
+  for (int64_t r = 0; r < rows; ++r) {
+    double m = -INFINITY, l = 0.0;
+    double* out = o + r * d;
+    for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+    for (int64_t s = 0; s < S; ++s) {
+      const double mt = lse_parts[s * rows + r], lt = 1.0;
+      if (mt == -INFINITY) continue;
+      const double* ot = o_parts + (s * rows + r) * d;
+      const double m_new = mt > m ? mt : m;
+      const double a_old = l * exp(m - m_new), a_new = lt * exp(mt - m_new);
+      const double l_new = a_old + a_new;
+      for (int64_t c = 0; c < d; ++c) out[c] = (a_old * out[c] + a_new * ot[c]) / l_new;
+      m = m_new;
+      l = l_new;
+    }
+    lse[r] = l > 0.0 ? m + log(l) : -INFINITY;
+  }
+  return 0;
 }

@@ -53,6 +53,16 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_fwd_gqa_f64.restype = ctypes.c_int
+        lib.oracle_fwd_gqa_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_combine_f64.restype = ctypes.c_int
+        lib.oracle_combine_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_widen.restype = ctypes.c_double
         lib.oracle_widen.argtypes = [ctypes.c_int, ctypes.c_uint32]
         _lib = lib
@@ -129,6 +139,65 @@ def fwd(q, k, v, scale: float, causal: bool, rows=None, threads: int | None = No
     if rows is None:
         return o.reshape(B, H, N, d), lse.reshape(B, H, N)
     return o[:, :d], lse
+
+
+def fwd_gqa(q, k, v, scale: float, causal: bool, rows=None, threads: int | None = None):
+    """Exact attention in fp64 with grouped K/V heads and N_q != N_kv.
+
+    q: [B, H, N_q, d]; k, v: [B, H_kv, N_kv, d] (H_kv divides H; query head
+    h reads K/V head h // (H // H_kv)).  Causal masking hides key j from
+    query i when j > i + N_kv - N_q.  ``rows`` lists flat indices
+    ``(b*H + h)*N_q + i``.  Returns ``(o, lse)`` as float64 numpy arrays:
+    [B, H, N_q, d] and [B, H, N_q] (or one row per entry of ``rows``).
+    """
+    qb, dt = _stored_bits(q)
+    kb, dtk = _stored_bits(k)
+    vb, dtv = _stored_bits(v)
+    if not (dt == dtk == dtv):
+        raise TypeError("q, k, v must share one dtype")
+    if qb.ndim != 4 or kb.ndim != 4 or kb.shape != vb.shape:
+        raise ValueError("q must be [B, H, N_q, d]; k and v one [B, H_kv, N_kv, d] shape")
+    B, H, Nq, d = (int(s) for s in qb.shape)
+    Bk, Hkv, Nk, dk = (int(s) for s in kb.shape)
+    if Bk != B or dk != d or Hkv == 0 or H % Hkv:
+        raise ValueError("q, k, v must share B and d, and H_kv must divide H")
+    scale64 = float(np.float32(scale))
+    if rows is None:
+        nrows, rows_ptr = B * H * Nq, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows, rows_ptr = int(rows_arr.size), rows_arr.ctypes.data
+    o = np.zeros((max(nrows, 0), max(d, 1)), dtype=np.float64)
+    lse = np.zeros((max(nrows, 0),), dtype=np.float64)
+    if nrows > 0:
+        rc = _load().oracle_fwd_gqa_f64(
+            qb.ctypes.data, kb.ctypes.data, vb.ctypes.data, DTYPE_CODES[dt],
+            B, H, Hkv, Nq, Nk, d, scale64, int(bool(causal)), rows_ptr, nrows,
+            o.ctypes.data, lse.ctypes.data, int(threads or default_threads()))
+        if rc != 0:
+            raise RuntimeError(f"oracle_fwd_gqa_f64 failed with code {rc}")
+    if rows is None:
+        return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
+    return o[:, :d], lse
+
+
+def combine(o_parts, lse_parts):
+    """Merge per-range results in fp64: o_parts [S, rows, d], lse_parts [S, rows].
+
+    Returns ``(o [rows, d], lse [rows])`` as float64 numpy arrays.
+    """
+    op = np.ascontiguousarray(np.asarray(o_parts, dtype=np.float64))
+    lp = np.ascontiguousarray(np.asarray(lse_parts, dtype=np.float64))
+    if op.ndim != 3 or lp.shape != op.shape[:2]:
+        raise ValueError("o_parts must be [S, rows, d] and lse_parts [S, rows]")
+    S, rows, d = op.shape
+    o = np.zeros((rows, d), dtype=np.float64)
+    lse = np.zeros((rows,), dtype=np.float64)
+    rc = _load().oracle_combine_f64(op.ctypes.data, lp.ctypes.data, S, rows, d,
+                                    o.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_combine_f64 failed with code {rc}")
+    return o, lse
 
 
 def widen(dtype: str, bits: int) -> float:

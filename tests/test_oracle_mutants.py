@@ -17,23 +17,34 @@ ROOT = Path(__file__).resolve().parents[1]
 SRC = ROOT / "oracle" / "fa_oracle.c"
 
 MUTANTS = {
-    "causal_off_by_one": ("J->causal ? i + 1 : N", "J->causal ? i : N"),
+    "causal_off_by_one": ("J->causal ? i + 1 + (Nk - Nq) : Nk", "J->causal ? i + (Nk - Nq) : Nk"),
+    "causal_offset_sign": ("J->causal ? i + 1 + (Nk - Nq) : Nk",
+                           "J->causal ? i + 1 - (Nk - Nq) : Nk"),
     "dropped_scale": ("s[j] = J->scale * dot;", "s[j] = dot;"),
-    "key_row_index": ("load_elem(J->k, J->dtype, head + j * d + c)",
-                      "load_elem(J->k, J->dtype, head + i * d + c)"),
-    "value_row_index": ("load_elem(J->v, J->dtype, head + j * d + c)",
-                        "load_elem(J->v, J->dtype, head + i * d + c)"),
-    "transposed_query": ("load_elem(J->q, J->dtype, head + i * d + c)",
-                         "load_elem(J->q, J->dtype, head + c * N + i)"),
+    "key_row_index": ("load_elem(J->k, J->dtype, kvhead + j * d + c)",
+                      "load_elem(J->k, J->dtype, kvhead + i * d + c)"),
+    "value_row_index": ("load_elem(J->v, J->dtype, kvhead + j * d + c)",
+                        "load_elem(J->v, J->dtype, kvhead + i * d + c)"),
+    "transposed_query": ("load_elem(J->q, J->dtype, qhead + i * d + c)",
+                         "load_elem(J->q, J->dtype, qhead + c * Nq + i)"),
     "dropped_normalisation": ("double p = exp(s[j] - m) / l;", "double p = exp(s[j] - m);"),
     "lse_sign": ("*lse_out = m + log(l);", "*lse_out = m - log(l);"),
     "lse_dropped_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
-    "head_offset": ("const int64_t head = bh * N * d;", "const int64_t head = bh * d;"),
+    "head_offset": ("const int64_t qhead = bh * Nq * d;", "const int64_t qhead = bh * d;"),
+    "kv_head_offset": ("(b * J->Hkv + kvh) * Nk * d;", "(b * J->Hkv + kvh) * d;"),
+    "grouped_head_map": ("const int64_t kvh = h / (J->H / J->Hkv);",
+                         "const int64_t kvh = h % J->Hkv;"),
     "max_not_subtracted_in_sum": ("l += exp(s[j] - m);", "l += exp(s[j]);"),
     "f16_bias": ("expo - 15);", "expo - 16);"),
     "f16_subnormal": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
     "bf16_shift": ("(uint32_t)bits << 16;", "(uint32_t)bits << 15;"),
     "max_uses_min": ("if (s[j] > m) m = s[j];", "if (s[j] < m || m == -INFINITY) m = s[j];"),
+    "combine_max_uses_min": ("const double m_new = mt > m ? mt : m;",
+                             "const double m_new = mt < m ? mt : m;"),
+    "combine_weight_sign": ("a_new = lt * exp(mt - m_new)", "a_new = lt * exp(m_new - mt)"),
+    "combine_dropped_old_scale": ("(a_old * out[c] + a_new * ot[c]) / l_new",
+                                  "(out[c] + a_new * ot[c]) / l_new"),
+    "combine_lse_sign": ("lse[r] = l > 0.0 ? m + log(l)", "lse[r] = l > 0.0 ? m - log(l)"),
 }
 
 

@@ -279,3 +279,132 @@ def test_row_subset_equals_full_rows(oracle_lib):
     os_, ls_ = oracle.fwd(q, k, v, 0.25, True, rows=rows)
     np.testing.assert_array_equal(os_, o.reshape(-1, d)[rows])
     np.testing.assert_array_equal(ls_, l.reshape(-1)[rows])
+
+
+# --------------------------------------------------------------------------
+# Grouped K/V heads, separate query/key lengths, merging key ranges
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,H_kv", [(4, 2), (6, 3), (4, 1), (3, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_heads_equal_repeated_kv_heads(oracle_lib, H, H_kv, causal):
+    # Query head h reads K/V head h // (H / H_kv): the same as multi-head
+    # attention on K/V whose heads are repeated H / H_kv times in place
+    # (torch fp64 reference on the repeated tensors).
+    B, N, d = 2, 13, 8
+    q = _rand((B, H, N, d), seed=71)
+    k, v = (_rand((B, H_kv, N, d), seed=s) for s in (72, 73))
+    o, lse = oracle.fwd_gqa(q, k, v, 0.3, causal)
+    g = H // H_kv
+    kr, vr = (t.repeat_interleave(g, dim=1).contiguous() for t in (k, v))
+    sc = float(np.float32(0.3))
+    q64, k64, v64 = (t.to(torch.float64) for t in (q, kr, vr))
+    logits = sc * torch.matmul(q64, k64.transpose(-1, -2).contiguous())
+    if causal:
+        logits = logits.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    ref = torch.matmul(torch.softmax(logits, -1), v64).numpy()
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(logits, -1).numpy(), rtol=1e-13, atol=1e-13)
+    o2, l2 = oracle.fwd(q, kr, vr, 0.3, causal)
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("n_q", [1, 2, 5, 17])
+def test_causal_rows_stand_at_the_end_of_the_keys(oracle_lib, n_q):
+    # With N_q < N_kv, causal query row i stands at key position
+    # N_kv - N_q + i: the N_q rows equal the last N_q rows of square causal
+    # attention over the same keys.  N_q = 1 (a decoding step) sees every key.
+    B, H, N, d = 1, 2, 17, 8
+    q, k, v = (_rand((B, H, N, d), seed=s) for s in (81, 82, 83))
+    o_full, l_full = oracle.fwd(q, k, v, 0.4, True)
+    qs = q[:, :, N - n_q:].contiguous()
+    o, lse = oracle.fwd_gqa(qs, k, v, 0.4, True)
+    np.testing.assert_array_equal(o, o_full[:, :, N - n_q:])
+    np.testing.assert_array_equal(lse, l_full[:, :, N - n_q:])
+    if n_q == 1:
+        o_nc, l_nc = oracle.fwd_gqa(qs, k, v, 0.4, False)
+        np.testing.assert_array_equal(o, o_nc)
+        np.testing.assert_array_equal(lse, l_nc)
+
+
+def test_more_queries_than_keys_leaves_early_rows_empty(oracle_lib):
+    # N_q > N_kv, causal: rows i < N_q - N_kv see no key (O = 0, LSE = -inf);
+    # the last N_kv rows are square causal attention over the keys.
+    B, H, Nq, Nk, d = 1, 2, 11, 6, 8
+    q = _rand((B, H, Nq, d), seed=91)
+    k, v = (_rand((B, H, Nk, d), seed=s) for s in (92, 93))
+    o, lse = oracle.fwd_gqa(q, k, v, 0.5, True)
+    e = Nq - Nk
+    assert np.all(o[:, :, :e] == 0.0) and np.all(np.isneginf(lse[:, :, :e]))
+    o_sq, l_sq = oracle.fwd(q[:, :, e:].contiguous(), k, v, 0.5, True)
+    np.testing.assert_array_equal(o[:, :, e:], o_sq)
+    np.testing.assert_array_equal(lse[:, :, e:], l_sq)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(1, 40), (7, 33), (30, 9)])
+def test_rectangular_non_causal_matches_library_softmax(oracle_lib, Nq, Nk):
+    from scipy.special import logsumexp, softmax
+    d = 16
+    q = _rand((1, 1, Nq, d), seed=101)
+    k, v = (_rand((1, 1, Nk, d), seed=s) for s in (102, 103))
+    o, lse = oracle.fwd_gqa(q, k, v, 0.25, False)
+    s = float(np.float32(0.25)) * (_f64(q[0, 0]) @ _f64(k[0, 0]).T)
+    np.testing.assert_allclose(o[0, 0], softmax(s, axis=1) @ _f64(v[0, 0]), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], logsumexp(s, axis=1), rtol=1e-13, atol=1e-13)
+
+
+def test_zero_keys_gives_empty_rows(oracle_lib):
+    q = _rand((1, 2, 3, 8), seed=104)
+    k = torch.zeros((1, 1, 0, 8))
+    o, lse = oracle.fwd_gqa(q, k, k, 0.5, False)
+    assert np.all(o == 0.0) and np.all(np.isneginf(lse))
+
+
+def _range_partials(q, k, v, scale, cuts):
+    """Oracle results of each key range [cuts[i], cuts[i+1]) (non-causal)."""
+    os_, ls_ = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        o, l = oracle.fwd_gqa(q, k[:, :, a:b].contiguous(), v[:, :, a:b].contiguous(), scale, False)
+        os_.append(o.reshape(-1, q.shape[-1]))
+        ls_.append(l.reshape(-1))
+    return np.stack(os_), np.stack(ls_)
+
+
+@pytest.mark.parametrize("cuts", [[0, 40], [0, 1, 40], [0, 13, 14, 27, 40], [0, 0, 20, 20, 40],
+                                  list(range(41))])
+def test_combine_of_key_ranges_equals_full_attention(oracle_lib, cuts):
+    # Splitting the keys into ranges, attending to each, and merging by
+    # logsumexp gives attention over all keys (empty ranges included: they
+    # carry LSE = -inf and must drop out).
+    B, H, N, d = 2, 2, 40, 8
+    q, k, v = (_rand((B, H, N, d), scale=1.5, seed=s) for s in (111, 112, 113))
+    o_full, l_full = oracle.fwd(q, k, v, 0.3, False)
+    op, lp = _range_partials(q, k, v, 0.3, cuts)
+    o, lse = oracle.combine(op, lp)
+    np.testing.assert_allclose(o, o_full.reshape(-1, d), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, l_full.reshape(-1), rtol=1e-13, atol=1e-13)
+    # the order of the ranges does not matter
+    perm = np.random.default_rng(114).permutation(len(cuts) - 1)
+    o2, l2 = oracle.combine(op[perm], lp[perm])
+    np.testing.assert_allclose(o2, o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(l2, lse, rtol=1e-14, atol=1e-14)
+
+
+def test_combine_closed_forms(oracle_lib):
+    # Two ranges with equal LSE a: the plain average, LSE a + ln 2.  One
+    # range: unchanged.  Only empty ranges: O = 0, LSE = -inf.
+    g = np.random.default_rng(115)
+    o1, o2 = g.standard_normal((2, 3, 4))
+    a = np.array([0.5, -3.0, 40.0])
+    o, lse = oracle.combine(np.stack([o1, o2]), np.stack([a, a]))
+    np.testing.assert_allclose(o, (o1 + o2) / 2, rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(lse, a + math.log(2.0), rtol=1e-15)
+    o, lse = oracle.combine(o1[None], a[None])
+    np.testing.assert_allclose(o, o1, rtol=1e-15, atol=0)
+    np.testing.assert_array_equal(lse, a)
+    o, lse = oracle.combine(np.zeros((3, 3, 4)), np.full((3, 3), -np.inf))
+    assert np.all(o == 0.0) and np.all(np.isneginf(lse))
+    # weights e^(LSE_s - LSE): ranges with LSE 0 and ln 3 weigh 1/4 and 3/4
+    o, lse = oracle.combine(np.stack([o1, o2]), np.stack([np.zeros(3), np.full(3, math.log(3.0))]))
+    np.testing.assert_allclose(o, 0.25 * o1 + 0.75 * o2, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse, np.full(3, math.log(4.0)), rtol=1e-15)
