@@ -5,7 +5,10 @@
 One step is one call of the whole forward pass (``fa_fwd``: one kernel) over
 the workload's inputs, which are resident in HBM before timing starts.  The
 default workload is the bf16 long-sequence shape B=1 H=16 N=16384 d=64,
-non-causal.  Prints ONE JSON line with:
+non-causal.  Workloads with grouped K/V heads, their own key length or a key
+split (C1s, D1, G1, G2) run through ``fa_fwd_ex`` instead: one step is then
+the whole call (the split kernel and, when split, the combine kernel), with
+its workspace allocated before timing.  Prints ONE JSON line with:
 
   value / ms_per_step   whole-job throughput (metric FLOPs 4*B*H*N^2*d, halved
                         when causal) from a wall clock around K steps,
@@ -13,7 +16,9 @@ non-causal.  Prints ONE JSON line with:
   roofline              the kernel's own average duration from HIP events
                         recorded on the launch stream around every timed
                         launch, against the MI355X dense MFMA peak of the
-                        input dtype; ``traffic`` is the HBM bytes per launch
+                        input dtype, or against HBM bandwidth (8 TB/s)
+                        when the workload's FLOP per algorithmic byte is
+                        below the ridge point; ``traffic`` is the HBM bytes per launch
                         from the committed rocprofv3 counter summary when it
                         was taken on the current kernel source, else null;
   cpu_baseline          the fp64 oracle timed on the host cores on a bounded
@@ -34,10 +39,11 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 METRIC = "fwd attention TFLOP/s & % MFMA peak, bf16 B=1 H=16 N=16384 d=64 (1 GPU)"
-# MI355X published dense peaks (TFLOP/s) per input dtype.
+# MI355X published dense peaks (TFLOP/s) per input dtype, and HBM bandwidth.
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_fwd_h16.hip", "fa_fwd_f32.hip",
-                  "fa_api.hip"]
+                  "fa_api.hip", "fa_combine.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -73,23 +79,25 @@ def cpu_baseline(w, q, k, v, target_s: float):
 
     threads = default_threads()
     pair_flops = 4.0 * w.d
+    nk = w.n_kv
 
     def rows_flops(rows):
-        n = w.N
-        vis = (rows % n + 1) if w.causal else np.full(rows.shape, n)
+        i = rows % w.N
+        vis = np.clip(i + 1 + nk - w.N, 0, nk) if w.causal else np.full(rows.shape, nk)
         return float(vis.sum()) * pair_flops
 
     rng = np.random.default_rng(99)
     total = w.B * w.H * w.N
     calib = np.sort(rng.choice(total, size=min(256, total), replace=False)).astype(np.int64)
     t0 = time.perf_counter()
-    oracle.fwd(q, k, v, w.scale, w.causal, rows=calib, threads=threads)
+    oracle.fwd_gqa(q, k, v, w.scale, w.causal, rows=calib, threads=threads)
     dt = max(time.perf_counter() - t0, 1e-3)
-    rate = rows_flops(calib) / dt
-    want = int(min(total, max(256, target_s * rate / (pair_flops * (w.N if not w.causal else w.N / 2)))))
+    rate = rows_flops(calib) / max(dt, 1e-9)
+    per_row = max(rows_flops(calib) / len(calib), 1.0)
+    want = int(min(total, max(256, target_s * rate / per_row)))
     rows = np.sort(rng.choice(total, size=want, replace=False)).astype(np.int64)
     t0 = time.perf_counter()
-    oracle.fwd(q, k, v, w.scale, w.causal, rows=rows, threads=threads)
+    oracle.fwd_gqa(q, k, v, w.scale, w.causal, rows=rows, threads=threads)
     dt = time.perf_counter() - t0
     fl = rows_flops(rows)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
@@ -105,6 +113,12 @@ def main():
     ap.add_argument("--workload", default="C4")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--read-bytes", type=int, default=0,
+                    help="instead of attention, time a plain reduction that reads this many "
+                         "bytes (the streaming-read rate a bandwidth-bound kernel can expect)")
+    ap.add_argument("--splits", type=int, default=None,
+                    help="key ranges for fa_fwd_ex workloads (default: the workload's, "
+                         "0 = the library's choice)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, run a plain device copy of this many bytes "
                          "(calibrates the HBM traffic counters)")
@@ -129,8 +143,26 @@ def main():
         print(json.dumps({"copy_bytes": n * 4, "launches": max(1, args.steps)}), flush=True)
         return
 
+    if args.read_bytes:
+        x = torch.ones(args.read_bytes // 4, dtype=torch.float32, device="cuda:0")
+        for _ in range(max(1, args.warmup)):
+            x.sum()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(max(1, args.steps)):
+            x.sum()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / max(1, args.steps)
+        print(json.dumps({"read_bytes": x.numel() * 4, "ms": round(ms, 5),
+                          "GB/s": round(x.numel() * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
+
     binding.load()  # fails loudly when libfa.so is missing
     w = WORKLOADS[args.workload]
+    if args.splits is not None:
+        w = w.with_(splits=args.splits)
     q, k, v = make_inputs(w)
     dev = torch.device("cuda:0")
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
@@ -138,8 +170,24 @@ def main():
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    splits, workspace = 1, None
+    if w.extended:
+        dt_code = {"f32": binding.FA_F32, "bf16": binding.FA_BF16, "f16": binding.FA_F16}[w.dtype]
+        splits = w.splits or binding.default_splits(w.B, w.H, w.h_kv, w.N, w.n_kv, w.d,
+                                                    w.causal, dt_code)
+        need = binding.workspace_bytes(w.B, w.H, w.N, w.n_kv, w.d, splits)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+
+        def step():
+            binding.fwd_ex(qd, kd, vd, w.scale, w.causal, num_splits=splits, out=o, lse=lse,
+                           workspace=workspace, stream=stream)
+    else:
+        def step():
+            binding.fwd(qd, kd, vd, w.scale, w.causal, out=o, lse=lse, stream=stream)
+
     for _ in range(args.warmup):
-        binding.fwd(qd, kd, vd, w.scale, w.causal, out=o, lse=lse, stream=stream)
+        step()
     torch.cuda.synchronize()
 
     # Kernel duration: events on the launch stream around every launch.
@@ -149,7 +197,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        binding.fwd(qd, kd, vd, w.scale, w.causal, out=o, lse=lse, stream=stream)
+        step()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -159,8 +207,12 @@ def main():
 
     flops = w.flops
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (avg_kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
+    hbm_bound = flops / w.io_bytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm_bound:
+        achieved, peak, unit = w.io_bytes / (avg_kernel_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, unit = flops / (avg_kernel_ms * 1e-3) / 1e12, "TFLOP/s"
     traffic = read_traffic(w.name)
 
     out = {
@@ -177,12 +229,16 @@ def main():
         "dtype": w.dtype,
         "data": f"synthetic: seeded ({w.dist}, numpy PCG64 seed {w.seed}) Q/K/V rounded to {w.dtype}",
         "config": {"workload": f"{w.name}: {w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} "
-                               f"{'causal' if w.causal else 'non-causal'}",
+                               f"{'causal' if w.causal else 'non-causal'}" + (
+                                   f" H_kv={w.h_kv} N_kv={w.n_kv} splits={splits} (fa_fwd_ex)"
+                                   if w.extended else ""),
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "flops_per_step": flops, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic,
+        "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "algorithmic_bytes": w.io_bytes,
+                     "timed": ("fa_fwd_ex call: split kernel + combine kernel" if splits > 1
+                               else "one forward kernel"),
                      "kernel_ms_avg": round(avg_kernel_ms, 5),
                      "kernel_ms_min": round(kernel_ms[0], 5),
                      "kernel_ms_median": round(kernel_ms[len(kernel_ms) // 2], 5)},

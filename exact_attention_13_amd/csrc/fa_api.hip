@@ -14,10 +14,19 @@
 #include "fa_device.hpp"
 
 #define LIBFA_VERSION_MAJOR 0
-#define LIBFA_VERSION_MINOR 1
+#define LIBFA_VERSION_MINOR 2
 #define LIBFA_VERSION_PATCH 0
 
 namespace {
+
+// Keys per split are a multiple of this (the largest key tile of any kernel).
+constexpr int64_t kSplitGranule = 64;
+// Most key ranges per problem a split launch uses.
+constexpr int64_t kMaxSplits = 256;
+// Rows past the end that a kernel may address (rounded-up tiles) before its
+// buffer range check turns them into zeros; every such byte offset must
+// still fit in 32 bits.
+constexpr int64_t kRowSlack = 1024;
 
 bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   if (!a || !b || na <= 0 || nb <= 0) return false;
@@ -27,74 +36,247 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 
 bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
-}  // namespace
+bool valid_dtype(fa_dtype t) { return (int)t >= (int)FA_F32 && (int)t <= (int)FA_F16; }
 
-extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                            int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
-                            fa_dtype dtype, void* stream) {
-  if (!q || !k || !v || !o) return FA_ERR_NULL;
-  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
-  if ((int)dtype < (int)FA_F32 || (int)dtype > (int)FA_F16) return FA_ERR_DTYPE;
+int64_t elem_bytes(fa_dtype t) { return t == FA_F32 ? 4 : 2; }
+
+// How the (batch, head) problems of a call are laid out for the kernels.
+struct Plan {
+  bool causal;       // a mask remains after the reductions below
+  int64_t problems;  // independent problems
+  int64_t nq;        // query rows per problem
+  int64_t hp, hkv, grp;
+  int64_t rows;      // B * H * N_q, the rows of o and lse
+  int64_t rpb;       // query rows per workgroup of the chosen instance
+  int64_t blocks;    // workgroups of an unsplit launch
+};
+
+// Shapes are assumed validated (non-negative, H_kv > 0, H % H_kv == 0).
+Plan make_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t d, int causal,
+               fa_dtype dtype) {
+  Plan p;
+  // One query row aligned to the end of the keys sees every key: no mask.
+  p.causal = causal != 0 && N_q > 1;
+  const int64_t g = H / H_kv;
+  // Without a row-dependent mask the query heads of a group are packed into
+  // the rows of one problem: they are adjacent in memory and share K/V.
+  const bool packed = g > 1 && !p.causal;
+  p.problems = B * (packed ? H_kv : H);
+  p.nq = packed ? g * N_q : N_q;
+  p.hp = packed ? H_kv : H;
+  p.hkv = H_kv;
+  p.grp = packed ? 1 : g;
+  p.rows = B * H * N_q;
+  p.rpb = dtype == FA_F32 ? fa_impl::f32_rows_per_block()
+                          : fa_impl::h16_rows_per_block((int)d, p.causal, p.nq);
+  p.blocks = p.problems * ((p.nq + p.rpb - 1) / p.rpb);
+  return p;
+}
+
+// Effective number of key ranges and keys per range for a requested count.
+void split_keys(int64_t N_kv, int64_t want, int64_t* splits, int64_t* chunk) {
+  const int64_t granules = (N_kv + kSplitGranule - 1) / kSplitGranule;
+  if (want <= 1 || granules <= 1) {
+    *splits = 1;
+    *chunk = granules * kSplitGranule;
+    return;
+  }
+  if (want > kMaxSplits) want = kMaxSplits;
+  const int64_t per = (granules + want - 1) / want;
+  *splits = (granules + per - 1) / per;
+  *chunk = per * kSplitGranule;
+}
+
+// Shared validation of the extended call; fills the plan on success.
+fa_status check_ex(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
+                   int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t d, float scale,
+                   fa_dtype dtype) {
+  // k and v are never read when there are no keys
+  if (!q || !o || ((!k || !v) && N_kv != 0)) return FA_ERR_NULL;
+  if (B < 0 || H < 0 || H_kv < 0 || N_q < 0 || N_kv < 0) return FA_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return FA_ERR_DTYPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
-  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  if (H_kv == 0 ? H != 0 : H % H_kv != 0) return FA_ERR_SHAPE;
+  return FA_OK;
+}
 
-  // Sizes: N and B*H must fit the kernels' 32-bit per-head indices (element
-  // offsets are 64-bit), byte counts must not overflow, and the workgroup
-  // count must fit the grid.
-  if (N > INT32_MAX || B > INT32_MAX / H) return FA_ERR_SHAPE;
-  const int64_t bh = B * H;
-  const int64_t elem = dtype == FA_F32 ? 4 : 2;
-  if (bh > INT64_MAX / N || bh * N > INT64_MAX / (d * elem)) return FA_ERR_SHAPE;
-  const int64_t rows = bh * N;
-  // one head's rows are addressed with 32-bit byte offsets (buffer loads)
-  if ((N + 256) * d * elem > INT32_MAX) return FA_ERR_SHAPE;
-  const int64_t grid = dtype == FA_F32 ? fa_impl::f32_grid_blocks(bh, N)
-                                       : fa_impl::h16_grid_blocks(bh, N);
-  if (grid > INT32_MAX) return FA_ERR_SHAPE;
+// Size limits of a non-empty call: 32-bit per-head indices and byte
+// offsets, no overflow of byte counts, grids that fit.
+fa_status check_sizes(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t d,
+                      fa_dtype dtype, const Plan& p, int64_t splits) {
+  const int64_t e = elem_bytes(dtype);
+  if (N_q > INT32_MAX || N_kv > INT32_MAX || H > INT32_MAX || B > INT32_MAX / H)
+    return FA_ERR_SHAPE;
+  const int64_t bh = B * H, bhkv = B * H_kv;
+  if (bh > INT64_MAX / N_q || bh * N_q > INT64_MAX / (d * 4 * kMaxSplits)) return FA_ERR_SHAPE;
+  if (N_kv > 0 && (bhkv > INT64_MAX / N_kv || bhkv * N_kv > INT64_MAX / (d * e)))
+    return FA_ERR_SHAPE;
+  if (p.problems > INT32_MAX || p.nq > INT32_MAX) return FA_ERR_SHAPE;
+  if ((p.nq + kRowSlack) * d * e > INT32_MAX || (N_kv + kRowSlack) * d * e > INT32_MAX)
+    return FA_ERR_SHAPE;
+  if (p.blocks > INT32_MAX / splits) return FA_ERR_SHAPE;
+  if (splits > 1 && fa_impl::combine_grid_blocks(p.rows, (int)d) > INT32_MAX) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+fa_status launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv,
+                               int64_t d, float scale, int causal, fa_dtype dtype,
+                               int64_t num_splits, void* workspace, int64_t workspace_bytes,
+                               void* stream) {
+  fa_status st = check_ex(q, k, v, o, B, H, H_kv, N_q, N_kv, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (num_splits < 1) return FA_ERR_WORKSPACE;
+  if (B == 0 || H == 0 || N_q == 0) return FA_OK;
+
+  const Plan p = make_plan(B, H, H_kv, N_q, d, causal, dtype);
+  int64_t splits, chunk;
+  split_keys(N_kv, num_splits, &splits, &chunk);
+  st = check_sizes(B, H, H_kv, N_q, N_kv, d, dtype, p, splits);
+  if (st != FA_OK) return st;
 
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
     return FA_ERR_ALIGN;
   if (lse && !aligned(lse, 4)) return FA_ERR_ALIGN;
 
-  const int64_t tbytes = rows * d * elem;
-  const int64_t lbytes = rows * 4;
-  if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, tbytes) ||
-      overlaps(o, tbytes, v, tbytes))
+  const int64_t e = elem_bytes(dtype);
+  const int64_t qbytes = p.rows * d * e;
+  const int64_t kvbytes = B * H_kv * N_kv * d * e;
+  const int64_t lbytes = p.rows * 4;
+  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kvbytes) ||
+      overlaps(o, qbytes, v, kvbytes))
     return FA_ERR_ALIAS;
-  if (lse && (overlaps(lse, lbytes, q, tbytes) || overlaps(lse, lbytes, k, tbytes) ||
-              overlaps(lse, lbytes, v, tbytes) || overlaps(lse, lbytes, o, tbytes)))
+  if (lse && (overlaps(lse, lbytes, q, qbytes) || overlaps(lse, lbytes, k, kvbytes) ||
+              overlaps(lse, lbytes, v, kvbytes) || overlaps(lse, lbytes, o, qbytes)))
     return FA_ERR_ALIAS;
+
+  const int64_t wbytes = splits > 1 ? splits * p.rows * (d + 1) * 4 : 0;
+  if (splits > 1) {
+    if (!workspace || workspace_bytes < wbytes || !aligned(workspace, 16))
+      return FA_ERR_WORKSPACE;
+    if (overlaps(workspace, wbytes, q, qbytes) || overlaps(workspace, wbytes, k, kvbytes) ||
+        overlaps(workspace, wbytes, v, kvbytes) || overlaps(workspace, wbytes, o, qbytes) ||
+        (lse && overlaps(workspace, wbytes, lse, lbytes)))
+      return FA_ERR_ALIAS;
+  }
 
   fa_impl::FwdArgs a;
   a.q = q;
   a.k = k;
   a.v = v;
-  a.o = o;
-  a.lse = lse;
-  a.bh = (int)bh;
-  a.n = (int)N;
+  a.problems = (int)p.problems;
+  a.nq = (int)p.nq;
+  a.nk = (int)N_kv;
+  a.hp = (int)p.hp;
+  a.hkv = (int)p.hkv;
+  a.grp = (int)p.grp;
+  a.causal_off = (int)(N_kv - N_q);
+  a.splits = (int)splits;
+  a.kv_chunk = (int)chunk;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  float* ws_o = (float*)workspace;
+  float* ws_lse = splits > 1 ? ws_o + splits * p.rows * d : nullptr;
+  a.o = splits > 1 ? (void*)ws_o : o;
+  a.lse = splits > 1 ? ws_lse : lse;
 
   hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = dtype == FA_F32
-                           ? fa_impl::launch_fwd_f32((int)d, causal != 0, a, s)
-                           : fa_impl::launch_fwd_h16(dtype == FA_BF16, (int)d, causal != 0, a, s);
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  const bool split = splits > 1;
+  st = launch_status(dtype == FA_F32
+                         ? fa_impl::launch_fwd_f32((int)d, p.causal, split, a, s)
+                         : fa_impl::launch_fwd_h16(dtype == FA_BF16, (int)d, p.causal, split, a, s));
+  if (st != FA_OK || !split) return st;
+  return launch_status(fa_impl::launch_lse_combine(ws_o, ws_lse, (int)splits, p.rows, (int)d, o,
+                                                   lse, (int)dtype, s));
+}
+
+extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                            fa_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  return fa_fwd_ex(q, k, v, o, lse, B, H, H, N, N, d, scale, causal, dtype, 1, nullptr, 0,
+                   stream);
+}
+
+extern "C" int64_t fa_fwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t N_q, int64_t N_kv,
+                                             int64_t d, int64_t num_splits) {
+  if (B <= 0 || H <= 0 || N_q <= 0 || N_kv < 0 || d <= 0 || num_splits < 1) return 0;
+  int64_t splits, chunk;
+  split_keys(N_kv, num_splits, &splits, &chunk);
+  if (splits <= 1) return 0;
+  if (B > INT64_MAX / H || B * H > INT64_MAX / N_q ||
+      B * H * N_q > INT64_MAX / ((d + 1) * 4 * splits))
+    return -1;
+  return splits * B * H * N_q * (d + 1) * 4;
+}
+
+extern "C" int64_t fa_fwd_ex_default_splits(int64_t B, int64_t H, int64_t H_kv, int64_t N_q,
+                                            int64_t N_kv, int64_t d, int causal,
+                                            fa_dtype dtype) {
+  if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || N_q <= 0 || N_kv <= 0) return 1;
+  if ((d != 64 && d != 128) || !valid_dtype(dtype)) return 1;
+  const Plan p = make_plan(B, H, H_kv, N_q, d, causal, dtype);
+  // Aim for two workgroups per compute unit (256 CUs).  More ranges do not
+  // stream K/V faster (a decoding step already reads at the rate a plain
+  // streaming read reaches) but cost partial results and a longer combine.
+  // Each range keeps enough keys that its fixed costs (Q load, partial
+  // write) stay small.
+  const int64_t target = 512;
+  if (p.blocks >= target / 2) return 1;
+  int64_t want = (target + p.blocks - 1) / p.blocks;
+  const int64_t min_keys = dtype == FA_F32 ? 64 : 256;
+  int64_t most = N_kv / min_keys;
+  if (most < 1) most = 1;
+  if (want > most) want = most;
+  if (want > kMaxSplits) want = kMaxSplits;
+  int64_t splits, chunk;
+  split_keys(N_kv, want, &splits, &chunk);
+  return splits;
+}
+
+extern "C" fa_status fa_lse_combine(const float* o_part, const float* lse_part, int64_t splits,
+                                    int64_t rows, int64_t d, void* o, float* lse,
+                                    fa_dtype dtype, void* stream) {
+  if (!o_part || !lse_part || !o) return FA_ERR_NULL;
+  if (rows < 0 || splits < 1 || splits > INT32_MAX) return FA_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (rows == 0) return FA_OK;
+  if (rows > INT64_MAX / (splits * (d + 1) * 4)) return FA_ERR_SHAPE;
+  if (fa_impl::combine_grid_blocks(rows, (int)d) > INT32_MAX) return FA_ERR_SHAPE;
+  if (!aligned(o_part, 16) || !aligned(o, 16) || !aligned(lse_part, 4)) return FA_ERR_ALIGN;
+  if (lse && !aligned(lse, 4)) return FA_ERR_ALIGN;
+  const int64_t pbytes = splits * rows * d * 4, plbytes = splits * rows * 4;
+  const int64_t obytes = rows * d * elem_bytes(dtype), lbytes = rows * 4;
+  if (overlaps(o, obytes, o_part, pbytes) || overlaps(o, obytes, lse_part, plbytes))
+    return FA_ERR_ALIAS;
+  if (lse && (overlaps(lse, lbytes, o_part, pbytes) || overlaps(lse, lbytes, lse_part, plbytes) ||
+              overlaps(lse, lbytes, o, obytes)))
+    return FA_ERR_ALIAS;
+  return launch_status(fa_impl::launch_lse_combine(o_part, lse_part, (int)splits, rows, (int)d, o,
+                                                   lse, (int)dtype, (hipStream_t)stream));
 }
 
 extern "C" const char* fa_strerror(fa_status s) {
   switch (s) {
     case FA_OK: return "success";
-    case FA_ERR_NULL: return "q, k, v or o is a null pointer";
-    case FA_ERR_SHAPE: return "B, H or N is negative or the problem exceeds the supported size";
+    case FA_ERR_NULL: return "a required pointer argument is null";
+    case FA_ERR_SHAPE:
+      return "a size is negative, H is not a multiple of H_kv, or the problem exceeds the "
+             "supported size";
     case FA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
     case FA_ERR_DTYPE: return "dtype is not FA_F32, FA_BF16 or FA_F16";
     case FA_ERR_SCALE: return "scale must be finite and greater than zero";
-    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
-    case FA_ERR_ALIAS: return "o or lse overlaps another argument buffer";
+    case FA_ERR_ALIGN: return "tensor pointers must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_ALIAS: return "an output or workspace buffer overlaps another argument buffer";
     case FA_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+    case FA_ERR_WORKSPACE:
+      return "num_splits is below 1, or the workspace is null, too small or misaligned";
   }
   return "unknown fa_status value";
 }

@@ -29,19 +29,48 @@ constexpr float kLn2 = 0.693147180559945309417f;
 // depend on the shift, so the result is the same up to rounding.
 constexpr float kRescaleLog2 = 8.0f;
 
-// Arguments common to every forward kernel.  Pointers are the caller's
-// [B, H, N, d] buffers; `bh` = B*H independent heads.
+// Arguments common to every forward kernel.
+//
+// The work is a set of independent attention problems.  Problem p has `nq`
+// query rows at q + p*nq*d (o and lse likewise) and reads the K/V head
+// kv(p) = (p / hp) * hkv + (p % hp) / grp, whose `nk` key rows start at
+// k + kv(p)*nk*d (v likewise).  Plain multi-head attention is hp = hkv = H,
+// grp = 1, nq = nk = N.  Grouped heads either map several query heads to one
+// K/V head (grp = H / H_kv) or, when no mask depends on the row, are packed
+// into the rows of one problem (nq = grp * N_q, grp = 1): the group's query
+// heads are adjacent in memory, so the packed rows are contiguous.
+//
+// Causal masking hides key j from row i when j > i + causal_off.
+//
+// Split launches cut the keys into ranges of kv_chunk keys (a multiple of
+// 64, so of every tile size): workgroup (p, split) attends to keys
+// [split*kv_chunk, min((split+1)*kv_chunk, nk)) only and writes its partial
+// result in fp32, already divided by its own row sum, to
+// o + ((split*problems + p)*nq + i)*d, and its partial logsumexp to
+// lse[(split*problems + p)*nq + i].
 struct FwdArgs {
   const void* q;
   const void* k;
   const void* v;
   void* o;
-  float* lse;      // may be null
-  int bh;          // B*H
-  int n;           // sequence length
+  float* lse;      // may be null unless split
+  int problems;    // independent (batch, head) problems
+  int nq;          // query rows per problem
+  int nk;          // key rows per K/V head
+  int hp;          // problems per batch entry
+  int hkv;         // K/V heads per batch entry
+  int grp;         // consecutive problems that share one K/V head
+  int causal_off;  // key j visible to row i iff j <= i + causal_off
+  int splits;      // key ranges per problem (1: no split)
+  int kv_chunk;    // keys per range when split
   float scale;     // multiplier of q.k
   float scale_log2;  // scale * log2(e): scores enter exp2 in this unit
 };
+
+// K/V head read by problem p.
+__device__ __forceinline__ int kv_head(const FwdArgs& a, int p) {
+  return (p / a.hp) * a.hkv + (p % a.hp) / a.grp;
+}
 
 // ---------------------------------------------------------------------------
 // Workgroup -> tile mapping.
@@ -96,12 +125,25 @@ __host__ __device__ constexpr int swap23(int kk) {
   return (kk & ~0xC) | ((kk & 4) << 1) | ((kk & 8) >> 1);
 }
 
-// Host-side launchers (one per element-type family).
-hipError_t launch_fwd_h16(bool bf16, int d, bool causal, const FwdArgs& a, hipStream_t s);
-hipError_t launch_fwd_f32(int d, bool causal, const FwdArgs& a, hipStream_t s);
+// Host-side launchers (one per element-type family).  `split` selects the
+// partial-output kernels (a.splits > 1).
+hipError_t launch_fwd_h16(bool bf16, int d, bool causal, bool split, const FwdArgs& a,
+                          hipStream_t s);
+hipError_t launch_fwd_f32(int d, bool causal, bool split, const FwdArgs& a, hipStream_t s);
 
-// Workgroup count of a launch (the host checks it fits the grid limit).
-int64_t h16_grid_blocks(int64_t bh, int64_t n);
-int64_t f32_grid_blocks(int64_t bh, int64_t n);
+// Merge `splits` partial results (fp32 O divided by its own row sum, and its
+// logsumexp) of `rows` rows of head size d into O of the I/O type and LSE.
+// dtype: 0 fp32, 1 bf16, 2 fp16.
+hipError_t launch_lse_combine(const float* o_part, const float* lse_part, int splits,
+                              int64_t rows, int d, void* o, float* lse, int dtype,
+                              hipStream_t s);
+
+// Workgroups of a combine launch over `rows` rows of head size d.
+int64_t combine_grid_blocks(int64_t rows, int d);
+
+// Query rows per workgroup of the instance a launch would use (the host
+// sizes grids and split counts with it).
+int h16_rows_per_block(int d, bool causal, int64_t nq);
+int f32_rows_per_block();
 
 }  // namespace fa_impl

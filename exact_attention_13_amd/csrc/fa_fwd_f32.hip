@@ -1,8 +1,8 @@
 // fa_fwd_f32.hip -- FlashAttention forward, fp32 in / fp32 MFMA / fp32 out,
 // for MI355X (gfx950).
 //
-// Same schedule as the bf16/fp16 kernel (one workgroup per (batch*head,
-// 128-query tile), four wave64s of 32 queries, K/V tiles of 64 keys double
+// Same schedule as the bf16/fp16 kernel (one workgroup per (problem,
+// 128-query tile[, key range]), four wave64s of 32 queries, K/V tiles of 64 keys double
 // buffered in LDS, S^T = K Q^T so that each lane holds one query's scores,
 // online softmax with exp2, one division by l at the end), with fp32 data:
 //   * both products run on v_mfma_f32_32x32x2_f32 (2-deep contraction per
@@ -46,7 +46,7 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, int total) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(16))) float lds[T::kLdsFloats];
@@ -56,22 +56,26 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
   // it) scalar instead of exec-masked
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, grp = lane >> 5;
-  const int N = a.n;
+  const int NQ = a.nq, NK = a.nk;
 
+  // logical tile -> (problem, key range, query tile)
   const int L = xcd_remap(blockIdx.x, total);
-  const int bh = L / n_qt;
-  int qt = L - bh * n_qt;
+  const int pr_sp = L / n_qt;
+  int qt = L - pr_sp * n_qt;
   if (CAUSAL) qt = n_qt - 1 - qt;
+  const int split = SPLIT ? pr_sp % a.splits : 0;
+  const int prob = SPLIT ? pr_sp / a.splits : pr_sp;
 
-  const int64_t head = (int64_t)bh * N * D;
-  const int head_bytes = N * D * 4;
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const float*)a.q + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const float*)a.k + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const float*)a.v + head, head_bytes);
+  const int64_t qhead = (int64_t)prob * NQ * D;
+  const int64_t kvhead = (int64_t)kv_head(a, prob) * NK * D;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const float*)a.q + qhead, NQ * D * 4);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const float*)a.k + kvhead, NK * D * 4);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const float*)a.v + kvhead, NK * D * 4);
 
   const int q0 = qt * kBM;
   const int qw0 = q0 + wave * kQPerWave;
   const int my_q = qw0 + col;
+  const int off = a.causal_off;
 
   // Q fragment: lane (col, grp) holds Q[my_q][8j + 4grp + e], e = 0..3; rows
   // past the end read as zero.
@@ -80,16 +84,20 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
   for (int j = 0; j < D / 8; ++j)
     qf[j] = __builtin_bit_cast(f32x4, buf_load16(qr, (my_q * D + j * 8 + grp * 4) * 4));
 
-  const int kv_end = CAUSAL ? min(q0 + kBM, N) : N;
-  const int n_kv = (kv_end + kBN - 1) / kBN;
-  const int wave_kv_end = CAUSAL ? min(qw0 + kQPerWave, N) : N;
+  // Keys of this workgroup and of this wave, as in the bf16/fp16 kernel.
+  const int kbeg = SPLIT ? split * a.kv_chunk : 0;
+  int kstop = SPLIT ? min(kbeg + a.kv_chunk, NK) : NK;
+  if (CAUSAL) kstop = min(kstop, q0 + kBM + off);
+  const int n_kv = kstop > kbeg ? (kstop - kbeg + kBN - 1) / kBN : 0;
+  int wave_kv_end = CAUSAL ? min(qw0 + kQPerWave + off, NK) : NK;
+  if (qw0 >= NQ) wave_kv_end = kbeg;
 
   f32x4 kst[T::kKChunks];
   f32x4 vst[T::kVUnits][4];
 
-  // HBM -> registers for tile t; keys >= N read as zeros (buffer range check).
-  auto load_tile = [&](int t) {
-    const int k0 = t * kBN;
+  // HBM -> registers for keys [k0, k0 + kBN); keys past the end read as
+  // zeros (buffer range check).
+  auto load_tile = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < T::kKChunks; ++i) {
       const int u = tid + i * kThreads;
@@ -134,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = (f32x16){};
 
-  load_tile(0);
+  load_tile(kbeg);
   store_tile(0);
   // Everything loaded so far (Q included) has landed: the loop below then
   // never waits on a prefetch before its own LDS store.
@@ -142,9 +150,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
   __syncthreads();
 
   for (int t = 0; t < n_kv; ++t) {
-    const int k0 = t * kBN;
+    const int k0 = kbeg + t * kBN;
     const bool more = t + 1 < n_kv;
-    if (more) load_tile(t + 1);
+    if (more) load_tile(k0 + kBN);
 
     if (k0 < wave_kv_end) {
       const float* ks = lds + (t & 1) * T::kKStage;
@@ -162,15 +170,15 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
           for (int e = 0; e < 4; ++e) s[kb] = mfma_f32(ka[e], qf[j][e], s[kb]);
         }
 
-      const bool ragged = k0 + kBN > N;
-      const bool diag = CAUSAL && (k0 + kBN - 1 > qw0);
+      const bool ragged = k0 + kBN > NK;
+      const bool diag = CAUSAL && (k0 + kBN - 1 > qw0 + off);
       if (ragged || diag) {
 #pragma unroll
         for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
-            const bool masked = key >= N || (CAUSAL && key > my_q);
+            const bool masked = key >= NK || (CAUSAL && key > my_q + off);
             s[kb][r] = masked ? kNegInf : s[kb][r];
           }
       }
@@ -222,8 +230,13 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
 
   const float l_tot = half_swap_sum(l_run);
   const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
-  if (my_q < N) {
-    float* og = (float*)a.o + head + (int64_t)my_q * D;
+  const float lse = l_tot > 0.f ? (m_run * c + fast_log2(l_tot)) * kLn2 : kNegInf;
+  if (my_q < NQ) {
+    // a split writes its partial result (fp32, like the output) to the
+    // workspace rows of its key range
+    const int64_t row = SPLIT ? ((int64_t)split * a.problems + prob) * NQ + my_q
+                              : (int64_t)prob * NQ + my_q;
+    float* og = (float*)a.o + row * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -232,29 +245,32 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
                          oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv};
         *(f32x4*)(og + db * 32 + 8 * j + 4 * grp) = w;
       }
-    if (grp == 0 && a.lse)
-      a.lse[(int64_t)bh * N + my_q] =
-          l_tot > 0.f ? (m_run * c + fast_log2(l_tot)) * kLn2 : kNegInf;
+    if (grp == 0 && a.lse) a.lse[row] = lse;
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
-  int n_qt = (a.n + kBM - 1) / kBM;
-  int total = (int)((int64_t)n_qt * a.bh);
+  int n_qt = (a.nq + kBM - 1) / kBM;
+  int total = (int)((int64_t)n_qt * a.problems * (SPLIT ? a.splits : 1));
   FwdArgs args = a;
   void* params[] = {&args, &n_qt, &total};
-  return hipLaunchKernel((const void*)&fwd_f32_kernel<D, CAUSAL>, dim3(total), dim3(kThreads),
-                         params, 0, s);
+  return hipLaunchKernel((const void*)&fwd_f32_kernel<D, CAUSAL, SPLIT>, dim3(total),
+                         dim3(kThreads), params, 0, s);
+}
+
+template <int D>
+hipError_t launch_d(bool causal, bool split, const FwdArgs& a, hipStream_t s) {
+  if (causal) return split ? launch<D, true, true>(a, s) : launch<D, true, false>(a, s);
+  return split ? launch<D, false, true>(a, s) : launch<D, false, false>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_f32(int d, bool causal, const FwdArgs& a, hipStream_t s) {
-  if (d == 64) return causal ? launch<64, true>(a, s) : launch<64, false>(a, s);
-  return causal ? launch<128, true>(a, s) : launch<128, false>(a, s);
+hipError_t launch_fwd_f32(int d, bool causal, bool split, const FwdArgs& a, hipStream_t s) {
+  return d == 64 ? launch_d<64>(causal, split, a, s) : launch_d<128>(causal, split, a, s);
 }
 
-int64_t f32_grid_blocks(int64_t bh, int64_t n) { return (n + kBM - 1) / kBM * bh; }
+int f32_rows_per_block() { return kBM; }
 
 }  // namespace fa_impl

@@ -1,8 +1,10 @@
 // fa_fwd_h16.hip -- FlashAttention forward, bf16 / fp16 inputs, fp32 accumulate,
 // for MI355X (gfx950).
 //
-// What runs (one workgroup per (batch*head, 128-query tile); four wave64s,
-// each owning 32 query rows):
+// What runs (one workgroup per (problem, query tile[, key range]); NW
+// wave64s, each owning 32*QB query rows; the instance table at the end picks
+// NW, QB and the key tile BN per head size, and a one-wave instance for
+// problems of at most 32 rows, i.e. decoding steps):
 //   * The query tile stays in registers for the whole key loop, as the
 //     B operand of S^T = K Q^T (course lesson "FlashAttention Inner Loop
 //     Implementation", section "Implementing the Inner Loop": Q is loaded
@@ -39,6 +41,13 @@
 //     diagonal are never loaded.
 //   * Epilogue ("FlashAttention dissected", pseudocode's final step): one
 //     division of O by l, rounding to the I/O type, and LSE = scale*m + ln l.
+//     A workgroup of a split launch covers one range of keys and writes its
+//     O / l in fp32 and its LSE as a partial result instead; a second kernel
+//     merges the ranges (fa_combine.hip).
+//   * Grouped K/V heads and query/key lengths of their own come in through
+//     FwdArgs (kv_head(), causal_off), see fa_device.hpp.
+#include <type_traits>
+
 #include "fa_h16.hpp"
 
 namespace fa_impl {
@@ -60,7 +69,11 @@ struct Cfg {
   static constexpr int kVStride = BN + 8;           // elements per transposed-V row (+16 B)
   static constexpr int kKStage = BN * kKStride;
   static constexpr int kVStage = D * kVStride;
-  static constexpr int kLdsElems = 2 * (kKStage + kVStage);
+  // A one-wave workgroup has nobody to overlap with inside the workgroup:
+  // it keeps one LDS stage (the next tile waits in registers) so that twice
+  // as many workgroups fit in a CU's LDS.
+  static constexpr int kStages = NW == 1 ? 1 : 2;
+  static constexpr int kLdsElems = kStages * (kKStage + kVStage);
   static constexpr int kKUnits = BN * D / 8;        // 16-byte K chunks per tile
   static constexpr int kVUnits = (BN / 2) * (D / 8);  // (key pair, 8 columns) per tile
   static constexpr int kKPer = (kKUnits + kThreads - 1) / kThreads;
@@ -68,7 +81,7 @@ struct Cfg {
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
 };
 
-template <bool BF16, bool CAUSAL, class C>
+template <bool BF16, bool CAUSAL, bool SPLIT, class C>
 __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_qt, int total) {
   using HH = Half<BF16>;
   constexpr int D = C::D, QB = C::QB, BN = C::BN;
@@ -79,21 +92,25 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
   // it) scalar instead of exec-masked
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, grp = lane >> 5;
-  const int N = a.n;
+  const int NQ = a.nq, NK = a.nk;
 
+  // logical tile -> (problem, key range, query tile)
   const int L = xcd_remap(blockIdx.x, total);
-  const int bh = L / n_qt;
-  int qt = L - bh * n_qt;
+  const int pr_sp = L / n_qt;
+  int qt = L - pr_sp * n_qt;
   if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
+  const int split = SPLIT ? pr_sp % a.splits : 0;
+  const int prob = SPLIT ? pr_sp / a.splits : pr_sp;
 
-  const int64_t head = (int64_t)bh * N * D;
-  const int head_bytes = N * D * 2;
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint16_t*)a.q + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.v + head, head_bytes);
+  const int64_t qhead = (int64_t)prob * NQ * D;
+  const int64_t kvhead = (int64_t)kv_head(a, prob) * NK * D;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint16_t*)a.q + qhead, NQ * D * 2);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + kvhead, NK * D * 2);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.v + kvhead, NK * D * 2);
 
   const int q0 = qt * C::kBM;
   const int qw0 = q0 + wave * C::kQPerWave;  // first query of this wave
+  const int off = a.causal_off;
 
   // Q fragments: block qb, lane (col, grp) holds Q[qw0 + 32qb + col][16kc + 8grp .. +8);
   // rows past the end read as zero.
@@ -104,18 +121,24 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
     for (int kc = 0; kc < D / 16; ++kc)
       qf[qb][kc] = buf_load16(qr, ((qw0 + 32 * qb + col) * D + kc * 16 + grp * 8) * 2);
 
-  const int kv_end = CAUSAL ? min(q0 + C::kBM, N) : N;
-  const int n_kv = (kv_end + BN - 1) / BN;
-  const int wave_kv_end = CAUSAL ? min(qw0 + C::kQPerWave, N) : N;
+  // Keys of this workgroup: its split's range, cut at the last key that the
+  // tile's last row may see.  A wave stops at its own last visible key, and
+  // a wave whose rows all lie past the end does no arithmetic at all.
+  const int kbeg = SPLIT ? split * a.kv_chunk : 0;
+  int kstop = SPLIT ? min(kbeg + a.kv_chunk, NK) : NK;
+  if (CAUSAL) kstop = min(kstop, q0 + C::kBM + off);
+  const int n_kv = kstop > kbeg ? (kstop - kbeg + BN - 1) / BN : 0;
+  int wave_kv_end = CAUSAL ? min(qw0 + C::kQPerWave + off, NK) : NK;
+  if (qw0 >= NQ) wave_kv_end = kbeg;
 
   u32x4 kst[C::kKPer];
   u32x4 vst[C::kVPer][2];
 
-  // HBM -> registers for tile t.  Keys >= N read as zeros through the
-  // buffer range check (their scores are masked, and zero V rows keep 0 * V
-  // finite); nothing waits on these loads until the tile is stored to LDS.
-  auto load_tile = [&](int t) {
-    const int k0 = t * BN;
+  // HBM -> registers for the tile of keys [k0, k0 + BN).  Keys past the
+  // end read as zeros through the buffer range check (their scores are
+  // masked, and zero V rows keep 0 * V finite); nothing waits on these loads
+  // until the tile is stored to LDS.
+  auto load_tile = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < C::kKPer; ++i) {
       const int u = tid + i * C::kThreads;
@@ -140,7 +163,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
   // keys interleaved in pairs: one 32-bit word holds (V[kk][c], V[kk+1][c]).
   auto store_tile = [&](int buf) {
     uint16_t* ks = lds + buf * C::kKStage;
-    uint16_t* vs = lds + 2 * C::kKStage + buf * C::kVStage;
+    uint16_t* vs = lds + C::kStages * C::kKStage + buf * C::kVStage;
 #pragma unroll
     for (int i = 0; i < C::kKPer; ++i) {
       const int u = tid + i * C::kThreads;
@@ -181,7 +204,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = (f32x16){};
   }
 
-  load_tile(0);
+  load_tile(kbeg);
   store_tile(0);
   // Everything loaded so far (Q included) has landed: the loop below then
   // never waits on a prefetch before its own LDS store.
@@ -189,13 +212,14 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
   __syncthreads();
 
   for (int t = 0; t < n_kv; ++t) {
-    const int k0 = t * BN;
+    const int k0 = kbeg + t * BN;
     const bool more = t + 1 < n_kv;
-    if (more) load_tile(t + 1);
+    if (more) load_tile(k0 + BN);
 
     if (k0 < wave_kv_end) {
-      const uint16_t* ks = lds + (t & 1) * C::kKStage;
-      const uint16_t* vs = lds + 2 * C::kKStage + (t & 1) * C::kVStage;
+      const int buf = C::kStages == 2 ? (t & 1) : 0;
+      const uint16_t* ks = lds + buf * C::kKStage;
+      const uint16_t* vs = lds + C::kStages * C::kKStage + buf * C::kVStage;
 
       // S^T = K Q^T: lane holds keys k0 + 32*kb + 8*(r/4) + 4*grp + r%4 of
       // query qw0 + 32*qb + col.
@@ -213,8 +237,8 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
         }
       }
 
-      const bool ragged = k0 + BN > N;
-      const bool diag = CAUSAL && (k0 + BN - 1 > qw0);
+      const bool ragged = k0 + BN > NK;
+      const bool diag = CAUSAL && (k0 + BN - 1 > qw0 + off);
       if (ragged || diag) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -223,7 +247,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
-              const bool masked = key >= N || (CAUSAL && key > qw0 + 32 * qb + col);
+              const bool masked = key >= NK || (CAUSAL && key > qw0 + 32 * qb + col + off);
               s[qb][kb][r] = masked ? kNegInf : s[qb][kb][r];
             }
       }
@@ -284,7 +308,8 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
         }
     }
 
-    if (more) store_tile((t + 1) & 1);
+    if (C::kStages == 1) __syncthreads();  // tile t's LDS reads are done
+    if (more) store_tile(C::kStages == 2 ? ((t + 1) & 1) : 0);
     __syncthreads();
   }
 
@@ -294,8 +319,26 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
     const int q = qw0 + 32 * qb + col;
     const float l_tot = half_swap_sum(l_run[qb]);
     const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
-    if (q < N) {
-      uint16_t* og = (uint16_t*)a.o + head + (int64_t)q * D;
+    const float lse = l_tot > 0.f ? (m_run[qb] * c + fast_log2(l_tot)) * kLn2 : kNegInf;
+    if (SPLIT) {
+      // partial result of this key range, fp32, for the combine step
+      if (q < NQ) {
+        const int64_t row = ((int64_t)split * a.problems + prob) * NQ + q;
+        float* og = (float*)a.o + row * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 w = {oacc[qb][db][4 * j] * inv, oacc[qb][db][4 * j + 1] * inv,
+                             oacc[qb][db][4 * j + 2] * inv, oacc[qb][db][4 * j + 3] * inv};
+            *(f32x4*)(og + db * 32 + 8 * j + 4 * grp) = w;
+          }
+        if (grp == 0) a.lse[row] = lse;
+      }
+      continue;
+    }
+    if (q < NQ) {
+      uint16_t* og = (uint16_t*)a.o + qhead + (int64_t)q * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -305,20 +348,18 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
                            HH::pack(oacc[qb][db][4 * j + 2] * inv, oacc[qb][db][4 * j + 3] * inv)};
           *(u32x2*)(og + d0) = w;
         }
-      if (grp == 0 && a.lse)
-        a.lse[(int64_t)bh * N + q] =
-            l_tot > 0.f ? (m_run[qb] * c + fast_log2(l_tot)) * kLn2 : kNegInf;
+      if (grp == 0 && a.lse) a.lse[(int64_t)prob * NQ + q] = lse;
     }
   }
 }
 
-template <bool BF16, bool CAUSAL, class C>
+template <bool BF16, bool CAUSAL, bool SPLIT, class C>
 hipError_t launch(const FwdArgs& a, hipStream_t s) {
-  int n_qt = (a.n + C::kBM - 1) / C::kBM;
-  int total = (int)((int64_t)n_qt * a.bh);
+  int n_qt = (a.nq + C::kBM - 1) / C::kBM;
+  int total = (int)((int64_t)n_qt * a.problems * (SPLIT ? a.splits : 1));
   FwdArgs args = a;
   void* params[] = {&args, &n_qt, &total};
-  return hipLaunchKernel((const void*)&fwd_h16_kernel<BF16, CAUSAL, C>, dim3(total),
+  return hipLaunchKernel((const void*)&fwd_h16_kernel<BF16, CAUSAL, SPLIT, C>, dim3(total),
                          dim3(C::kThreads), params, 0, s);
 }
 
@@ -326,6 +367,9 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
 // d = 64 is VALU-heavy, so eight waves of 64 query rows each halve the LDS
 // reads per MFMA; d = 128 prefers four waves of 32 rows with 32-key tiles).
 // Overridable at build time (FA_H16_D64_CFG / FA_H16_D128_CFG = QB, BN, NW).
+// Problems with at most 32 query rows (decoding, grouped heads packed into
+// rows) take a one-wave workgroup instead, so that the grid is made of key
+// ranges rather than of idle query rows.
 #ifndef FA_H16_D64_CFG
 #define FA_H16_D64_CFG 2, 64, 8
 #endif
@@ -334,23 +378,36 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
 #endif
 using CfgD64 = Cfg<64, FA_H16_D64_CFG>;
 using CfgD128 = Cfg<128, FA_H16_D128_CFG>;
+using CfgD64Small = Cfg<64, 1, 64, 1>;
+using CfgD128Small = Cfg<128, 1, 32, 1>;
 
-template <bool BF16, class C>
-hipError_t launch_c(bool causal, const FwdArgs& a, hipStream_t s) {
-  return causal ? launch<BF16, true, C>(a, s) : launch<BF16, false, C>(a, s);
+bool use_small(bool causal, int64_t nq) { return !causal && nq <= 32; }
+
+template <bool BF16, int D>
+hipError_t launch_d(bool causal, bool split, const FwdArgs& a, hipStream_t s) {
+  using Big = typename std::conditional<D == 64, CfgD64, CfgD128>::type;
+  using Small = typename std::conditional<D == 64, CfgD64Small, CfgD128Small>::type;
+  if (use_small(causal, a.nq))
+    return split ? launch<BF16, false, true, Small>(a, s) : launch<BF16, false, false, Small>(a, s);
+  if (causal)
+    return split ? launch<BF16, true, true, Big>(a, s) : launch<BF16, true, false, Big>(a, s);
+  return split ? launch<BF16, false, true, Big>(a, s) : launch<BF16, false, false, Big>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_h16(bool bf16, int d, bool causal, const FwdArgs& a, hipStream_t s) {
+hipError_t launch_fwd_h16(bool bf16, int d, bool causal, bool split, const FwdArgs& a,
+                          hipStream_t s) {
   if (bf16)
-    return d == 64 ? launch_c<true, CfgD64>(causal, a, s) : launch_c<true, CfgD128>(causal, a, s);
-  return d == 64 ? launch_c<false, CfgD64>(causal, a, s) : launch_c<false, CfgD128>(causal, a, s);
+    return d == 64 ? launch_d<true, 64>(causal, split, a, s)
+                   : launch_d<true, 128>(causal, split, a, s);
+  return d == 64 ? launch_d<false, 64>(causal, split, a, s)
+                 : launch_d<false, 128>(causal, split, a, s);
 }
 
-int64_t h16_grid_blocks(int64_t bh, int64_t n) {
-  const int64_t bm = CfgD64::kBM < CfgD128::kBM ? CfgD64::kBM : CfgD128::kBM;
-  return (n + bm - 1) / bm * bh;
+int h16_rows_per_block(int d, bool causal, int64_t nq) {
+  if (use_small(causal, nq)) return 32;
+  return d == 64 ? CfgD64::kBM : CfgD128::kBM;
 }
 
 }  // namespace fa_impl

@@ -47,14 +47,15 @@ typedef enum {
 
 typedef enum {
   FA_OK = 0,
-  FA_ERR_NULL = 1,     /* q, k, v or o is NULL                                  */
-  FA_ERR_SHAPE = 2,    /* B, H or N negative, or the problem is too large       */
+  FA_ERR_NULL = 1,     /* a required pointer (q, k, v, o, partials) is NULL     */
+  FA_ERR_SHAPE = 2,    /* a size negative, H not a multiple of H_kv, too large  */
   FA_ERR_HEAD_DIM = 3, /* d is not one of the supported head sizes (64, 128)    */
   FA_ERR_DTYPE = 4,    /* dtype is not an fa_dtype value                        */
   FA_ERR_SCALE = 5,    /* scale is not finite or not > 0                        */
-  FA_ERR_ALIGN = 6,    /* q, k, v or o not 16-byte aligned, lse not 4-byte      */
-  FA_ERR_ALIAS = 7,    /* o or lse overlaps another buffer                      */
-  FA_ERR_LAUNCH = 8    /* the HIP runtime refused the kernel launch             */
+  FA_ERR_ALIGN = 6,    /* a tensor not 16-byte aligned, lse not 4-byte          */
+  FA_ERR_ALIAS = 7,    /* an output or the workspace overlaps another buffer    */
+  FA_ERR_LAUNCH = 8,   /* the HIP runtime refused the kernel launch             */
+  FA_ERR_WORKSPACE = 9 /* num_splits < 1, or workspace null, small or misaligned */
 } fa_status;
 
 /*
@@ -71,7 +72,7 @@ typedef enum {
  * B, H, N  batch, heads, sequence length (queries = keys = N).  Any of them
  *          zero is a valid empty problem and returns FA_OK with no launch.
  *          Limits (else FA_ERR_SHAPE): B*H <= 2^31-1, one head's N x d
- *          array (plus 256 rows) below 2^31 bytes, and the launch grid
+ *          array (plus 1024 rows) below 2^31 bytes, and the launch grid
  *          (B*H*ceil(N/128) workgroups) below 2^31.
  * d        head dimension: 64 or 128.
  * scale    multiplier of the dot products (usually 1/sqrt(d)); finite, > 0.
@@ -92,6 +93,89 @@ typedef enum {
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
                  fa_dtype dtype, void* stream);
+
+/*
+ * fa_fwd_ex -- the forward pass for decoding, grouped K/V heads and short
+ * grids, with the work optionally split over key ranges.
+ *
+ * Same operation as fa_fwd, generalised in three ways:
+ *   - queries and keys have their own lengths: q and o are [B, H, N_q, d],
+ *     k and v are [B, H_kv, N_kv, d], lse is [B, H, N_q];
+ *   - grouped heads: H_kv divides H and query head h reads K/V head
+ *     h / (H / H_kv) (H_kv = H is ordinary multi-head attention, H_kv = 1
+ *     shares one K/V head among all query heads).  The pages only name the
+ *     technique ("FlashAttention dissected", section "Interaction with the
+ *     KV cache during inference": several query heads share the same key and
+ *     value heads);
+ *   - causal masking is aligned to the end of the keys: key j is masked for
+ *     query i when j > i + (N_kv - N_q), so that query row i stands at key
+ *     position N_kv - N_q + i, as a decoding step that appends N_q tokens to
+ *     a cache of N_kv keys does.  With N_q = N_kv this is fa_fwd's mask; a
+ *     query with no visible key (possible when N_q > N_kv) gets O = 0 and
+ *     LSE = -inf.
+ * Split over keys (FlashDecoding, same section of "FlashAttention
+ * dissected": with one query row the keys are split across compute units
+ * to keep them busy): with num_splits > 1 the keys are cut into at most
+ * num_splits ranges of equal length (a multiple of 64 keys; fewer ranges
+ * when N_kv is short), every range is computed by its own workgroups into
+ * an fp32 partial result plus its logsumexp in `workspace`, and a second
+ * kernel merges the ranges exactly as fa_lse_combine does.  num_splits = 1
+ * runs one kernel and needs no workspace (workspace may then be NULL).
+ * fa_fwd_ex_default_splits gives a split count that fills the GPU.
+ *
+ * workspace        device memory of at least
+ *                  fa_fwd_ex_workspace_bytes(B, H, N_q, N_kv, d, num_splits)
+ *                  bytes, 16-byte aligned, owned by the caller and not
+ *                  overlapping any other argument; its contents on entry do
+ *                  not matter and are overwritten.  Two calls that share a
+ *                  workspace must be ordered (same stream, or synchronised).
+ * Everything else: as fa_fwd (validation before any launch, asynchronous on
+ * `stream`, no allocation, no retained pointers).  Status: FA_ERR_SHAPE
+ * also when H is not a multiple of H_kv (H_kv = 0 is allowed only with
+ * H = 0); FA_ERR_WORKSPACE when num_splits < 1 or, for a split launch, the
+ * workspace is NULL, smaller than required or misaligned.  N_kv = 0 is
+ * valid: every row then has no visible key, and k and v may be NULL.
+ */
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t d,
+                    float scale, int causal, fa_dtype dtype, int64_t num_splits,
+                    void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_fwd_ex needs for `num_splits` (0 when the call runs
+ * unsplit; -1 when the size overflows int64).  Invalid sizes give 0. */
+int64_t fa_fwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t N_q, int64_t N_kv, int64_t d,
+                                  int64_t num_splits);
+
+/* A split count for fa_fwd_ex that gives MI355X's 256 compute units enough
+ * workgroups when the unsplit grid is short (1 when it is already full or
+ * the arguments are invalid). */
+int64_t fa_fwd_ex_default_splits(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv,
+                                 int64_t d, int causal, fa_dtype dtype);
+
+/*
+ * fa_lse_combine -- merge attention results computed over disjoint key
+ * ranges (the split-KV partials above, or the per-device results of a
+ * sequence sharded across GPUs).
+ *
+ * o_part    device fp32 [splits, rows, d]: range s's output for each row,
+ *           already divided by that range's own sum of exponentials
+ *           (0 for a row with no visible key in the range).
+ * lse_part  device fp32 [splits, rows]: range s's natural-log logsumexp
+ *           (-inf for a row with no visible key in the range).
+ * o         device [rows, d] of `dtype`, written in full:
+ *           O = sum_s exp(LSE_s - LSE) O_s with LSE = log sum_s exp(LSE_s),
+ *           the online-softmax rescaling of "FlashAttention dissected",
+ *           section "The mathematical breakthrough: Tiling and Online
+ *           Softmax", applied to whole ranges; a row with every LSE_s = -inf
+ *           gets O = 0.
+ * lse       device fp32 [rows] written in full (-inf for such rows), or NULL.
+ * d         64 or 128.
+ * Ownership, ordering and validation as fa_fwd: o_part and lse_part are only
+ * read and must not overlap o or lse; o_part and o 16-byte aligned.
+ */
+fa_status fa_lse_combine(const float* o_part, const float* lse_part, int64_t splits,
+                         int64_t rows, int64_t d, void* o, float* lse, fa_dtype dtype,
+                         void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(fa_status s);
