@@ -11,10 +11,13 @@ Contents:
   * ``reference.fwd_gqa``   -- the same with grouped K/V heads and separate
                                query / key lengths (decoding);
   * ``reference.combine``   -- fp64 merge of results over disjoint key ranges;
+  * ``reference.bwd``       -- fp64 gradients of sum(dO * O) w.r.t. Q, K, V
+                               (``bwd_dq_rows``: dQ of sampled rows only);
   * ``online_ref``          -- the tile-by-tile online-softmax recurrence in
                                numpy fp64, in the deferred-normalisation form and
                                in the per-step-normalised form, used only to pin
                                the method's claim that it equals the plain
                                definition.
 """
-from .reference import build, fwd, fwd_gqa, combine, widen, FLAT_ROWS_ALL  # noqa: F401
+from .reference import (build, fwd, fwd_gqa, combine, bwd, bwd_dq_rows, widen,  # noqa: F401
+                        FLAT_ROWS_ALL)

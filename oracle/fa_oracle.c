@@ -38,6 +38,9 @@
  * position N_kv - N_q + i (the rows are the newest tokens), so key j is
  * visible when j <= i + N_kv - N_q.  For N_q = N_kv this is the mask above.
  *
+ * oracle_bwd_f64 gives the gradients of L = sum(dO * O) with respect to Q, K
+ * and V for a given upstream gradient dO (see that function).
+ *
  * oracle_combine_f64 merges results computed over disjoint key ranges,
  * following the normalised update of "How Did I Write My First
  * FlashAttention Kernel in CUDA?", pseudo-algorithm steps 4 and 5, applied
@@ -279,5 +282,182 @@ int oracle_combine_f64(const double* o_parts, const double* lse_parts, int64_t S
     }
     lse[r] = l > 0.0 ? m + log(l) : -INFINITY;
   }
+  return 0;
+}
+
+/* ---- gradients ------------------------------------------------------------
+ *
+ * The pages only state that the backward pass recomputes the attention
+ * weights from Q, K, V and the saved softmax statistics instead of storing
+ * them ("FlashAttention dissected", section "Memory complexity: from O(N^2)
+ * to O(N)").  The gradients themselves are the chain rule through the
+ * definition above; per head, with P_ij = softmax_j(s_ij) over the visible
+ * keys (P_ij = 0 for masked ones) and O = P V:
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   D_i   = sum_j P_ij dP_ij  (= dO_i . O_i)
+ *   dS_ij = P_ij (dP_ij - D_i)          (derivative of a softmax row)
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i
+ * Written out per row with the row's probabilities recomputed by the same
+ * three passes as the forward oracle. */
+
+typedef struct {
+  const void *q, *k, *v, *dout;
+  int dtype;
+  int64_t H, N, d;
+  double scale;
+  int causal;
+  double *dq, *dk, *dv;  /* [B*H, N, d] */
+  int64_t first, last;   /* this worker's heads */
+} bjob_t;
+
+/* Probabilities of row i of head `head` (element offset) into p[0..nvis). */
+static int64_t row_probs(const void* q, const void* k, int dtype, int64_t N, int64_t d,
+                         double scale, int causal, int64_t head, int64_t i, double* p) {
+  const int64_t nvis = causal ? i + 1 : N;
+  double m = -INFINITY;
+  for (int64_t j = 0; j < nvis; ++j) {
+    double dot = 0.0;
+    for (int64_t c = 0; c < d; ++c)
+      dot += load_elem(q, dtype, head + i * d + c) * load_elem(k, dtype, head + j * d + c);
+    p[j] = scale * dot;
+    if (p[j] > m) m = p[j];
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j < nvis; ++j) l += exp(p[j] - m);
+  for (int64_t j = 0; j < nvis; ++j) p[j] = exp(p[j] - m) / l;
+  return nvis;
+}
+
+static void* bwd_worker(void* arg) {
+  const bjob_t* J = (const bjob_t*)arg;
+  const int64_t N = J->N, d = J->d;
+  double* p = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+  double* ds = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+  double* o = (double*)malloc(sizeof(double) * (size_t)d);
+  if (!p || !ds || !o) {
+    free(p); free(ds); free(o);
+    return (void*)1;
+  }
+  for (int64_t bh = J->first; bh < J->last; ++bh) {
+    const int64_t head = bh * N * d;
+    double *dq = J->dq + head, *dk = J->dk + head, *dv = J->dv + head;
+    for (int64_t e = 0; e < N * d; ++e) dq[e] = dk[e] = dv[e] = 0.0;
+    for (int64_t i = 0; i < N; ++i) {
+      const int64_t nvis = row_probs(J->q, J->k, J->dtype, N, d, J->scale, J->causal, head, i, p);
+      /* O_i and D_i = dO_i . O_i */
+      for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+      for (int64_t j = 0; j < nvis; ++j)
+        for (int64_t c = 0; c < d; ++c) o[c] += p[j] * load_elem(J->v, J->dtype, head + j * d + c);
+      double D = 0.0;
+      for (int64_t c = 0; c < d; ++c) D += load_elem(J->dout, J->dtype, head + i * d + c) * o[c];
+      /* dP_ij, dS_ij; dV_j += P_ij dO_i */
+      for (int64_t j = 0; j < nvis; ++j) {
+        double dp = 0.0;
+        for (int64_t c = 0; c < d; ++c) {
+          const double g = load_elem(J->dout, J->dtype, head + i * d + c);
+          dp += g * load_elem(J->v, J->dtype, head + j * d + c);
+          dv[j * d + c] += p[j] * g;
+        }
+        ds[j] = p[j] * (dp - D);
+      }
+      /* dQ_i = scale sum_j dS_ij k_j ; dK_j += scale dS_ij q_i */
+      for (int64_t j = 0; j < nvis; ++j)
+        for (int64_t c = 0; c < d; ++c) {
+          dq[i * d + c] += J->scale * ds[j] * load_elem(J->k, J->dtype, head + j * d + c);
+          dk[j * d + c] += J->scale * ds[j] * load_elem(J->q, J->dtype, head + i * d + c);
+        }
+    }
+  }
+  free(p); free(ds); free(o);
+  return NULL;
+}
+
+/*
+ * oracle_bwd_f64 -- q, k, v, dout: contiguous [B, H, N, d] of `dtype`.
+ * dq, dk, dv: [B, H, N, d] doubles, written in full.  Threads work on whole
+ * heads.  Returns 0, -1 on a bad argument, -2 when out of memory.
+ */
+int oracle_bwd_f64(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                   int64_t B, int64_t H, int64_t N, int64_t d, double scale, int causal,
+                   double* dq, double* dk, double* dv, int nthreads) {
+  if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return -1;
+  if (B < 0 || H < 0 || N < 0 || d <= 0) return -1;
+  const int64_t heads = B * H;
+  if (heads == 0 || N == 0) return 0;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > heads) nthreads = (int)heads;
+  bjob_t* jobs = (bjob_t*)calloc((size_t)nthreads, sizeof(bjob_t));
+  pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  if (!jobs || !tids) {
+    free(jobs);
+    free(tids);
+    return -2;
+  }
+  int rc = 0, started = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    bjob_t* J = &jobs[t];
+    J->q = q; J->k = k; J->v = v; J->dout = dout; J->dtype = dtype;
+    J->H = H; J->N = N; J->d = d; J->scale = scale; J->causal = causal;
+    J->dq = dq; J->dk = dk; J->dv = dv;
+    J->first = heads * t / nthreads;
+    J->last = heads * (t + 1) / nthreads;
+    if (pthread_create(&tids[t], NULL, bwd_worker, J) != 0) {
+      if (bwd_worker(J)) rc = -2;
+      continue;
+    }
+    tids[started++] = tids[t];
+  }
+  for (int t = 0; t < started; ++t) {
+    void* ret = NULL;
+    pthread_join(tids[t], &ret);
+    if (ret) rc = -2;
+  }
+  free(jobs);
+  free(tids);
+  return rc;
+}
+
+/*
+ * oracle_bwd_dq_rows_f64 -- dQ for a list of flat rows ((b*H + h)*N + i)
+ * only: row i's gradient needs just row i's probabilities, so sampled rows
+ * of a large problem cost O(N d) each.  dq: [nrows, d] doubles.
+ */
+int oracle_bwd_dq_rows_f64(const void* q, const void* k, const void* v, const void* dout,
+                           int dtype, int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                           int causal, const int64_t* rows, int64_t nrows, double* dq) {
+  if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return -1;
+  if (B < 0 || H < 0 || N < 0 || d <= 0 || nrows < 0) return -1;
+  if (nrows == 0) return 0;
+  if (!q || !k || !v || !dout || !rows || !dq) return -1;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= B * H * N) return -1;
+  double* p = (double*)malloc(sizeof(double) * (size_t)N);
+  double* o = (double*)malloc(sizeof(double) * (size_t)d);
+  if (!p || !o) {
+    free(p); free(o);
+    return -2;
+  }
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t bh = rows[r] / N, i = rows[r] % N, head = bh * N * d;
+    const int64_t nvis = row_probs(q, k, dtype, N, d, scale, causal, head, i, p);
+    for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+    for (int64_t j = 0; j < nvis; ++j)
+      for (int64_t c = 0; c < d; ++c) o[c] += p[j] * load_elem(v, dtype, head + j * d + c);
+    double D = 0.0;
+    for (int64_t c = 0; c < d; ++c) D += load_elem(dout, dtype, head + i * d + c) * o[c];
+    double* out = dq + r * d;
+    for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) {
+      double dp = 0.0;
+      for (int64_t c = 0; c < d; ++c)
+        dp += load_elem(dout, dtype, head + i * d + c) * load_elem(v, dtype, head + j * d + c);
+      const double ds = p[j] * (dp - D);
+      for (int64_t c = 0; c < d; ++c) out[c] += scale * ds * load_elem(k, dtype, head + j * d + c);
+    }
+  }
+  free(p); free(o);
   return 0;
 }

@@ -63,6 +63,16 @@ def _load():
         lib.oracle_combine_f64.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_bwd_f64.restype = ctypes.c_int
+        lib.oracle_bwd_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_bwd_dq_rows_f64.restype = ctypes.c_int
+        lib.oracle_bwd_dq_rows_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_widen.restype = ctypes.c_double
         lib.oracle_widen.argtypes = [ctypes.c_int, ctypes.c_uint32]
         _lib = lib
@@ -198,6 +208,52 @@ def combine(o_parts, lse_parts):
     if rc != 0:
         raise RuntimeError(f"oracle_combine_f64 failed with code {rc}")
     return o, lse
+
+
+def _four(q, k, v, dout):
+    qb, dt = _stored_bits(q)
+    kb, dtk = _stored_bits(k)
+    vb, dtv = _stored_bits(v)
+    gb, dtg = _stored_bits(dout)
+    if not (dt == dtk == dtv == dtg):
+        raise TypeError("q, k, v, dout must share one dtype")
+    if not (qb.shape == kb.shape == vb.shape == gb.shape) or qb.ndim != 4:
+        raise ValueError("q, k, v, dout must all be [B, H, N, d] of one shape")
+    return qb, kb, vb, gb, dt
+
+
+def bwd(q, k, v, dout, scale: float, causal: bool, threads: int | None = None):
+    """Gradients of sum(dout * O) w.r.t. q, k, v in fp64 (square heads).
+
+    Returns ``(dq, dk, dv)`` as float64 numpy arrays of shape [B, H, N, d].
+    """
+    qb, kb, vb, gb, dt = _four(q, k, v, dout)
+    B, H, N, d = (int(s) for s in qb.shape)
+    dq = np.zeros((B, H, N, d), dtype=np.float64)
+    dk = np.zeros_like(dq)
+    dv = np.zeros_like(dq)
+    rc = _load().oracle_bwd_f64(qb.ctypes.data, kb.ctypes.data, vb.ctypes.data, gb.ctypes.data,
+                                DTYPE_CODES[dt], B, H, N, d, float(np.float32(scale)),
+                                int(bool(causal)), dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                                int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_bwd_f64 failed with code {rc}")
+    return dq, dk, dv
+
+
+def bwd_dq_rows(q, k, v, dout, scale: float, causal: bool, rows):
+    """dQ for the flat rows ``(b*H + h)*N + i`` only: [len(rows), d] float64."""
+    qb, kb, vb, gb, dt = _four(q, k, v, dout)
+    B, H, N, d = (int(s) for s in qb.shape)
+    rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    dq = np.zeros((rows_arr.size, d), dtype=np.float64)
+    rc = _load().oracle_bwd_dq_rows_f64(qb.ctypes.data, kb.ctypes.data, vb.ctypes.data,
+                                        gb.ctypes.data, DTYPE_CODES[dt], B, H, N, d,
+                                        float(np.float32(scale)), int(bool(causal)),
+                                        rows_arr.ctypes.data, rows_arr.size, dq.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle_bwd_dq_rows_f64 failed with code {rc}")
+    return dq
 
 
 def widen(dtype: str, bits: int) -> float:

@@ -45,6 +45,17 @@ MUTANTS = {
     "combine_dropped_old_scale": ("(a_old * out[c] + a_new * ot[c]) / l_new",
                                   "(out[c] + a_new * ot[c]) / l_new"),
     "combine_lse_sign": ("lse[r] = l > 0.0 ? m + log(l)", "lse[r] = l > 0.0 ? m - log(l)"),
+    "bwd_dropped_row_dot": ("ds[j] = p[j] * (dp - D);", "ds[j] = p[j] * dp;"),
+    "bwd_dk_from_keys": ("dk[j * d + c] += J->scale * ds[j] * load_elem(J->q,",
+                         "dk[j * d + c] += J->scale * ds[j] * load_elem(J->k,"),
+    "bwd_dv_from_ds": ("dv[j * d + c] += p[j] * g;", "dv[j * d + c] += ds[j] * g;"),
+    "bwd_dq_dropped_scale": ("dq[i * d + c] += J->scale * ds[j] *", "dq[i * d + c] += ds[j] *"),
+    "bwd_causal_bound": ("const int64_t nvis = causal ? i + 1 : N;",
+                         "const int64_t nvis = causal ? i : N;"),
+    "bwd_rows_dropped_row_dot": ("const double ds = p[j] * (dp - D);",
+                                 "const double ds = p[j] * dp;"),
+    "bwd_row_dot_from_v": ("D += load_elem(J->dout, J->dtype, head + i * d + c) * o[c];",
+                           "D += load_elem(J->v, J->dtype, head + i * d + c) * o[c];"),
 }
 
 

@@ -408,3 +408,81 @@ def test_combine_closed_forms(oracle_lib):
     o, lse = oracle.combine(np.stack([o1, o2]), np.stack([np.zeros(3), np.full(3, math.log(3.0))]))
     np.testing.assert_allclose(o, 0.25 * o1 + 0.75 * o2, rtol=1e-14, atol=1e-15)
     np.testing.assert_allclose(lse, np.full(3, math.log(4.0)), rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Gradients (backward pass)
+# --------------------------------------------------------------------------
+
+def _eighths(shape, seed):
+    # values k/8 with |k| <= 16: a +-2^-12 step is exact in fp32
+    g = np.random.default_rng(seed)
+    return torch.from_numpy((g.integers(-16, 17, size=shape) / 8.0).astype(np.float32))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradients_match_finite_differences_of_the_forward(oracle_lib, causal):
+    # dL/dx for L = sum(dO * O(x)): central differences of the (separately
+    # pinned) forward oracle with an exact step h = 2^-12.
+    B, H, N, d = 1, 2, 5, 4
+    q, k, v, g = (_eighths((B, H, N, d), s) for s in (121, 122, 123, 124))
+    scale = 0.5
+    dq, dk, dv = oracle.bwd(q, k, v, g, scale, causal)
+    h = 2.0 ** -12
+    gg = _f64(g)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.fwd(q_, k_, v_, scale, causal)
+        return float((o * gg).sum())
+
+    worst = 0.0
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for idx in np.ndindex(B, H, N, d):
+            args_p = [q.clone(), k.clone(), v.clone()]
+            args_m = [q.clone(), k.clone(), v.clone()]
+            args_p[which][idx] += h
+            args_m[which][idx] -= h
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            worst = max(worst, abs(fd - grad[idx]))
+    assert worst <= 1e-6, worst
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,d", [(1, 8), (9, 16), (40, 8)])
+def test_gradients_match_torch_autograd_fp64(oracle_lib, dtype, causal, N, d):
+    B, H = 2, 2
+    q, k, v, g = (_rand((B, H, N, d), dtype, seed=s) for s in (131, 132, 133, 134))
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = oracle.bwd(q, k, v, g, scale, causal)
+    sc = float(np.float32(scale))
+    q64, k64, v64 = (t.to(torch.float64).requires_grad_(True) for t in (q, k, v))
+    logits = sc * torch.matmul(q64, k64.transpose(-1, -2))
+    if causal:
+        logits = logits.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    o = torch.matmul(torch.softmax(logits, -1), v64)
+    o.backward(g.to(torch.float64))
+    for got, ref in ((dq, q64.grad), (dk, k64.grad), (dv, v64.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradient_invariants(oracle_lib, causal):
+    # Softmax rows are shift-invariant, so every dS row sums to zero and the
+    # key gradients of a head sum to zero; the weights of a row sum to one,
+    # so the value gradients of a head sum to the sum of dO rows.
+    B, H, N, d = 2, 3, 33, 8
+    q, k, v, g = (_rand((B, H, N, d), seed=s) for s in (141, 142, 143, 144))
+    dq, dk, dv = oracle.bwd(q, k, v, g, 0.4, causal)
+    assert np.max(np.abs(dk.sum(axis=2))) <= 1e-12 * max(1.0, np.abs(dk).max())
+    np.testing.assert_allclose(dv.sum(axis=2), _f64(g).sum(axis=2), rtol=1e-12, atol=1e-12)
+
+
+def test_dq_rows_equal_full_gradient(oracle_lib):
+    B, H, N, d = 2, 2, 30, 8
+    q, k, v, g = (_rand((B, H, N, d), seed=s) for s in (151, 152, 153, 154))
+    for causal in (False, True):
+        dq, _, _ = oracle.bwd(q, k, v, g, 0.3, causal)
+        rows = np.array([0, 7, 29, 30, 59, 100, B * H * N - 1])
+        got = oracle.bwd_dq_rows(q, k, v, g, 0.3, causal, rows)
+        np.testing.assert_allclose(got, dq.reshape(-1, d)[rows], rtol=1e-14, atol=1e-15)
