@@ -8,7 +8,11 @@ default workload is the bf16 long-sequence shape B=1 H=16 N=16384 d=64,
 non-causal.  Workloads with grouped K/V heads, their own key length or a key
 split (C1s, D1, G1, G2) run through ``fa_fwd_ex`` instead: one step is then
 the whole call (the split kernel and, when split, the combine kernel), with
-its workspace allocated before timing.  Prints ONE JSON line with:
+its workspace allocated before timing.  ``--pass bwd`` times the backward
+pass instead (``fa_bwd``: row dot products, dK/dV, dQ) on a square bf16/fp16
+workload, after one forward call that provides O and LSE; its FLOPs follow
+the usual convention of 2.5x the forward's (five products of 2*d FLOPs per
+visible pair).  Prints ONE JSON line with:
 
   value / ms_per_step   whole-job throughput (metric FLOPs 4*B*H*N^2*d, halved
                         when causal) from a wall clock around K steps,
@@ -105,12 +109,48 @@ def cpu_baseline(w, q, k, v, target_s: float):
                       f"{fl:.3e} FLOPs in {dt:.1f} s, fp64 three-pass, {threads} threads"}
 
 
+def cpu_baseline_bwd(w, q, k, v, dout, target_s: float):
+    """fp64 oracle dQ rows on a bounded row sample, scaled to TFLOP/s.
+
+    A dQ row recomputes its scores, weights and output (2 + 2 FLOPs per key
+    and column), dP (2) and dQ (2): 8*d FLOPs per visible key.  The oracle's
+    row routine runs on one thread.
+    """
+    import numpy as np
+    import oracle
+
+    rng = np.random.default_rng(98)
+    total = w.B * w.H * w.N
+
+    def rows_flops(rows):
+        vis = (rows % w.N + 1) if w.causal else np.full(rows.shape, w.N)
+        return float(vis.sum()) * 8.0 * w.d
+
+    calib = np.sort(rng.choice(total, size=min(16, total), replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.bwd_dq_rows(q, k, v, dout, w.scale, w.causal, calib)
+    rate = rows_flops(calib) / max(time.perf_counter() - t0, 1e-6)
+    per_row = rows_flops(calib) / len(calib)
+    want = int(min(total, max(16, target_s * rate / per_row)))
+    rows = np.sort(rng.choice(total, size=want, replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.bwd_dq_rows(q, k, v, dout, w.scale, w.causal, rows)
+    dt = time.perf_counter() - t0
+    fl = rows_flops(rows)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"dQ of {want} of {total} query rows (uniform, seed 98) of the same "
+                      f"workload, 8*d FLOPs per visible key, {fl:.3e} FLOPs in {dt:.1f} s, fp64, "
+                      f"1 thread"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="C4")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="time the forward pass (default) or the backward pass")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-bytes", type=int, default=0,
@@ -129,6 +169,7 @@ def main():
               "in this library (heads shard across GPUs with no exchange).", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     from exact_attention_13_amd import binding
     from exact_attention_13_amd.inputs import WORKLOADS, make_inputs
@@ -171,7 +212,25 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     splits, workspace = 1, None
-    if w.extended:
+    if args.which == "bwd":
+        if w.extended or w.dtype == "f32":
+            sys.exit("the backward pass runs on square bf16/fp16 workloads (C3, C4, C5)")
+        g = np.random.default_rng(w.seed + 100)
+        dout = torch.from_numpy(g.standard_normal((w.B, w.H, w.N, w.d)).astype(np.float32)).to(
+            qd.dtype).to(dev)
+        binding.fwd(qd, kd, vd, w.scale, w.causal, out=o, lse=lse, stream=stream)
+        grads = [torch.empty_like(qd) for _ in range(3)]
+        delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        dt_code = binding.FA_BF16 if w.dtype == "bf16" else binding.FA_F16
+
+        def step():
+            st = binding.fa_bwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                                dout.data_ptr(), lse.data_ptr(), *(t.data_ptr() for t in grads),
+                                delta.data_ptr(), w.B, w.H, w.N, w.d, w.scale, w.causal, dt_code,
+                                stream.cuda_stream)
+            if st != 0:
+                raise binding.FaError(st)
+    elif w.extended:
         dt_code = {"f32": binding.FA_F32, "bf16": binding.FA_BF16, "f16": binding.FA_F16}[w.dtype]
         splits = w.splits or binding.default_splits(w.B, w.H, w.h_kv, w.N, w.n_kv, w.d,
                                                     w.causal, dt_code)
@@ -205,18 +264,22 @@ def main():
     avg_kernel_ms = sum(kernel_ms) / len(kernel_ms)
     ms_per_step = wall * 1e3 / args.steps
 
-    flops = w.flops
+    flops = w.flops * (2.5 if args.which == "bwd" else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    hbm_bound = flops / w.io_bytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    hbm_bound = args.which == "fwd" and flops / w.io_bytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     if hbm_bound:
         achieved, peak, unit = w.io_bytes / (avg_kernel_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
     else:
         achieved, unit = flops / (avg_kernel_ms * 1e-3) / 1e12, "TFLOP/s"
     traffic = read_traffic(w.name)
 
+    if args.which == "bwd":
+        metric = f"bwd attention TFLOP/s (2.5x fwd FLOPs), workload {w.name}"
+    else:
+        metric = METRIC if w.name == "C4" else f"fwd attention TFLOP/s, workload {w.name}"
     out = {
-        "metric": METRIC if w.name == "C4" else f"fwd attention TFLOP/s, workload {w.name}",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -237,14 +300,18 @@ def main():
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "algorithmic_bytes": w.io_bytes,
-                     "timed": ("fa_fwd_ex call: split kernel + combine kernel" if splits > 1
+                     "timed": ("fa_bwd call: row-dot, dK/dV and dQ kernels" if args.which == "bwd"
+                               else "fa_fwd_ex call: split kernel + combine kernel" if splits > 1
                                else "one forward kernel"),
                      "kernel_ms_avg": round(avg_kernel_ms, 5),
                      "kernel_ms_min": round(kernel_ms[0], 5),
                      "kernel_ms_median": round(kernel_ms[len(kernel_ms) // 2], 5)},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        if args.which == "bwd":
+            out["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, dout.cpu(), args.cpu_seconds)
+        else:
+            out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

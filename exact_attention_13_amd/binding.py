@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD
 _DTYPE_CODES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
 
 # Every symbol include/fa.h declares.
-EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_ex_default_splits", "fa_fwd_ex_workspace_bytes",
+EXPORTED = ("fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_ex_default_splits", "fa_fwd_ex_workspace_bytes",
             "fa_lse_combine", "fa_strerror", "fa_version")
 
 _lib = None
@@ -61,6 +61,9 @@ def load() -> ctypes.CDLL:
         lib.fa_lse_combine.restype = ctypes.c_int
         lib.fa_lse_combine.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int64] * 3 + [
             ctypes.c_void_p] * 2 + [ctypes.c_int, ctypes.c_void_p]
+        lib.fa_bwd.restype = ctypes.c_int
+        lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_strerror.argtypes = [ctypes.c_int]
         lib.fa_version.restype = ctypes.c_int
@@ -232,3 +235,44 @@ def lse_combine(o_part: torch.Tensor, lse_part: torch.Tensor, dtype: torch.dtype
     if st != FA_OK:
         raise FaError(st)
     return out, lse
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, dtype,
+           stream) -> int:
+    """Raw C call with integer pointers; returns the fa_status code."""
+    return int(load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, int(B), int(H), int(N),
+                             int(d), float(scale), int(bool(causal)), int(dtype), stream))
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+        lse: torch.Tensor, dout: torch.Tensor, scale: float | None = None,
+        causal: bool = False, stream: torch.cuda.Stream | None = None):
+    """Gradients (dq, dk, dv) of the forward pass for [B, H, N, d] bf16/fp16 tensors.
+
+    ``o`` and ``lse`` are what ``fwd`` returned for the same inputs.  Returns
+    ``(dq, dk, dv)`` of q's dtype; the row dot products D = rowsum(dO * O)
+    go to a scratch tensor allocated here.
+    """
+    if q.dim() != 4 or not (q.shape == k.shape == v.shape == o.shape == dout.shape):
+        raise ValueError("q, k, v, o, dout must be [B, H, N, d] tensors of one shape")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype) or \
+            q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("the backward pass takes bfloat16 or float16 tensors of one dtype")
+    tensors = (q, k, v, o, dout, lse)
+    if not all(t.is_cuda and t.is_contiguous() for t in tensors):
+        raise ValueError("inputs must be contiguous GPU tensors")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                B, H, N, d, scale, causal, _DTYPE_CODES[q.dtype], stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st)
+    return dq, dk, dv

@@ -262,6 +262,59 @@ extern "C" fa_status fa_lse_combine(const float* o_part, const float* lse_part, 
                                                    lse, (int)dtype, (hipStream_t)stream));
 }
 
+extern "C" fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            float* delta, int64_t B, int64_t H, int64_t N, int64_t d,
+                            float scale, int causal, fa_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (!valid_dtype(dtype) || dtype == FA_F32) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  if (N > INT32_MAX || H > INT32_MAX || B > INT32_MAX / H) return FA_ERR_SHAPE;
+  const int64_t bh = B * H;
+  if (bh > INT64_MAX / N || bh * N > INT64_MAX / (d * 2)) return FA_ERR_SHAPE;
+  if ((N + kRowSlack) * d * 2 > INT32_MAX) return FA_ERR_SHAPE;
+  if (fa_impl::bwd_grid_blocks(bh, N) > INT32_MAX) return FA_ERR_SHAPE;
+  if ((bh * N + 255) / 256 * (d / 8) > INT32_MAX) return FA_ERR_SHAPE;  // row-dot grid
+
+  const void* in[6] = {q, k, v, o, dout, lse};
+  void* out[4] = {dq, dk, dv, delta};
+  for (int i = 0; i < 5; ++i)
+    if (!aligned(in[i], 16)) return FA_ERR_ALIGN;
+  for (int i = 0; i < 3; ++i)
+    if (!aligned(out[i], 16)) return FA_ERR_ALIGN;
+  if (!aligned(lse, 4) || !aligned(delta, 4)) return FA_ERR_ALIGN;
+
+  const int64_t tb = bh * N * d * 2, lb = bh * N * 4;
+  const int64_t in_bytes[6] = {tb, tb, tb, tb, tb, lb};
+  const int64_t out_bytes[4] = {tb, tb, tb, lb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(out[i], out_bytes[i], in[j], in_bytes[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out[i], out_bytes[i], out[j], out_bytes[j])) return FA_ERR_ALIAS;
+  }
+
+  fa_impl::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.bh = (int)bh;
+  a.n = (int)N;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  return launch_status(fa_impl::launch_bwd_h16(dtype == FA_BF16, (int)d, causal != 0, a, o, delta,
+                                               (hipStream_t)stream));
+}
+
 extern "C" const char* fa_strerror(fa_status s) {
   switch (s) {
     case FA_OK: return "success";

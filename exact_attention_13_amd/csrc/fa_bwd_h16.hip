@@ -1,0 +1,504 @@
+// fa_bwd_h16.hip -- FlashAttention backward pass, bf16 / fp16 inputs, fp32
+// accumulate, for MI355X (gfx950).
+//
+// The attention weights are never stored: they are recomputed from Q, K and
+// the forward pass's logsumexp ("FlashAttention dissected", section "Memory
+// complexity: from O(N^2) to O(N)": the backward pass recomputes the blocks
+// it needs from Q, K, V and the saved softmax statistics).  With
+// P_ij = exp(scale q_i.k_j - LSE_i) (0 where masked):
+//     D_i   = dO_i . O_i
+//     dS_ij = P_ij (dO_i . v_j - D_i)
+//     dV_j  = sum_i P_ij dO_i
+//     dK_j  = scale sum_i dS_ij q_i
+//     dQ_i  = scale sum_j dS_ij k_j
+// Three kernels, no atomics (the result is bitwise reproducible):
+//   * bwd_delta_kernel: D_i, one row per d/8 lanes, v_dot2 on the stored pairs;
+//   * bwd_dkdv_kernel: a workgroup owns 128 keys (four waves x 32), keeps its
+//     K and V fragments in registers and streams 32-query tiles of Q and dO
+//     through double-buffered LDS, each tile stored twice: row-major (for
+//     S = Q K^T and dP = dO V^T, whose accumulators give every lane one key)
+//     and transposed with the query order permuted inside 16-row chunks (bits
+//     2 and 3 swapped), so that the P and dS accumulators are, unchanged, the
+//     B operands of dV^T += dO^T P and dK^T += Q^T dS;
+//   * bwd_dq_kernel: the forward kernel's shape: a workgroup owns 128 queries
+//     (Q and dO fragments in registers, one query per lane in S^T = K Q^T and
+//     dP^T = V dO^T) and streams 32-key tiles of K (row-major and transposed)
+//     and V (row-major); dS^T is the B operand of dQ^T += K^T dS^T.
+// Causal masking, ragged tails and the -inf guard follow the forward kernels.
+#include "fa_h16.hpp"
+
+namespace fa_impl {
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdRows = 32 * kBwdWaves;  // keys (dK/dV) or queries (dQ) per workgroup
+constexpr int kBT = 32;                   // rows of a streamed tile
+constexpr float kLog2e = 1.44269504088896340736f;
+
+template <int D>
+struct BwdTile {
+  static constexpr int kRowStride = D + 8;  // row-major tile (+16 B per row)
+  static constexpr int kTStride = kBT + 8;  // transposed tile (+16 B per row)
+  static constexpr int kRowElems = kBT * kRowStride;
+  static constexpr int kTElems = D * kTStride;
+  static constexpr int kPairUnits = (kBT / 2) * (D / 8);  // (row pair, 8 columns)
+};
+
+// Position of row rr of a tile in the transposed layout (bits 2, 3 swapped
+// inside each 16-row chunk; see swap23).
+__device__ __forceinline__ int tpos(int rr) { return (rr & ~15) | swap23(rr & 15); }
+
+// Rows 2p and 2p+1, columns 8cc .. 8cc+7, of a [rows, D] array.
+template <int D>
+__device__ __forceinline__ void load_pair(__amdgpu_buffer_rsrc_t r, int row0, int p, int cc,
+                                          u32x4& x, u32x4& y) {
+  x = buf_load16(r, ((row0 + 2 * p) * D + cc * 8) * 2);
+  y = buf_load16(r, ((row0 + 2 * p + 1) * D + cc * 8) * 2);
+}
+
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t* rm, int p, int cc, u32x4 x, u32x4 y) {
+  using T = BwdTile<D>;
+  *(u32x4*)(rm + (2 * p) * T::kRowStride + cc * 8) = x;
+  *(u32x4*)(rm + (2 * p + 1) * T::kRowStride + cc * 8) = y;
+}
+
+// Transposed store: one 32-bit word holds the pair (row 2p, row 2p+1) of a
+// column; rows 2p, 2p+1 stay adjacent under tpos.
+template <int D>
+__device__ __forceinline__ void store_cols(uint16_t* tm, int p, int cc, u32x4 x, u32x4 y) {
+  using T = BwdTile<D>;
+  const int pos = tpos(2 * p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = __builtin_amdgcn_perm(y[j], x[j], 0x05040100u);
+    const uint32_t hi = __builtin_amdgcn_perm(y[j], x[j], 0x07060302u);
+    *(uint32_t*)(tm + (cc * 8 + 2 * j) * T::kTStride + pos) = lo;
+    *(uint32_t*)(tm + (cc * 8 + 2 * j + 1) * T::kTStride + pos) = hi;
+  }
+}
+
+// logsumexp in exp2 units; a row without a visible key (LSE = -inf) gets +inf
+// so that every weight exp2(s c - lse2) is 0 instead of inf.
+__device__ __forceinline__ float lse_log2(float lse) {
+  return lse == kNegInf ? __builtin_inff() : lse * kLog2e;
+}
+
+// ---------------------------------------------------------------------------
+// D_i = dO_i . O_i
+// ---------------------------------------------------------------------------
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ o,
+                                                        const uint16_t* __restrict__ dout,
+                                                        float* __restrict__ delta,
+                                                        int64_t rows) {
+  using HH = Half<BF16>;
+  constexpr int kLanes = D / 8;
+  constexpr int kRowsPerBlock = 256 / kLanes;
+  const int sub = threadIdx.x % kLanes;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanes;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 x = *(const u32x4*)(o + row * D + sub * 8);
+    const u32x4 y = *(const u32x4*)(dout + row * D + sub * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = HH::dot2(x[e], y[e], acc);
+  }
+#pragma unroll
+  for (int off = kLanes / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && sub == 0) delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (head, 128 keys)
+// ---------------------------------------------------------------------------
+template <bool BF16, bool CAUSAL, int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdArgs a, int n_kt, int total) {
+  using HH = Half<BF16>;
+  using T = BwdTile<D>;
+  constexpr int kStage = 2 * (T::kRowElems + T::kTElems);  // Qr, Qt, dOr, dOt
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][kBT];  // [stage][lse2, D][query]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, grp = lane >> 5;
+  const int N = a.n;
+
+  const int L = xcd_remap(blockIdx.x, total);
+  const int bh = L / n_kt;
+  const int kt = L - bh * n_kt;  // causal: low key tiles see the most queries and go first
+  const int k0 = kt * kBwdRows;
+  const int kw0 = k0 + wave * 32;  // this wave's first key
+
+  const int64_t head = (int64_t)bh * N * D;
+  const int hb = N * D * 2;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint16_t*)a.q + head, hb);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + head, hb);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.v + head, hb);
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc((const uint16_t*)a.dout + head, hb);
+  const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.lse + (int64_t)bh * N, N * 4);
+  const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.delta + (int64_t)bh * N, N * 4);
+
+  // K and V rows of this wave's keys as B operands: lane (col, grp) holds
+  // row kw0 + col, columns 16 kc + 8 grp .. + 8 (zero past the end).
+  u32x4 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+    kf[kc] = buf_load16(kr, ((kw0 + col) * D + kc * 16 + grp * 8) * 2);
+    vf[kc] = buf_load16(vr, ((kw0 + col) * D + kc * 16 + grp * 8) * 2);
+  }
+
+  const int n_qt = (N + kBT - 1) / kBT;
+  const int qt_begin = CAUSAL ? k0 / kBT : 0;  // earlier queries see none of these keys
+
+  // Staging of one query tile: (row pair, 8 columns) units of Q then dO,
+  // plus the tile's 32 lse and 32 D values.
+  constexpr int kUnits = 2 * T::kPairUnits;
+  constexpr int kPer = (kUnits + kBwdThreads - 1) / kBwdThreads;
+  u32x4 sx[kPer], sy[kPer];
+  float st = 0.f;
+  // Units are dealt by whole waves (kPairUnits is a multiple of 64), so the
+  // Q-or-dO choice is wave-uniform and the buffer resource stays scalar.
+  static_assert(T::kPairUnits % 64 == 0 && kUnits % kBwdThreads == 0, "unit split");
+  auto load_tile = [&](int q0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = tid + i * kBwdThreads;
+      const int w = u % T::kPairUnits;
+      const int p = w % (kBT / 2), cc = w / (kBT / 2);
+      if (wave * 64 + i * kBwdThreads < T::kPairUnits)
+        load_pair<D>(qr, q0, p, cc, sx[i], sy[i]);
+      else
+        load_pair<D>(gr, q0, p, cc, sx[i], sy[i]);
+    }
+    if (tid < kBT)
+      st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, (q0 + tid) * 4, 0, 0));
+    else if (tid < 2 * kBT)
+      st = __builtin_bit_cast(float,
+                              __builtin_amdgcn_raw_buffer_load_b32(dr, (q0 + tid - kBT) * 4, 0, 0));
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* base = lds + buf * kStage;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = tid + i * kBwdThreads;
+      const int w = u % T::kPairUnits;
+      const int p = w % (kBT / 2), cc = w / (kBT / 2);
+      const bool first = wave * 64 + i * kBwdThreads < T::kPairUnits;
+      uint16_t* rm = base + (first ? 0 : T::kRowElems + T::kTElems);
+      store_rows<D>(rm, p, cc, sx[i], sy[i]);
+      store_cols<D>(rm + T::kRowElems, p, cc, sx[i], sy[i]);
+    }
+    if (tid < 2 * kBT) stat[buf][tid / kBT][tid % kBT] = tid < kBT ? lse_log2(st) : st;
+  };
+
+  const float c = a.scale_log2;
+  f32x16 dkT[D / 32], dvT[D / 32];  // dK^T, dV^T: lane holds key kw0 + col
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dkT[db] = dvT[db] = (f32x16){};
+
+  load_tile(qt_begin * kBT);
+  store_tile(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int qt = qt_begin; qt < n_qt; ++qt) {
+    const int it = qt - qt_begin, buf = it & 1;
+    const int q0 = qt * kBT;
+    const bool more = qt + 1 < n_qt;
+    if (more) load_tile(q0 + kBT);
+
+    // causal: a tile whose last query comes before this wave's first key is empty
+    if (!(CAUSAL && q0 + kBT - 1 < kw0)) {
+      const uint16_t* qrm = lds + buf * kStage;
+      const uint16_t* qtm = qrm + T::kRowElems;
+      const uint16_t* grm = qtm + T::kTElems;
+      const uint16_t* gtm = grm + T::kRowElems;
+
+      // S = Q K^T and dP = dO V^T: lane holds key kw0 + col of the queries
+      // q0 + 8 (r/4) + 4 grp + r%4.
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const u32x4 qa = *(const u32x4*)(qrm + col * T::kRowStride + kc * 16 + grp * 8);
+        s = HH::mfma(qa, kf[kc], s);
+      }
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const u32x4 ga = *(const u32x4*)(grm + col * T::kRowStride + kc * 16 + grp * 8);
+        dp = HH::mfma(ga, vf[kc], dp);
+      }
+
+      const int key = kw0 + col;
+      const bool edge = q0 + kBT > N || kw0 + 32 > N || (CAUSAL && q0 < kw0 + 31);
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 l4 = *(const f32x4*)(&stat[buf][0][8 * j + 4 * grp]);
+        const f32x4 d4 = *(const f32x4*)(&stat[buf][1][8 * j + 4 * grp]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * j + e;
+          float p = fast_exp2(fmaf(s[r], c, -l4[e]));
+          if (edge) {
+            const int q = q0 + 8 * j + 4 * grp + e;
+            const bool ok = q < N && key < N && (!CAUSAL || key <= q);
+            p = ok ? p : 0.f;
+          }
+          pv[r] = p;
+          dsv[r] = p * (dp[r] - d4[e]);
+        }
+      }
+      uint32_t pp[8], pd[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pp[i] = HH::pack(pv[2 * i], pv[2 * i + 1]);
+        pd[i] = HH::pack(dsv[2 * i], dsv[2 * i + 1]);
+      }
+
+      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query chunks.
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+          const u32x4 bp = {pp[4 * ch], pp[4 * ch + 1], pp[4 * ch + 2], pp[4 * ch + 3]};
+          const u32x4 bd = {pd[4 * ch], pd[4 * ch + 1], pd[4 * ch + 2], pd[4 * ch + 3]};
+          const u32x4 ga = *(const u32x4*)(gtm + (db * 32 + col) * T::kTStride + ch * 16 + grp * 8);
+          const u32x4 qa = *(const u32x4*)(qtm + (db * 32 + col) * T::kTStride + ch * 16 + grp * 8);
+          dvT[db] = HH::mfma(ga, bp, dvT[db]);
+          dkT[db] = HH::mfma(qa, bd, dkT[db]);
+        }
+    }
+
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dK = scale * (Q^T dS)^T, dV = (dO^T P)^T; lane holds key kw0 + col.
+  const int key = kw0 + col;
+  if (key < N) {
+    uint16_t* dkg = (uint16_t*)a.dk + head + (int64_t)key * D;
+    uint16_t* dvg = (uint16_t*)a.dv + head + (int64_t)key * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = db * 32 + 8 * j + 4 * grp;
+        const u32x2 wk = {HH::pack(dkT[db][4 * j] * a.scale, dkT[db][4 * j + 1] * a.scale),
+                          HH::pack(dkT[db][4 * j + 2] * a.scale, dkT[db][4 * j + 3] * a.scale)};
+        const u32x2 wv = {HH::pack(dvT[db][4 * j], dvT[db][4 * j + 1]),
+                          HH::pack(dvT[db][4 * j + 2], dvT[db][4 * j + 3])};
+        *(u32x2*)(dkg + d0) = wk;
+        *(u32x2*)(dvg + d0) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (head, 128 queries)
+// ---------------------------------------------------------------------------
+template <bool BF16, bool CAUSAL, int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a, int n_qt, int total) {
+  using HH = Half<BF16>;
+  using T = BwdTile<D>;
+  constexpr int kStage = 2 * T::kRowElems + T::kTElems;  // Kr, Kt, Vr
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, grp = lane >> 5;
+  const int N = a.n;
+
+  const int L = xcd_remap(blockIdx.x, total);
+  const int bh = L / n_qt;
+  int qt = L - bh * n_qt;
+  if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
+  const int q0 = qt * kBwdRows;
+  const int qw0 = q0 + wave * 32;
+  const int my_q = qw0 + col;
+
+  const int64_t head = (int64_t)bh * N * D;
+  const int hb = N * D * 2;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint16_t*)a.q + head, hb);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + head, hb);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.v + head, hb);
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc((const uint16_t*)a.dout + head, hb);
+  const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.lse + (int64_t)bh * N, N * 4);
+  const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.delta + (int64_t)bh * N, N * 4);
+
+  // Q and dO rows of this lane's query as B operands.
+  u32x4 qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+    qf[kc] = buf_load16(qr, (my_q * D + kc * 16 + grp * 8) * 2);
+    gf[kc] = buf_load16(gr, (my_q * D + kc * 16 + grp * 8) * 2);
+  }
+  const float lse2 =
+      lse_log2(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, my_q * 4, 0, 0)));
+  const float drow =
+      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dr, my_q * 4, 0, 0));
+
+  const int kv_end = CAUSAL ? min(q0 + kBwdRows, N) : N;
+  const int n_kv = (kv_end + kBT - 1) / kBT;
+  const int wave_kv_end = CAUSAL ? min(qw0 + 32, N) : N;
+
+  // Staging of one key tile: (row pair, 8 columns) units of K then V.
+  constexpr int kUnits = 2 * T::kPairUnits;
+  constexpr int kPer = (kUnits + kBwdThreads - 1) / kBwdThreads;
+  u32x4 sx[kPer], sy[kPer];
+  static_assert(T::kPairUnits % 64 == 0 && kUnits % kBwdThreads == 0, "unit split");
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = tid + i * kBwdThreads;
+      const int w = u % T::kPairUnits;
+      const int p = w % (kBT / 2), cc = w / (kBT / 2);
+      if (wave * 64 + i * kBwdThreads < T::kPairUnits)
+        load_pair<D>(kr, k0, p, cc, sx[i], sy[i]);
+      else
+        load_pair<D>(vr, k0, p, cc, sx[i], sy[i]);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* base = lds + buf * kStage;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = tid + i * kBwdThreads;
+      const int w = u % T::kPairUnits;
+      const int p = w % (kBT / 2), cc = w / (kBT / 2);
+      if (wave * 64 + i * kBwdThreads < T::kPairUnits) {
+        store_rows<D>(base, p, cc, sx[i], sy[i]);                 // Kr
+        store_cols<D>(base + T::kRowElems, p, cc, sx[i], sy[i]);  // Kt
+      } else {
+        store_rows<D>(base + T::kRowElems + T::kTElems, p, cc, sx[i], sy[i]);  // Vr
+      }
+    }
+  };
+
+  const float c = a.scale_log2;
+  f32x16 dqT[D / 32];  // dQ^T: lane holds query my_q
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dqT[db] = (f32x16){};
+
+  load_tile(0);
+  store_tile(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_kv; ++t) {
+    const int k0 = t * kBT, buf = t & 1;
+    const bool more = t + 1 < n_kv;
+    if (more) load_tile(k0 + kBT);
+
+    if (k0 < wave_kv_end) {
+      const uint16_t* krm = lds + buf * kStage;
+      const uint16_t* ktm = krm + T::kRowElems;
+      const uint16_t* vrm = ktm + T::kTElems;
+
+      // S^T = K Q^T, dP^T = V dO^T: lane holds query my_q, keys
+      // k0 + 8 (r/4) + 4 grp + r%4.
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const u32x4 ka = *(const u32x4*)(krm + col * T::kRowStride + kc * 16 + grp * 8);
+        s = HH::mfma(ka, qf[kc], s);
+      }
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const u32x4 va = *(const u32x4*)(vrm + col * T::kRowStride + kc * 16 + grp * 8);
+        dp = HH::mfma(va, gf[kc], dp);
+      }
+
+      const bool edge = k0 + kBT > N || (CAUSAL && k0 + kBT - 1 > qw0);
+      float dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(s[r], c, -lse2));
+        if (edge) {
+          const int key = k0 + 8 * (r >> 2) + 4 * grp + (r & 3);
+          const bool ok = key < N && (!CAUSAL || key <= my_q);
+          p = ok ? p : 0.f;
+        }
+        dsv[r] = p * (dp[r] - drow);
+      }
+      uint32_t pd[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pd[i] = HH::pack(dsv[2 * i], dsv[2 * i + 1]);
+
+      // dQ^T += K^T dS^T over the two 16-key chunks.
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+          const u32x4 bd = {pd[4 * ch], pd[4 * ch + 1], pd[4 * ch + 2], pd[4 * ch + 3]};
+          const u32x4 ka = *(const u32x4*)(ktm + (db * 32 + col) * T::kTStride + ch * 16 + grp * 8);
+          dqT[db] = HH::mfma(ka, bd, dqT[db]);
+        }
+    }
+
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (my_q < N) {
+    uint16_t* g = (uint16_t*)a.dq + head + (int64_t)my_q * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = db * 32 + 8 * j + 4 * grp;
+        const u32x2 w = {HH::pack(dqT[db][4 * j] * a.scale, dqT[db][4 * j + 1] * a.scale),
+                         HH::pack(dqT[db][4 * j + 2] * a.scale, dqT[db][4 * j + 3] * a.scale)};
+        *(u32x2*)(g + d0) = w;
+      }
+  }
+}
+
+template <bool BF16, bool CAUSAL, int D>
+hipError_t launch_bwd(const BwdArgs& a, const void* o, float* delta, hipStream_t s) {
+  // D_i = dO_i . O_i for every row
+  const int64_t rows = (int64_t)a.bh * a.n;
+  constexpr int kRowsPerBlock = 256 / (D / 8);
+  const uint16_t* op = (const uint16_t*)o;
+  const uint16_t* gp = (const uint16_t*)a.dout;
+  int64_t rows_arg = rows;
+  void* p0[] = {&op, &gp, &delta, &rows_arg};
+  hipError_t e = hipLaunchKernel((const void*)&bwd_delta_kernel<BF16, D>,
+                                 dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                                 dim3(256), p0, 0, s);
+  if (e != hipSuccess) return e;
+  BwdArgs args = a;
+  int n_t = (a.n + kBwdRows - 1) / kBwdRows;
+  int total = (int)((int64_t)n_t * a.bh);
+  void* p1[] = {&args, &n_t, &total};
+  e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<BF16, CAUSAL, D>, dim3(total),
+                      dim3(kBwdThreads), p1, 0, s);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel((const void*)&bwd_dq_kernel<BF16, CAUSAL, D>, dim3(total),
+                         dim3(kBwdThreads), p1, 0, s);
+}
+
+template <bool BF16, int D>
+hipError_t launch_d(bool causal, const BwdArgs& a, const void* o, float* delta, hipStream_t s) {
+  return causal ? launch_bwd<BF16, true, D>(a, o, delta, s)
+                : launch_bwd<BF16, false, D>(a, o, delta, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_h16(bool bf16, int d, bool causal, const BwdArgs& a, const void* o,
+                          float* delta, hipStream_t s) {
+  if (bf16)
+    return d == 64 ? launch_d<true, 64>(causal, a, o, delta, s)
+                   : launch_d<true, 128>(causal, a, o, delta, s);
+  return d == 64 ? launch_d<false, 64>(causal, a, o, delta, s)
+                 : launch_d<false, 128>(causal, a, o, delta, s);
+}
+
+int64_t bwd_grid_blocks(int64_t bh, int64_t n) {
+  return (n + kBwdRows - 1) / kBwdRows * bh;
+}
+
+}  // namespace fa_impl

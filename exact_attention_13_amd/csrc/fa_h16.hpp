@@ -25,6 +25,11 @@ struct Half<true> {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
   }
+  // acc + x.lo * y.lo + x.hi * y.hi (products exact in fp32)
+  static __device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
+                                           __builtin_bit_cast(bf16x2, y), acc, false);
+  }
 };
 
 template <>
@@ -40,6 +45,10 @@ struct Half<false> {
   static __device__ __forceinline__ float dot2(uint32_t p, float acc) {
     const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), one, acc, false);
+  }
+  static __device__ __forceinline__ float dot2(uint32_t x, uint32_t y, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, y),
+                                  acc, false);
   }
 };
 

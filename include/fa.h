@@ -50,7 +50,7 @@ typedef enum {
   FA_ERR_NULL = 1,     /* a required pointer (q, k, v, o, partials) is NULL     */
   FA_ERR_SHAPE = 2,    /* a size negative, H not a multiple of H_kv, too large  */
   FA_ERR_HEAD_DIM = 3, /* d is not one of the supported head sizes (64, 128)    */
-  FA_ERR_DTYPE = 4,    /* dtype is not an fa_dtype value                        */
+  FA_ERR_DTYPE = 4,    /* dtype not an fa_dtype value (fa_bwd: FA_F32 too)      */
   FA_ERR_SCALE = 5,    /* scale is not finite or not > 0                        */
   FA_ERR_ALIGN = 6,    /* a tensor not 16-byte aligned, lse not 4-byte          */
   FA_ERR_ALIAS = 7,    /* an output or the workspace overlaps another buffer    */
@@ -176,6 +176,40 @@ int64_t fa_fwd_ex_default_splits(int64_t B, int64_t H, int64_t H_kv, int64_t N_q
 fa_status fa_lse_combine(const float* o_part, const float* lse_part, int64_t splits,
                          int64_t rows, int64_t d, void* o, float* lse, fa_dtype dtype,
                          void* stream);
+
+/*
+ * fa_bwd -- gradients of the forward pass: given dO = dL/dO for
+ * O = softmax(Q K^T * scale) V, computes dQ, dK, dV.
+ *
+ * The attention weights are not stored by fa_fwd; they are recomputed from
+ * q, k and the forward pass's `lse` ("FlashAttention dissected", section
+ * "Memory complexity: from O(N^2) to O(N)": the backward pass recomputes
+ * what it needs from Q, K, V and the saved softmax statistics).  With
+ * P_ij = exp(scale q_i.k_j - LSE_i) on the visible keys:
+ *     D_i = dO_i . O_i,   dS_ij = P_ij (dO_i . v_j - D_i),
+ *     dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,
+ *     dQ_i = scale sum_j dS_ij k_j.
+ *
+ * q, k, v, o   the forward call's inputs and output: device, contiguous
+ *              [B, H, N, d] of `dtype` (FA_BF16 or FA_F16; FA_F32 returns
+ *              FA_ERR_DTYPE), read only.
+ * dout         device [B, H, N, d] of `dtype`: dL/dO, read only.
+ * lse          device fp32 [B, H, N]: the lse fa_fwd wrote for the same
+ *              q, k, v, scale and causal flag, read only.
+ * dq, dk, dv   device [B, H, N, d] of `dtype`, written in full (rounded to
+ *              nearest-even from fp32 accumulators).
+ * delta        device fp32 [B, H, N], caller-owned scratch: overwritten with
+ *              D_i = dO_i . O_i (the row dot products the gradients use).
+ * B, H, N, d, scale, causal: as fa_fwd.
+ * Buffers: 16-byte aligned (lse and delta 4-byte); outputs and delta may
+ * not overlap each other or any input.  Runs three kernels on `stream`
+ * (row dot products, then dK/dV, then dQ); no atomics, so results are
+ * bitwise reproducible.  Validation, ordering and ownership as fa_fwd.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B,
+                 int64_t H, int64_t N, int64_t d, float scale, int causal, fa_dtype dtype,
+                 void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(fa_status s);

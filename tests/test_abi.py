@@ -204,3 +204,37 @@ def test_lse_combine_rejects(kw, status):
 
 def test_lse_combine_empty_is_a_noop():
     assert libfa.fa_lse_combine(Q, K, 3, 0, 64, O, L, libfa.FA_F32, None) == 0
+
+
+# --------------------------------------------------------------------------
+# fa_bwd (validation only, no launch)
+# --------------------------------------------------------------------------
+
+OB, GB, DQ, DK, DV, DL = (BASE + (6 + i) * (1 << 32) for i in range(6))
+BWD_ARGS = dict(q=Q, k=K, v=V, o=OB, dout=GB, lse=L, dq=DQ, dk=DK, dv=DV, delta=DL, B=1, H=2,
+                N=256, d=64, scale=0.125, causal=1, dtype=libfa.FA_BF16, stream=None)
+
+
+def call_bwd(**kw):
+    a = dict(BWD_ARGS)
+    a.update(kw)
+    return libfa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                        a["dv"], a["delta"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                        a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(dout=None), 1), (dict(lse=None), 1), (dict(dv=None), 1),
+    (dict(delta=None), 1), (dict(N=-1), 2), (dict(N=1 << 31), 2), (dict(d=32), 3),
+    (dict(dtype=libfa.FA_F32), 4), (dict(dtype=3), 4), (dict(scale=0.0), 5),
+    (dict(dq=DQ + 8), 6), (dict(o=OB + 4), 6), (dict(delta=DL + 2), 6),
+    (dict(dq=Q), 7), (dict(dk=DQ + 64), 7), (dict(dv=GB), 7), (dict(delta=L), 7),
+    (dict(delta=DV + 128), 7), (dict(dk=K - 16), 7),
+])
+def test_bwd_rejects(kw, status):
+    assert call_bwd(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
+def test_bwd_empty_is_a_noop(kw):
+    assert call_bwd(**kw) == 0

@@ -59,19 +59,37 @@ MUTANTS = {
 }
 
 
-@pytest.mark.slow
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_mutant_is_caught(tmp_path, name):
+def _run_mutant(name, workdir):
     old, new = MUTANTS[name]
     text = SRC.read_text()
-    assert text.count(old) == 1, f"mutation anchor for {name} not found exactly once"
-    src = tmp_path / "fa_oracle_mutant.c"
+    if text.count(old) != 1:
+        return name, None, f"mutation anchor for {name} not found exactly once"
+    src = workdir / f"fa_oracle_{name}.c"
     src.write_text(text.replace(old, new))
-    lib = tmp_path / "liboracle_mutant.so"
+    lib = workdir / f"liboracle_{name}.so"
     subprocess.run(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-pthread", "-o",
                     str(lib), str(src), "-lm"], check=True)
-    env = dict(os.environ, FA_ORACLE_LIB=str(lib))
+    env = dict(os.environ, FA_ORACLE_LIB=str(lib), OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         str(ROOT / "tests" / "test_oracle_pins.py")],
-                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
+    return name, r.returncode, r.stdout[-2000:]
+
+
+@pytest.fixture(scope="module")
+def mutant_results(tmp_path_factory):
+    """Run every mutant's pin suite, several at a time (each is one process)."""
+    from concurrent.futures import ThreadPoolExecutor
+    workdir = tmp_path_factory.mktemp("mutants")
+    workers = max(1, min(6, (os.cpu_count() or 2) - 1))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        results = list(pool.map(lambda n: _run_mutant(n, workdir), sorted(MUTANTS)))
+    return {name: (rc, out) for name, rc, out in results}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(mutant_results, name):
+    rc, out = mutant_results[name]
+    assert rc is not None, out
+    assert rc != 0, f"mutant {name} passed every pin:\n{out}"
