@@ -220,65 +220,64 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
       const int buf = C::kStages == 2 ? (t & 1) : 0;
       const uint16_t* ks = lds + buf * C::kKStage;
       const uint16_t* vs = lds + C::kStages * C::kKStage + buf * C::kVStage;
-
-      // S^T = K Q^T: lane holds keys k0 + 32*kb + 8*(r/4) + 4*grp + r%4 of
-      // query qw0 + 32*qb + col.
-      f32x16 s[QB][BN / 32];
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = (f32x16){};
-#pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-          const u32x4 ka =
-              *(const u32x4*)(ks + (kb * 32 + col) * C::kKStride + kc * 16 + grp * 8);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = HH::mfma(ka, qf[qb][kc], s[qb][kb]);
-        }
-      }
-
       const bool ragged = k0 + BN > NK;
       const bool diag = CAUSAL && (k0 + BN - 1 > qw0 + off);
-      if (ragged || diag) {
+
+      // S^T = K Q^T for row block qb: lane holds keys
+      // k0 + 32*kb + 8*(r/4) + 4*grp + r%4 of query qw0 + 32*qb + col.
+      auto qk = [&](int qb, f32x16 (&sv)[BN / 32]) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+        for (int kb = 0; kb < BN / 32; ++kb) {
+          sv[kb] = (f32x16){};
+#pragma unroll
+          for (int kc = 0; kc < D / 16; ++kc) {
+            const u32x4 ka =
+                *(const u32x4*)(ks + (kb * 32 + col) * C::kKStride + kc * 16 + grp * 8);
+            sv[kb] = HH::mfma(ka, qf[qb][kc], sv[kb]);
+          }
+        }
+      };
+      auto mask = [&](int qb, f32x16 (&sv)[BN / 32]) {
+        if (ragged || diag) {
 #pragma unroll
           for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
               const bool masked = key >= NK || (CAUSAL && key > qw0 + 32 * qb + col + off);
-              s[qb][kb][r] = masked ? kNegInf : s[qb][kb][r];
+              sv[kb][r] = masked ? kNegInf : sv[kb][r];
             }
-      }
+        }
+      };
 
+      // P = exp2(S c - m c), rounded; the row sum adds the rounded pairs, so
+      // the weights that multiply V sum exactly to l.
       uint32_t pk[QB][BN / 32][8];
+      auto exp_row = [&](int qb, const f32x16 (&sv)[BN / 32], float nmc) {
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent sum chains
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        // P = exp2(S c - m c), rounded; the row sum adds the rounded pairs,
-        // so the weights that multiply V sum exactly to l.
-        auto exp_row = [&](float nmc) {
-          float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent sum chains
+        for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-          for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float p0 = fast_exp2(fmaf(s[qb][kb][2 * j], c, nmc));
-              const float p1 = fast_exp2(fmaf(s[qb][kb][2 * j + 1], c, nmc));
-              pk[qb][kb][j] = HH::pack(p0, p1);
-              ls[j & 3] = HH::dot2(pk[qb][kb][j], ls[j & 3]);
-            }
-          return (ls[0] + ls[1]) + (ls[2] + ls[3]);
-        };
-        // Fast path: no row max.  P is formed against the current reference
-        // max m, and the lane's partial sum bounds every weight it added; a
-        // sum <= 2^15 means no weight can overflow fp16/bf16.  Otherwise (a
-        // score rose well above m, or the row has no m yet: the shift is
-        // +inf and the sum inf/NaN) take the exact max over both half-waves,
-        // rescale O and l by exp2((m_old - m_new) c) and recompute P.
-        float lt = exp_row(m_run[qb] == kNegInf ? __builtin_inff() : -m_run[qb] * c);
+          for (int j = 0; j < 8; ++j) {
+            const float p0 = fast_exp2(fmaf(sv[kb][2 * j], c, nmc));
+            const float p1 = fast_exp2(fmaf(sv[kb][2 * j + 1], c, nmc));
+            pk[qb][kb][j] = HH::pack(p0, p1);
+            ls[j & 3] = HH::dot2(pk[qb][kb][j], ls[j & 3]);
+          }
+        return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      };
+      // Fast path: no row max.  P is formed against the current reference
+      // max m, and the lane's partial sum bounds every weight it added; a sum
+      // <= 2^15 means no weight can overflow fp16/bf16.  Otherwise (a score
+      // rose well above m, or the row has no m yet: the shift is +inf and
+      // the sum inf/NaN) take the exact max over both half-waves, rescale O
+      // and l by exp2((m_old - m_new) c) and recompute P.
+      auto fast = [&](int qb, const f32x16 (&sv)[BN / 32]) {
+        return exp_row(qb, sv, m_run[qb] == kNegInf ? __builtin_inff() : -m_run[qb] * c);
+      };
+      auto settle = [&](int qb, const f32x16 (&sv)[BN / 32], float lt) {
         if (__any(!(lt <= kFastSumLimit))) {
-          float mx = tree_max<BN / 32>(s[qb]);
+          float mx = tree_max<BN / 32>(sv);
           mx = half_swap_max(mx);
           const float m_new = fmaxf(m_run[qb], mx);
           const float alpha = m_new > m_run[qb] ? fast_exp2((m_run[qb] - m_new) * c) : 1.f;
@@ -286,26 +285,51 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
           m_run[qb] = m_new;
-          lt = exp_row(m_run[qb] == kNegInf ? 0.f : -m_run[qb] * c);
+          lt = exp_row(qb, sv, m_run[qb] == kNegInf ? 0.f : -m_run[qb] * c);
         }
         l_run[qb] += lt;
-      }
-
+      };
       // O^T += V^T P^T over 16-key chunks.
+      auto pv = [&](int qb) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int pc = 0; pc < BN / 16; ++pc) {
-          const u32x4 va =
-              *(const u32x4*)(vs + (db * 32 + col) * C::kVStride + pc * 16 + grp * 8);
-          const int kb = pc >> 1, h = (pc & 1) * 4;
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
+          for (int pc = 0; pc < BN / 16; ++pc) {
+            const u32x4 va =
+                *(const u32x4*)(vs + (db * 32 + col) * C::kVStride + pc * 16 + grp * 8);
+            const int kb = pc >> 1, h = (pc & 1) * 4;
             const u32x4 pb = {pk[qb][kb][h], pk[qb][kb][h + 1], pk[qb][kb][h + 2],
                               pk[qb][kb][h + 3]};
             oacc[qb][db] = HH::mfma(va, pb, oacc[qb][db]);
           }
-        }
+      };
+
+      if constexpr (QB == 2) {
+        // The two 32-row blocks are independent: issued in this order, the
+        // QK MFMAs of block 1 run under the softmax of block 0 and the PV
+        // MFMAs of block 0 under the softmax of block 1, so each wave keeps
+        // its matrix pipe busy while its VALU works (+4 % on the d = 64
+        // headline shape against QK, QK, softmax, softmax, PV, PV).
+        f32x16 s0[BN / 32], s1[BN / 32];
+        qk(0, s0);
+        mask(0, s0);
+        qk(1, s1);
+        const float lt0 = fast(0, s0);
+        settle(0, s0, lt0);
+        mask(1, s1);
+        pv(0);
+        const float lt1 = fast(1, s1);
+        settle(1, s1, lt1);
+        pv(1);
+      } else {
+        static_assert(QB == 1, "row blocks per wave");
+        f32x16 s0[BN / 32];
+        qk(0, s0);
+        mask(0, s0);
+        const float lt0 = fast(0, s0);
+        settle(0, s0, lt0);
+        pv(0);
+      }
     }
 
     if (C::kStages == 1) __syncthreads();  // tile t's LDS reads are done
