@@ -19,7 +19,9 @@
 
 namespace {
 
-// Keys per split are a multiple of this (the largest key tile of any kernel).
+// Keys per split are a multiple of this.  A kernel whose key tile is larger
+// masks the keys past its range's end and skips compute steps that start
+// there.
 constexpr int64_t kSplitGranule = 64;
 // Most key ranges per problem a split launch uses.
 constexpr int64_t kMaxSplits = 256;

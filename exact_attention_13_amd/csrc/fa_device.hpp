@@ -43,7 +43,8 @@ constexpr float kRescaleLog2 = 8.0f;
 // Causal masking hides key j from row i when j > i + causal_off.
 //
 // Split launches cut the keys into ranges of kv_chunk keys (a multiple of
-// 64, so of every tile size): workgroup (p, split) attends to keys
+// 64; kernels mask keys past the end of their range): workgroup (p, split)
+// attends to keys
 // [split*kv_chunk, min((split+1)*kv_chunk, nk)) only and writes its partial
 // result in fp32, already divided by its own row sum, to
 // o + ((split*problems + p)*nq + i)*d, and its partial logsumexp to

@@ -86,7 +86,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
 
   // Keys of this workgroup and of this wave, as in the bf16/fp16 kernel.
   const int kbeg = SPLIT ? split * a.kv_chunk : 0;
-  int kstop = SPLIT ? min(kbeg + a.kv_chunk, NK) : NK;
+  const int kend = SPLIT ? min(kbeg + a.kv_chunk, NK) : NK;  // keys >= kend are masked
+  int kstop = kend;
   if (CAUSAL) kstop = min(kstop, q0 + kBM + off);
   const int n_kv = kstop > kbeg ? (kstop - kbeg + kBN - 1) / kBN : 0;
   int wave_kv_end = CAUSAL ? min(qw0 + kQPerWave + off, NK) : NK;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
           for (int e = 0; e < 4; ++e) s[kb] = mfma_f32(ka[e], qf[j][e], s[kb]);
         }
 
-      const bool ragged = k0 + kBN > NK;
+      const bool ragged = k0 + kBN > kend;
       const bool diag = CAUSAL && (k0 + kBN - 1 > qw0 + off);
       if (ragged || diag) {
 #pragma unroll
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
-            const bool masked = key >= NK || (CAUSAL && key > my_q + off);
+            const bool masked = key >= kend || (CAUSAL && key > my_q + off);
             s[kb][r] = masked ? kNegInf : s[kb][r];
           }
       }

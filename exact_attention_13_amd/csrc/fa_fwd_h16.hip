@@ -85,6 +85,9 @@ template <bool BF16, bool CAUSAL, bool SPLIT, class C>
 __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_qt, int total) {
   using HH = Half<BF16>;
   constexpr int D = C::D, QB = C::QB, BN = C::BN;
+  // keys per compute step: a staged tile of BN keys is consumed in BN / SB
+  // steps, so a larger tile costs LDS but no registers
+  constexpr int SB = BN > 64 ? 64 : BN;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLdsElems];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -125,7 +128,8 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
   // tile's last row may see.  A wave stops at its own last visible key, and
   // a wave whose rows all lie past the end does no arithmetic at all.
   const int kbeg = SPLIT ? split * a.kv_chunk : 0;
-  int kstop = SPLIT ? min(kbeg + a.kv_chunk, NK) : NK;
+  const int kend = SPLIT ? min(kbeg + a.kv_chunk, NK) : NK;  // keys >= kend are masked
+  int kstop = kend;
   if (CAUSAL) kstop = min(kstop, q0 + C::kBM + off);
   const int n_kv = kstop > kbeg ? (kstop - kbeg + BN - 1) / BN : 0;
   int wave_kv_end = CAUSAL ? min(qw0 + C::kQPerWave + off, NK) : NK;
@@ -216,18 +220,21 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
     const bool more = t + 1 < n_kv;
     if (more) load_tile(k0 + BN);
 
-    if (k0 < wave_kv_end) {
-      const int buf = C::kStages == 2 ? (t & 1) : 0;
-      const uint16_t* ks = lds + buf * C::kKStage;
-      const uint16_t* vs = lds + C::kStages * C::kKStage + buf * C::kVStage;
-      const bool ragged = k0 + BN > NK;
-      const bool diag = CAUSAL && (k0 + BN - 1 > qw0 + off);
+    const int buf = C::kStages == 2 ? (t & 1) : 0;
+#pragma unroll
+    for (int hsub = 0; hsub < BN / SB; ++hsub)
+    if (k0 + hsub * SB < wave_kv_end && k0 + hsub * SB < kend) {
+      const int kh = k0 + hsub * SB;
+      const uint16_t* ks = lds + buf * C::kKStage + hsub * SB * C::kKStride;
+      const uint16_t* vs = lds + C::kStages * C::kKStage + buf * C::kVStage + hsub * SB;
+      const bool ragged = kh + SB > kend;
+      const bool diag = CAUSAL && (kh + SB - 1 > qw0 + off);
 
       // S^T = K Q^T for row block qb: lane holds keys
       // k0 + 32*kb + 8*(r/4) + 4*grp + r%4 of query qw0 + 32*qb + col.
-      auto qk = [&](int qb, f32x16 (&sv)[BN / 32]) {
+      auto qk = [&](int qb, f32x16 (&sv)[SB / 32]) {
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
+        for (int kb = 0; kb < SB / 32; ++kb) {
           sv[kb] = (f32x16){};
 #pragma unroll
           for (int kc = 0; kc < D / 16; ++kc) {
@@ -237,14 +244,14 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
           }
         }
       };
-      auto mask = [&](int qb, f32x16 (&sv)[BN / 32]) {
+      auto mask = [&](int qb, f32x16 (&sv)[SB / 32]) {
         if (ragged || diag) {
 #pragma unroll
-          for (int kb = 0; kb < BN / 32; ++kb)
+          for (int kb = 0; kb < SB / 32; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
-              const bool masked = key >= NK || (CAUSAL && key > qw0 + 32 * qb + col + off);
+              const int key = kh + kb * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
+              const bool masked = key >= kend || (CAUSAL && key > qw0 + 32 * qb + col + off);
               sv[kb][r] = masked ? kNegInf : sv[kb][r];
             }
         }
@@ -252,11 +259,11 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
 
       // P = exp2(S c - m c), rounded; the row sum adds the rounded pairs, so
       // the weights that multiply V sum exactly to l.
-      uint32_t pk[QB][BN / 32][8];
-      auto exp_row = [&](int qb, const f32x16 (&sv)[BN / 32], float nmc) {
+      uint32_t pk[QB][SB / 32][8];
+      auto exp_row = [&](int qb, const f32x16 (&sv)[SB / 32], float nmc) {
         float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent sum chains
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
+        for (int kb = 0; kb < SB / 32; ++kb)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float p0 = fast_exp2(fmaf(sv[kb][2 * j], c, nmc));
@@ -272,12 +279,12 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
       // rose well above m, or the row has no m yet: the shift is +inf and
       // the sum inf/NaN) take the exact max over both half-waves, rescale O
       // and l by exp2((m_old - m_new) c) and recompute P.
-      auto fast = [&](int qb, const f32x16 (&sv)[BN / 32]) {
+      auto fast = [&](int qb, const f32x16 (&sv)[SB / 32]) {
         return exp_row(qb, sv, m_run[qb] == kNegInf ? __builtin_inff() : -m_run[qb] * c);
       };
-      auto settle = [&](int qb, const f32x16 (&sv)[BN / 32], float lt) {
+      auto settle = [&](int qb, const f32x16 (&sv)[SB / 32], float lt) {
         if (__any(!(lt <= kFastSumLimit))) {
-          float mx = tree_max<BN / 32>(sv);
+          float mx = tree_max<SB / 32>(sv);
           mx = half_swap_max(mx);
           const float m_new = fmaxf(m_run[qb], mx);
           const float alpha = m_new > m_run[qb] ? fast_exp2((m_run[qb] - m_new) * c) : 1.f;
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int pc = 0; pc < BN / 16; ++pc) {
+          for (int pc = 0; pc < SB / 16; ++pc) {
             const u32x4 va =
                 *(const u32x4*)(vs + (db * 32 + col) * C::kVStride + pc * 16 + grp * 8);
             const int kb = pc >> 1, h = (pc & 1) * 4;
@@ -310,7 +317,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
         // MFMAs of block 0 under the softmax of block 1, so each wave keeps
         // its matrix pipe busy while its VALU works (+4 % on the d = 64
         // headline shape against QK, QK, softmax, softmax, PV, PV).
-        f32x16 s0[BN / 32], s1[BN / 32];
+        f32x16 s0[SB / 32], s1[SB / 32];
         qk(0, s0);
         mask(0, s0);
         qk(1, s1);
@@ -323,7 +330,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
         pv(1);
       } else {
         static_assert(QB == 1, "row blocks per wave");
-        f32x16 s0[BN / 32];
+        f32x16 s0[SB / 32];
         qk(0, s0);
         mask(0, s0);
         const float lt0 = fast(0, s0);
@@ -389,13 +396,15 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
 
 // Instance table: one tile configuration per head size (measured on MI355X:
 // d = 64 is VALU-heavy, so eight waves of 64 query rows each halve the LDS
-// reads per MFMA; d = 128 prefers four waves of 32 rows with 32-key tiles).
+// reads per MFMA, and 128-key tiles, computed as two 64-key steps, halve the
+// workgroup barriers (the two waves that share a SIMD drift apart less
+// often); d = 128 prefers four waves of 32 rows with 32-key tiles).
 // Overridable at build time (FA_H16_D64_CFG / FA_H16_D128_CFG = QB, BN, NW).
 // Problems with at most 32 query rows (decoding, grouped heads packed into
 // rows) take a one-wave workgroup instead, so that the grid is made of key
 // ranges rather than of idle query rows.
 #ifndef FA_H16_D64_CFG
-#define FA_H16_D64_CFG 2, 64, 8
+#define FA_H16_D64_CFG 2, 128, 8
 #endif
 #ifndef FA_H16_D128_CFG
 #define FA_H16_D128_CFG 1, 32, 4

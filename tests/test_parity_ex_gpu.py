@@ -89,7 +89,10 @@ def test_unsplit_square_equals_fa_fwd_bitwise(dtype, d, causal):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_split_keys_small(dtype, d, causal):
-    for i, (n, splits) in enumerate([(65, 2), (200, 3), (513, 5), (1000, 16), (129, 300)]):
+    # (1000, 6): ranges of 192 keys, not a multiple of the 128-key tiles of
+    # the d = 64 kernel, so a tile crosses into the next range and must mask
+    for i, (n, splits) in enumerate([(65, 2), (200, 3), (513, 5), (1000, 16), (129, 300),
+                                     (1000, 6)]):
         w, (q, k, v) = case(dtype, 1 + i % 2, 2, 2, n, n, d, causal, seed=600 + i)
         _note(f"split {dtype} d={d} causal={causal} N={n} splits={splits}")
         o, lse = run_ex(q, k, v, w.scale, causal, num_splits=splits)
