@@ -233,43 +233,45 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdArgs a, int n_
 
       const int key = kw0 + col;
       const bool edge = q0 + kBT > N || kw0 + 32 > N || (CAUSAL && q0 < kw0 + 31);
-      float pv[16], dsv[16];
+      // One 16-query chunk at a time (registers 8 ch .. 8 ch + 7): P, dS,
+      // their packed pairs, then dV^T += dO^T P and dK^T += Q^T dS for the
+      // chunk, so only one chunk's weights are live.
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 l4 = *(const f32x4*)(&stat[buf][0][8 * j + 4 * grp]);
-        const f32x4 d4 = *(const f32x4*)(&stat[buf][1][8 * j + 4 * grp]);
+      for (int ch = 0; ch < 2; ++ch) {
+        uint32_t pp[4], pd[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * j + e;
-          float p = fast_exp2(fmaf(s[r], c, -l4[e]));
-          if (edge) {
-            const int q = q0 + 8 * j + 4 * grp + e;
-            const bool ok = q < N && key < N && (!CAUSAL || key <= q);
-            p = ok ? p : 0.f;
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * ch + jj;
+          const f32x4 l4 = *(const f32x4*)(&stat[buf][0][8 * j + 4 * grp]);
+          const f32x4 d4 = *(const f32x4*)(&stat[buf][1][8 * j + 4 * grp]);
+          float pv[4], dsv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * j + e;
+            float p = fast_exp2(fmaf(s[r], c, -l4[e]));
+            if (edge) {
+              const int q = q0 + 8 * j + 4 * grp + e;
+              const bool ok = q < N && key < N && (!CAUSAL || key <= q);
+              p = ok ? p : 0.f;
+            }
+            pv[e] = p;
+            dsv[e] = p * (dp[r] - d4[e]);
           }
-          pv[r] = p;
-          dsv[r] = p * (dp[r] - d4[e]);
+          pp[2 * jj] = HH::pack(pv[0], pv[1]);
+          pp[2 * jj + 1] = HH::pack(pv[2], pv[3]);
+          pd[2 * jj] = HH::pack(dsv[0], dsv[1]);
+          pd[2 * jj + 1] = HH::pack(dsv[2], dsv[3]);
         }
-      }
-      uint32_t pp[8], pd[8];
+        const u32x4 bp = {pp[0], pp[1], pp[2], pp[3]};
+        const u32x4 bd = {pd[0], pd[1], pd[2], pd[3]};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pp[i] = HH::pack(pv[2 * i], pv[2 * i + 1]);
-        pd[i] = HH::pack(dsv[2 * i], dsv[2 * i + 1]);
-      }
-
-      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query chunks.
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-          const u32x4 bp = {pp[4 * ch], pp[4 * ch + 1], pp[4 * ch + 2], pp[4 * ch + 3]};
-          const u32x4 bd = {pd[4 * ch], pd[4 * ch + 1], pd[4 * ch + 2], pd[4 * ch + 3]};
+        for (int db = 0; db < D / 32; ++db) {
           const u32x4 ga = *(const u32x4*)(gtm + (db * 32 + col) * T::kTStride + ch * 16 + grp * 8);
           const u32x4 qa = *(const u32x4*)(qtm + (db * 32 + col) * T::kTStride + ch * 16 + grp * 8);
           dvT[db] = HH::mfma(ga, bp, dvT[db]);
           dkT[db] = HH::mfma(qa, bd, dkT[db]);
         }
+      }
     }
 
     if (more) store_tile(buf ^ 1);
