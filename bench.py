@@ -50,9 +50,12 @@ KERNEL_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_fwd_h16.hip", "fa_fwd_f32.h
                   "fa_api.hip", "fa_combine.hip"]
 
 
-def kernel_source_hash() -> str:
+BWD_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_bwd_h16.hip", "fa_api.hip"]
+
+
+def kernel_source_hash(names=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in names:
         h.update((ROOT / "exact_attention_13_amd" / "csrc" / name).read_bytes())
     return h.hexdigest()[:16]
 

@@ -36,6 +36,18 @@ constexpr int kBwdRows = 32 * kBwdWaves;  // keys (dK/dV) or queries (dQ) per wo
 constexpr int kBT = 32;                   // rows of a streamed tile
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// Waves per SIMD that the register allocation must leave room for.  Both
+// kernels keep a wave's rows (K and V, or Q and dO) and its gradient
+// accumulators in registers; at d = 128 the dK/dV kernel needs a few more
+// than half the register file, and letting the compiler spill those few (two
+// reloads per query tile) so that two waves share a SIMD is worth +37-51 %,
+// because one wave's exponentials and packing then hide under the other's
+// MFMAs.  At d = 64 three dK/dV waves and four dQ waves per SIMD measured
+// best (+3 % non-causal, +8 % causal, where the dK/dV kernel reloads one
+// 16-byte fragment per query tile).
+template <int D> constexpr int kDkdvWaves = D == 128 ? 2 : 3;
+template <int D> constexpr int kDqWaves = D == 128 ? 2 : 4;
+
 template <int D>
 struct BwdTile {
   static constexpr int kRowStride = D + 8;  // row-major tile (+16 B per row)
@@ -114,7 +126,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 // dK, dV: one workgroup per (head, 128 keys)
 // ---------------------------------------------------------------------------
 template <bool BF16, bool CAUSAL, int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdArgs a, int n_kt, int total) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<D>))) void bwd_dkdv_kernel(BwdArgs a, int n_kt, int total) {
   using HH = Half<BF16>;
   using T = BwdTile<D>;
   constexpr int kStage = 2 * (T::kRowElems + T::kTElems);  // Qr, Qt, dOr, dOt
@@ -154,53 +166,69 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdArgs a, int n_
   const int qt_begin = CAUSAL ? k0 / kBT : 0;  // earlier queries see none of these keys
 
   // Staging of one query tile: (row pair, 8 columns) units of Q then dO,
-  // plus the tile's 32 lse and 32 D values.
+  // plus the tile's 32 lse and 32 D values.  Part i of the units goes through
+  // register slot i; at d = 128 there are two parts (Q, then dO) and they
+  // share one slot: the Q half of the next tile is stored halfway through the
+  // current tile, before the dO half is loaded, so only one half is in flight
+  // (16 fewer live registers, which lets two waves share a SIMD).
   constexpr int kUnits = 2 * T::kPairUnits;
   constexpr int kPer = (kUnits + kBwdThreads - 1) / kBwdThreads;
-  u32x4 sx[kPer], sy[kPer];
+  constexpr bool kHalves = kPer == 2;
+  constexpr int kSlots = kHalves ? 1 : kPer;
+  u32x4 sx[kSlots], sy[kSlots];
   float st = 0.f;
   // Units are dealt by whole waves (kPairUnits is a multiple of 64), so the
   // Q-or-dO choice is wave-uniform and the buffer resource stays scalar.
   static_assert(T::kPairUnits % 64 == 0 && kUnits % kBwdThreads == 0, "unit split");
-  auto load_tile = [&](int q0) {
+  auto load_part = [&](int q0, int i0, int i1) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int u = tid + i * kBwdThreads;
       const int w = u % T::kPairUnits;
       const int p = w % (kBT / 2), cc = w / (kBT / 2);
+      const int sl = kHalves ? 0 : i;
       if (wave * 64 + i * kBwdThreads < T::kPairUnits)
-        load_pair<D>(qr, q0, p, cc, sx[i], sy[i]);
+        load_pair<D>(qr, q0, p, cc, sx[sl], sy[sl]);
       else
-        load_pair<D>(gr, q0, p, cc, sx[i], sy[i]);
+        load_pair<D>(gr, q0, p, cc, sx[sl], sy[sl]);
     }
-    if (tid < kBT)
-      st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, (q0 + tid) * 4, 0, 0));
-    else if (tid < 2 * kBT)
-      st = __builtin_bit_cast(float,
-                              __builtin_amdgcn_raw_buffer_load_b32(dr, (q0 + tid - kBT) * 4, 0, 0));
+    if (i0 == 0) {
+      if (tid < kBT)
+        st = __builtin_bit_cast(float,
+                                __builtin_amdgcn_raw_buffer_load_b32(lr, (q0 + tid) * 4, 0, 0));
+      else if (tid < 2 * kBT)
+        st = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(dr, (q0 + tid - kBT) * 4, 0, 0));
+    }
   };
-  auto store_tile = [&](int buf) {
+  auto store_part = [&](int buf, int i0, int i1) {
     uint16_t* base = lds + buf * kStage;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int u = tid + i * kBwdThreads;
       const int w = u % T::kPairUnits;
       const int p = w % (kBT / 2), cc = w / (kBT / 2);
+      const int sl = kHalves ? 0 : i;
       const bool first = wave * 64 + i * kBwdThreads < T::kPairUnits;
       uint16_t* rm = base + (first ? 0 : T::kRowElems + T::kTElems);
-      store_rows<D>(rm, p, cc, sx[i], sy[i]);
-      store_cols<D>(rm + T::kRowElems, p, cc, sx[i], sy[i]);
+      store_rows<D>(rm, p, cc, sx[sl], sy[sl]);
+      store_cols<D>(rm + T::kRowElems, p, cc, sx[sl], sy[sl]);
     }
-    if (tid < 2 * kBT) stat[buf][tid / kBT][tid % kBT] = tid < kBT ? lse_log2(st) : st;
+    if (i0 == 0 && tid < 2 * kBT) stat[buf][tid / kBT][tid % kBT] = tid < kBT ? lse_log2(st) : st;
   };
+  constexpr int kFirst = kHalves ? 1 : kPer;  // parts loaded at the top of an iteration
 
   const float c = a.scale_log2;
   f32x16 dkT[D / 32], dvT[D / 32];  // dK^T, dV^T: lane holds key kw0 + col
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dkT[db] = dvT[db] = (f32x16){};
 
-  load_tile(qt_begin * kBT);
-  store_tile(0);
+  load_part(qt_begin * kBT, 0, kFirst);
+  store_part(0, 0, kFirst);
+  if (kHalves) {
+    load_part(qt_begin * kBT, 1, 2);
+    store_part(0, 1, 2);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -208,18 +236,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdArgs a, int n_
     const int it = qt - qt_begin, buf = it & 1;
     const int q0 = qt * kBT;
     const bool more = qt + 1 < n_qt;
-    if (more) load_tile(q0 + kBT);
+    if (more) load_part(q0 + kBT, 0, kFirst);
 
     // causal: a tile whose last query comes before this wave's first key is empty
-    if (!(CAUSAL && q0 + kBT - 1 < kw0)) {
-      const uint16_t* qrm = lds + buf * kStage;
-      const uint16_t* qtm = qrm + T::kRowElems;
-      const uint16_t* grm = qtm + T::kTElems;
-      const uint16_t* gtm = grm + T::kRowElems;
+    const bool active = !(CAUSAL && q0 + kBT - 1 < kw0);
+    const uint16_t* qrm = lds + buf * kStage;
+    const uint16_t* qtm = qrm + T::kRowElems;
+    const uint16_t* grm = qtm + T::kTElems;
+    const uint16_t* gtm = grm + T::kRowElems;
 
-      // S = Q K^T and dP = dO V^T: lane holds key kw0 + col of the queries
-      // q0 + 8 (r/4) + 4 grp + r%4.
-      f32x16 s = {}, dp = {};
+    // S = Q K^T and dP = dO V^T: lane holds key kw0 + col of the queries
+    // q0 + 8 (r/4) + 4 grp + r%4.
+    f32x16 s = {}, dp = {};
+    if (active) {
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
         const u32x4 qa = *(const u32x4*)(qrm + col * T::kRowStride + kc * 16 + grp * 8);
@@ -230,51 +259,55 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdArgs a, int n_
         const u32x4 ga = *(const u32x4*)(grm + col * T::kRowStride + kc * 16 + grp * 8);
         dp = HH::mfma(ga, vf[kc], dp);
       }
-
-      const int key = kw0 + col;
-      const bool edge = q0 + kBT > N || kw0 + 32 > N || (CAUSAL && q0 < kw0 + 31);
-      // One 16-query chunk at a time (registers 8 ch .. 8 ch + 7): P, dS,
-      // their packed pairs, then dV^T += dO^T P and dK^T += Q^T dS for the
-      // chunk, so only one chunk's weights are live.
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        uint32_t pp[4], pd[4];
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int j = 2 * ch + jj;
-          const f32x4 l4 = *(const f32x4*)(&stat[buf][0][8 * j + 4 * grp]);
-          const f32x4 d4 = *(const f32x4*)(&stat[buf][1][8 * j + 4 * grp]);
-          float pv[4], dsv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * j + e;
-            float p = fast_exp2(fmaf(s[r], c, -l4[e]));
-            if (edge) {
-              const int q = q0 + 8 * j + 4 * grp + e;
-              const bool ok = q < N && key < N && (!CAUSAL || key <= q);
-              p = ok ? p : 0.f;
-            }
-            pv[e] = p;
-            dsv[e] = p * (dp[r] - d4[e]);
-          }
-          pp[2 * jj] = HH::pack(pv[0], pv[1]);
-          pp[2 * jj + 1] = HH::pack(pv[2], pv[3]);
-          pd[2 * jj] = HH::pack(dsv[0], dsv[1]);
-          pd[2 * jj + 1] = HH::pack(dsv[2], dsv[3]);
-        }
-        const u32x4 bp = {pp[0], pp[1], pp[2], pp[3]};
-        const u32x4 bd = {pd[0], pd[1], pd[2], pd[3]};
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const u32x4 ga = *(const u32x4*)(gtm + (db * 32 + col) * T::kTStride + ch * 16 + grp * 8);
-          const u32x4 qa = *(const u32x4*)(qtm + (db * 32 + col) * T::kTStride + ch * 16 + grp * 8);
-          dvT[db] = HH::mfma(ga, bp, dvT[db]);
-          dkT[db] = HH::mfma(qa, bd, dkT[db]);
-        }
-      }
     }
 
-    if (more) store_tile(buf ^ 1);
+    const int key = kw0 + col;
+    const bool edge = q0 + kBT > N || kw0 + 32 > N || (CAUSAL && q0 < kw0 + 31);
+    // One 16-query chunk at a time (registers 8 ch .. 8 ch + 7): P, dS,
+    // their packed pairs, then dV^T += dO^T P and dK^T += Q^T dS for the
+    // chunk, so only one chunk's weights are live.
+    auto chunk = [&](int ch) {
+      uint32_t pp[4], pd[4];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * ch + jj;
+        const f32x4 l4 = *(const f32x4*)(&stat[buf][0][8 * j + 4 * grp]);
+        const f32x4 d4 = *(const f32x4*)(&stat[buf][1][8 * j + 4 * grp]);
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * j + e;
+          float p = fast_exp2(fmaf(s[r], c, -l4[e]));
+          if (edge) {
+            const int q = q0 + 8 * j + 4 * grp + e;
+            const bool ok = q < N && key < N && (!CAUSAL || key <= q);
+            p = ok ? p : 0.f;
+          }
+          pv[e] = p;
+          dsv[e] = p * (dp[r] - d4[e]);
+        }
+        pp[2 * jj] = HH::pack(pv[0], pv[1]);
+        pp[2 * jj + 1] = HH::pack(pv[2], pv[3]);
+        pd[2 * jj] = HH::pack(dsv[0], dsv[1]);
+        pd[2 * jj + 1] = HH::pack(dsv[2], dsv[3]);
+      }
+      const u32x4 bp = {pp[0], pp[1], pp[2], pp[3]};
+      const u32x4 bd = {pd[0], pd[1], pd[2], pd[3]};
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const u32x4 ga = *(const u32x4*)(gtm + (db * 32 + col) * T::kTStride + ch * 16 + grp * 8);
+        const u32x4 qa = *(const u32x4*)(qtm + (db * 32 + col) * T::kTStride + ch * 16 + grp * 8);
+        dvT[db] = HH::mfma(ga, bp, dvT[db]);
+        dkT[db] = HH::mfma(qa, bd, dkT[db]);
+      }
+    };
+    if (active) chunk(0);
+    if (kHalves && more) {
+      store_part(buf ^ 1, 0, 1);
+      load_part(q0 + kBT, 1, 2);
+    }
+    if (active) chunk(1);
+    if (more) store_part(buf ^ 1, kHalves ? 1 : 0, kPer);
     __syncthreads();
   }
 
@@ -302,7 +335,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdArgs a, int n_
 // dQ: one workgroup per (head, 128 queries)
 // ---------------------------------------------------------------------------
 template <bool BF16, bool CAUSAL, int D>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a, int n_qt, int total) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDqWaves<D>))) void bwd_dq_kernel(BwdArgs a, int n_qt, int total) {
   using HH = Half<BF16>;
   using T = BwdTile<D>;
   constexpr int kStage = 2 * T::kRowElems + T::kTElems;  // Kr, Kt, Vr
