@@ -25,6 +25,8 @@
 //     dP^T = V dO^T) and streams 32-key tiles of K (row-major and transposed)
 //     and V (row-major); dS^T is the B operand of dQ^T += K^T dS^T.
 // Causal masking, ragged tails and the -inf guard follow the forward kernels.
+#include <type_traits>
+
 #include "fa_h16.hpp"
 
 namespace fa_impl {
@@ -42,11 +44,11 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // than half the register file, and letting the compiler spill those few (two
 // reloads per query tile) so that two waves share a SIMD is worth +37-51 %,
 // because one wave's exponentials and packing then hide under the other's
-// MFMAs.  At d = 64 three dK/dV waves and four dQ waves per SIMD measured
-// best (+3 % non-causal, +8 % causal, where the dK/dV kernel reloads one
-// 16-byte fragment per query tile).
-template <int D> constexpr int kDkdvWaves = D == 128 ? 2 : 3;
-template <int D> constexpr int kDqWaves = D == 128 ? 2 : 4;
+// MFMAs.  At d = 64 the dQ kernel runs three waves per SIMD; the dK/dV kernel
+// stays at two, where its separate unmasked branch (below) fits without
+// spills.
+template <int D> constexpr int kDkdvWaves = 2;
+template <int D> constexpr int kDqWaves = D == 128 ? 2 : 3;
 
 template <int D>
 struct BwdTile {
@@ -266,8 +268,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     // One 16-query chunk at a time (registers 8 ch .. 8 ch + 7): P, dS,
     // their packed pairs, then dV^T += dO^T P and dK^T += Q^T dS for the
     // chunk, so only one chunk's weights are live.
-    auto chunk = [&](int ch) {
-      uint32_t pp[4], pd[4];
+    // Mask modes: 0 none, 1 always, 2 where `edge` holds.  At d = 64 the
+    // masked form is its own wave-uniform branch, taken only by diagonal and
+    // ragged tiles (as selects in every tile it costs four VALU instructions
+    // per score); at d = 128 the second copy of the code would cost more in
+    // spilled registers than the selects, so mode 2 folds the test into
+    // every tile.
+    auto weights = [&](auto mode, int ch, uint32_t* pp, uint32_t* pd) {
+      constexpr int M = decltype(mode)::value;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int j = 2 * ch + jj;
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * j + e;
           float p = fast_exp2(fmaf(s[r], c, -l4[e]));
-          if (edge) {
+          if (M == 1 || (M == 2 && edge)) {
             const int q = q0 + 8 * j + 4 * grp + e;
             const bool ok = q < N && key < N && (!CAUSAL || key <= q);
             p = ok ? p : 0.f;
@@ -290,6 +298,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
         pp[2 * jj + 1] = HH::pack(pv[2], pv[3]);
         pd[2 * jj] = HH::pack(dsv[0], dsv[1]);
         pd[2 * jj + 1] = HH::pack(dsv[2], dsv[3]);
+      }
+    };
+    auto chunk = [&](int ch) {
+      uint32_t pp[4], pd[4];
+      if constexpr (D == 64) {
+        if (edge)
+          weights(std::integral_constant<int, 1>{}, ch, pp, pd);
+        else
+          weights(std::integral_constant<int, 0>{}, ch, pp, pd);
+      } else {
+        weights(std::integral_constant<int, 2>{}, ch, pp, pd);
       }
       const u32x4 bp = {pp[0], pp[1], pp[2], pp[3]};
       const u32x4 bd = {pd[0], pd[1], pd[2], pd[3]};
@@ -446,21 +465,29 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
         dp = HH::mfma(va, gf[kc], dp);
       }
 
-      const bool edge = k0 + kBT > N || (CAUSAL && k0 + kBT - 1 > qw0);
-      float dsv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(s[r], c, -lse2));
-        if (edge) {
-          const int key = k0 + 8 * (r >> 2) + 4 * grp + (r & 3);
-          const bool ok = key < N && (!CAUSAL || key <= my_q);
-          p = ok ? p : 0.f;
-        }
-        dsv[r] = p * (dp[r] - drow);
-      }
+      // dS^T = P^T (dP^T - D).  The masked form runs only on diagonal and
+      // ragged tiles, as its own wave-uniform branch: folded into every tile
+      // as selects it would add four VALU instructions per score.
       uint32_t pd[8];
+      auto weights = [&](auto masked) {
+        float dsv[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pd[i] = HH::pack(dsv[2 * i], dsv[2 * i + 1]);
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(fmaf(s[r], c, -lse2));
+          if constexpr (decltype(masked)::value) {
+            const int key = k0 + 8 * (r >> 2) + 4 * grp + (r & 3);
+            const bool ok = key < N && (!CAUSAL || key <= my_q);
+            p = ok ? p : 0.f;
+          }
+          dsv[r] = p * (dp[r] - drow);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pd[i] = HH::pack(dsv[2 * i], dsv[2 * i + 1]);
+      };
+      if (k0 + kBT > N || (CAUSAL && k0 + kBT - 1 > qw0))
+        weights(std::true_type{});
+      else
+        weights(std::false_type{});
 
       // dQ^T += K^T dS^T over the two 16-key chunks.
 #pragma unroll
