@@ -11,7 +11,8 @@ Contents:
   * ``reference.fwd_gqa``   -- the same with grouped K/V heads and separate
                                query / key lengths (decoding);
   * ``reference.combine``   -- fp64 merge of results over disjoint key ranges;
-  * ``reference.bwd``       -- fp64 gradients of sum(dO * O) w.r.t. Q, K, V
+  * ``reference.bwd``       -- fp64 gradients of sum(dO * O) w.r.t. Q, K, V,
+                               grouped K/V heads and N_q != N_kv included
                                (``bwd_dq_rows``: dQ of sampled rows only);
   * ``online_ref``          -- the tile-by-tile online-softmax recurrence in
                                numpy fp64, in the deferred-normalisation form and

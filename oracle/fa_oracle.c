@@ -300,27 +300,39 @@ int oracle_combine_f64(const double* o_parts, const double* lse_parts, int64_t S
  *   dQ_i  = scale * sum_j dS_ij k_j
  *   dK_j  = scale * sum_i dS_ij q_i
  * Written out per row with the row's probabilities recomputed by the same
- * three passes as the forward oracle. */
+ * three passes as the forward oracle.
+ *
+ * With grouped K/V heads (query head h reads K/V head h / (H / H_kv)) the
+ * same rules hold per query head, and K/V head g, being used by every query
+ * head of its group, receives the sum of their contributions:
+ *   dK_g = sum over h in group g of dK_h,   dV_g likewise.
+ * With N_q != N_kv the visible keys of query row i are those of the forward
+ * oracle (j <= i + N_kv - N_q when causal); a row with no visible key has no
+ * weights and contributes nothing, and its dQ row is 0. */
 
 typedef struct {
   const void *q, *k, *v, *dout;
   int dtype;
-  int64_t H, N, d;
+  int64_t H, Hkv, Nq, Nk, d;
   double scale;
   int causal;
-  double *dq, *dk, *dv;  /* [B*H, N, d] */
-  int64_t first, last;   /* this worker's heads */
+  double *dq, *dk, *dv;  /* dq: [B*H, Nq, d]; dk, dv: [B*Hkv, Nk, d] */
+  int64_t first, last;   /* this worker's K/V heads, b * Hkv + g */
 } bjob_t;
 
-/* Probabilities of row i of head `head` (element offset) into p[0..nvis). */
-static int64_t row_probs(const void* q, const void* k, int dtype, int64_t N, int64_t d,
-                         double scale, int causal, int64_t head, int64_t i, double* p) {
-  const int64_t nvis = causal ? i + 1 : N;
+/* Probabilities of query row i (q rows at element offset qhead) against the
+ * keys at element offset kvhead, into p[0..nvis); returns nvis (0 when the
+ * row sees no key). */
+static int64_t row_probs(const void* q, const void* k, int dtype, int64_t Nq, int64_t Nk,
+                         int64_t d, double scale, int causal, int64_t qhead, int64_t kvhead,
+                         int64_t i, double* p) {
+  const int64_t nvis = causal ? i + 1 + (Nk - Nq) : Nk;
+  if (nvis <= 0) return 0;
   double m = -INFINITY;
   for (int64_t j = 0; j < nvis; ++j) {
     double dot = 0.0;
     for (int64_t c = 0; c < d; ++c)
-      dot += load_elem(q, dtype, head + i * d + c) * load_elem(k, dtype, head + j * d + c);
+      dot += load_elem(q, dtype, qhead + i * d + c) * load_elem(k, dtype, kvhead + j * d + c);
     p[j] = scale * dot;
     if (p[j] > m) m = p[j];
   }
@@ -332,42 +344,54 @@ static int64_t row_probs(const void* q, const void* k, int dtype, int64_t N, int
 
 static void* bwd_worker(void* arg) {
   const bjob_t* J = (const bjob_t*)arg;
-  const int64_t N = J->N, d = J->d;
-  double* p = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
-  double* ds = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+  const int64_t Nq = J->Nq, Nk = J->Nk, d = J->d;
+  const int64_t grp = J->H / J->Hkv;
+  double* p = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+  double* ds = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
   double* o = (double*)malloc(sizeof(double) * (size_t)d);
   if (!p || !ds || !o) {
     free(p); free(ds); free(o);
     return (void*)1;
   }
-  for (int64_t bh = J->first; bh < J->last; ++bh) {
-    const int64_t head = bh * N * d;
-    double *dq = J->dq + head, *dk = J->dk + head, *dv = J->dv + head;
-    for (int64_t e = 0; e < N * d; ++e) dq[e] = dk[e] = dv[e] = 0.0;
-    for (int64_t i = 0; i < N; ++i) {
-      const int64_t nvis = row_probs(J->q, J->k, J->dtype, N, d, J->scale, J->causal, head, i, p);
-      /* O_i and D_i = dO_i . O_i */
-      for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
-      for (int64_t j = 0; j < nvis; ++j)
-        for (int64_t c = 0; c < d; ++c) o[c] += p[j] * load_elem(J->v, J->dtype, head + j * d + c);
-      double D = 0.0;
-      for (int64_t c = 0; c < d; ++c) D += load_elem(J->dout, J->dtype, head + i * d + c) * o[c];
-      /* dP_ij, dS_ij; dV_j += P_ij dO_i */
-      for (int64_t j = 0; j < nvis; ++j) {
-        double dp = 0.0;
-        for (int64_t c = 0; c < d; ++c) {
-          const double g = load_elem(J->dout, J->dtype, head + i * d + c);
-          dp += g * load_elem(J->v, J->dtype, head + j * d + c);
-          dv[j * d + c] += p[j] * g;
+  for (int64_t bg = J->first; bg < J->last; ++bg) {
+    const int64_t b = bg / J->Hkv, g = bg % J->Hkv;
+    const int64_t kvhead = bg * Nk * d;
+    double *dk = J->dk + kvhead, *dv = J->dv + kvhead;
+    for (int64_t e = 0; e < Nk * d; ++e) dk[e] = dv[e] = 0.0;
+    for (int64_t hh = 0; hh < grp; ++hh) {
+      const int64_t h = g * grp + hh;
+      const int64_t qhead = (b * J->H + h) * Nq * d;
+      double* dq = J->dq + qhead;
+      for (int64_t e = 0; e < Nq * d; ++e) dq[e] = 0.0;
+      for (int64_t i = 0; i < Nq; ++i) {
+        const int64_t nvis = row_probs(J->q, J->k, J->dtype, Nq, Nk, d, J->scale, J->causal,
+                                       qhead, kvhead, i, p);
+        if (nvis == 0) continue;
+        /* O_i and D_i = dO_i . O_i */
+        for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+        for (int64_t j = 0; j < nvis; ++j)
+          for (int64_t c = 0; c < d; ++c)
+            o[c] += p[j] * load_elem(J->v, J->dtype, kvhead + j * d + c);
+        double D = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+          D += load_elem(J->dout, J->dtype, qhead + i * d + c) * o[c];
+        /* dP_ij, dS_ij; dV_j += P_ij dO_i */
+        for (int64_t j = 0; j < nvis; ++j) {
+          double dp = 0.0;
+          for (int64_t c = 0; c < d; ++c) {
+            const double g = load_elem(J->dout, J->dtype, qhead + i * d + c);
+            dp += g * load_elem(J->v, J->dtype, kvhead + j * d + c);
+            dv[j * d + c] += p[j] * g;
+          }
+          ds[j] = p[j] * (dp - D);
         }
-        ds[j] = p[j] * (dp - D);
+        /* dQ_i = scale sum_j dS_ij k_j ; dK_j += scale dS_ij q_i */
+        for (int64_t j = 0; j < nvis; ++j)
+          for (int64_t c = 0; c < d; ++c) {
+            dq[i * d + c] += J->scale * ds[j] * load_elem(J->k, J->dtype, kvhead + j * d + c);
+            dk[j * d + c] += J->scale * ds[j] * load_elem(J->q, J->dtype, qhead + i * d + c);
+          }
       }
-      /* dQ_i = scale sum_j dS_ij k_j ; dK_j += scale dS_ij q_i */
-      for (int64_t j = 0; j < nvis; ++j)
-        for (int64_t c = 0; c < d; ++c) {
-          dq[i * d + c] += J->scale * ds[j] * load_elem(J->k, J->dtype, head + j * d + c);
-          dk[j * d + c] += J->scale * ds[j] * load_elem(J->q, J->dtype, head + i * d + c);
-        }
     }
   }
   free(p); free(ds); free(o);
@@ -375,17 +399,21 @@ static void* bwd_worker(void* arg) {
 }
 
 /*
- * oracle_bwd_f64 -- q, k, v, dout: contiguous [B, H, N, d] of `dtype`.
- * dq, dk, dv: [B, H, N, d] doubles, written in full.  Threads work on whole
- * heads.  Returns 0, -1 on a bad argument, -2 when out of memory.
+ * oracle_bwd_gqa_f64 -- q, dout: contiguous [B, H, Nq, d]; k, v: [B, Hkv,
+ * Nk, d], all of `dtype`; H a multiple of Hkv.  dq: [B, H, Nq, d] and dk,
+ * dv: [B, Hkv, Nk, d] doubles, written in full.  Threads work on whole K/V
+ * heads (and so on whole groups of query heads).  Returns 0, -1 on a bad
+ * argument, -2 when out of memory.
  */
-int oracle_bwd_f64(const void* q, const void* k, const void* v, const void* dout, int dtype,
-                   int64_t B, int64_t H, int64_t N, int64_t d, double scale, int causal,
-                   double* dq, double* dk, double* dv, int nthreads) {
+int oracle_bwd_gqa_f64(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                       int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                       double scale, int causal, double* dq, double* dk, double* dv,
+                       int nthreads) {
   if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return -1;
-  if (B < 0 || H < 0 || N < 0 || d <= 0) return -1;
-  const int64_t heads = B * H;
-  if (heads == 0 || N == 0) return 0;
+  if (B < 0 || H < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d <= 0) return -1;
+  if ((H == 0) != (Hkv == 0) || (Hkv > 0 && H % Hkv != 0)) return -1;
+  const int64_t heads = B * Hkv;
+  if (heads == 0 || (Nq == 0 && Nk == 0)) return 0;
   if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
   if (nthreads < 1) nthreads = 1;
   if (nthreads > heads) nthreads = (int)heads;
@@ -400,7 +428,8 @@ int oracle_bwd_f64(const void* q, const void* k, const void* v, const void* dout
   for (int t = 0; t < nthreads; ++t) {
     bjob_t* J = &jobs[t];
     J->q = q; J->k = k; J->v = v; J->dout = dout; J->dtype = dtype;
-    J->H = H; J->N = N; J->d = d; J->scale = scale; J->causal = causal;
+    J->H = H; J->Hkv = Hkv; J->Nq = Nq; J->Nk = Nk; J->d = d;
+    J->scale = scale; J->causal = causal;
     J->dq = dq; J->dk = dk; J->dv = dv;
     J->first = heads * t / nthreads;
     J->last = heads * (t + 1) / nthreads;
@@ -420,44 +449,67 @@ int oracle_bwd_f64(const void* q, const void* k, const void* v, const void* dout
   return rc;
 }
 
+/* oracle_bwd_f64 -- the square case: q, k, v, dout, dq, dk, dv all [B, H, N, d]. */
+int oracle_bwd_f64(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                   int64_t B, int64_t H, int64_t N, int64_t d, double scale, int causal,
+                   double* dq, double* dk, double* dv, int nthreads) {
+  return oracle_bwd_gqa_f64(q, k, v, dout, dtype, B, H, H, N, N, d, scale, causal, dq, dk, dv,
+                            nthreads);
+}
+
 /*
- * oracle_bwd_dq_rows_f64 -- dQ for a list of flat rows ((b*H + h)*N + i)
- * only: row i's gradient needs just row i's probabilities, so sampled rows
- * of a large problem cost O(N d) each.  dq: [nrows, d] doubles.
+ * oracle_bwd_dq_rows_gqa_f64 -- dQ for a list of flat query rows
+ * ((b*H + h)*Nq + i) only: row i's gradient needs just row i's
+ * probabilities, so sampled rows of a large problem cost O(Nk d) each.
+ * Shapes as oracle_bwd_gqa_f64.  dq: [nrows, d] doubles.
  */
-int oracle_bwd_dq_rows_f64(const void* q, const void* k, const void* v, const void* dout,
-                           int dtype, int64_t B, int64_t H, int64_t N, int64_t d, double scale,
-                           int causal, const int64_t* rows, int64_t nrows, double* dq) {
+int oracle_bwd_dq_rows_gqa_f64(const void* q, const void* k, const void* v, const void* dout,
+                               int dtype, int64_t B, int64_t H, int64_t Hkv, int64_t Nq,
+                               int64_t Nk, int64_t d, double scale, int causal,
+                               const int64_t* rows, int64_t nrows, double* dq) {
   if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return -1;
-  if (B < 0 || H < 0 || N < 0 || d <= 0 || nrows < 0) return -1;
+  if (B < 0 || H < 0 || Hkv <= 0 || Nq < 0 || Nk < 0 || d <= 0 || nrows < 0) return -1;
+  if (H % Hkv != 0) return -1;
   if (nrows == 0) return 0;
   if (!q || !k || !v || !dout || !rows || !dq) return -1;
   for (int64_t r = 0; r < nrows; ++r)
-    if (rows[r] < 0 || rows[r] >= B * H * N) return -1;
-  double* p = (double*)malloc(sizeof(double) * (size_t)N);
+    if (rows[r] < 0 || rows[r] >= B * H * Nq) return -1;
+  double* p = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
   double* o = (double*)malloc(sizeof(double) * (size_t)d);
   if (!p || !o) {
     free(p); free(o);
     return -2;
   }
   for (int64_t r = 0; r < nrows; ++r) {
-    const int64_t bh = rows[r] / N, i = rows[r] % N, head = bh * N * d;
-    const int64_t nvis = row_probs(q, k, dtype, N, d, scale, causal, head, i, p);
-    for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
-    for (int64_t j = 0; j < nvis; ++j)
-      for (int64_t c = 0; c < d; ++c) o[c] += p[j] * load_elem(v, dtype, head + j * d + c);
-    double D = 0.0;
-    for (int64_t c = 0; c < d; ++c) D += load_elem(dout, dtype, head + i * d + c) * o[c];
+    const int64_t bh = rows[r] / Nq, i = rows[r] % Nq;
+    const int64_t b = bh / H, h = bh % H;
+    const int64_t qhead = bh * Nq * d, kvhead = (b * Hkv + h / (H / Hkv)) * Nk * d;
     double* out = dq + r * d;
     for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+    const int64_t nvis = row_probs(q, k, dtype, Nq, Nk, d, scale, causal, qhead, kvhead, i, p);
+    if (nvis == 0) continue;
+    for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+    for (int64_t j = 0; j < nvis; ++j)
+      for (int64_t c = 0; c < d; ++c) o[c] += p[j] * load_elem(v, dtype, kvhead + j * d + c);
+    double D = 0.0;
+    for (int64_t c = 0; c < d; ++c) D += load_elem(dout, dtype, qhead + i * d + c) * o[c];
     for (int64_t j = 0; j < nvis; ++j) {
       double dp = 0.0;
       for (int64_t c = 0; c < d; ++c)
-        dp += load_elem(dout, dtype, head + i * d + c) * load_elem(v, dtype, head + j * d + c);
+        dp += load_elem(dout, dtype, qhead + i * d + c) * load_elem(v, dtype, kvhead + j * d + c);
       const double ds = p[j] * (dp - D);
-      for (int64_t c = 0; c < d; ++c) out[c] += scale * ds * load_elem(k, dtype, head + j * d + c);
+      for (int64_t c = 0; c < d; ++c)
+        out[c] += scale * ds * load_elem(k, dtype, kvhead + j * d + c);
     }
   }
   free(p); free(o);
   return 0;
+}
+
+/* oracle_bwd_dq_rows_f64 -- the square case of oracle_bwd_dq_rows_gqa_f64. */
+int oracle_bwd_dq_rows_f64(const void* q, const void* k, const void* v, const void* dout,
+                           int dtype, int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                           int causal, const int64_t* rows, int64_t nrows, double* dq) {
+  return oracle_bwd_dq_rows_gqa_f64(q, k, v, dout, dtype, B, H, H, N, N, d, scale, causal, rows,
+                                    nrows, dq);
 }

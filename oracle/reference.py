@@ -73,6 +73,18 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
             ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.oracle_bwd_gqa_f64.restype = ctypes.c_int
+        lib.oracle_bwd_gqa_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_bwd_dq_rows_gqa_f64.restype = ctypes.c_int
+        lib.oracle_bwd_dq_rows_gqa_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p]
         lib.oracle_widen.restype = ctypes.c_double
         lib.oracle_widen.argtypes = [ctypes.c_int, ctypes.c_uint32]
         _lib = lib
@@ -217,42 +229,52 @@ def _four(q, k, v, dout):
     gb, dtg = _stored_bits(dout)
     if not (dt == dtk == dtv == dtg):
         raise TypeError("q, k, v, dout must share one dtype")
-    if not (qb.shape == kb.shape == vb.shape == gb.shape) or qb.ndim != 4:
-        raise ValueError("q, k, v, dout must all be [B, H, N, d] of one shape")
+    if qb.ndim != 4 or kb.ndim != 4 or qb.shape != gb.shape or kb.shape != vb.shape:
+        raise ValueError("q, dout must be [B, H, N_q, d] and k, v [B, H_kv, N_kv, d]")
+    B, H, _, d = (int(s) for s in qb.shape)
+    Bk, Hkv, _, dk = (int(s) for s in kb.shape)
+    if Bk != B or dk != d or (Hkv == 0) != (H == 0) or (Hkv and H % Hkv):
+        raise ValueError("q, k, v must share B and d, and H_kv must divide H")
     return qb, kb, vb, gb, dt
 
 
 def bwd(q, k, v, dout, scale: float, causal: bool, threads: int | None = None):
-    """Gradients of sum(dout * O) w.r.t. q, k, v in fp64 (square heads).
+    """Gradients of sum(dout * O) w.r.t. q, k, v in fp64.
 
-    Returns ``(dq, dk, dv)`` as float64 numpy arrays of shape [B, H, N, d].
+    q, dout: [B, H, N_q, d]; k, v: [B, H_kv, N_kv, d] with H_kv dividing H
+    (query head h reads K/V head h // (H // H_kv)); the causal mask is the
+    forward oracle's (key j visible to row i when j <= i + N_kv - N_q).
+    Returns ``(dq, dk, dv)`` as float64 numpy arrays shaped like q, k, v.
     """
     qb, kb, vb, gb, dt = _four(q, k, v, dout)
-    B, H, N, d = (int(s) for s in qb.shape)
-    dq = np.zeros((B, H, N, d), dtype=np.float64)
-    dk = np.zeros_like(dq)
-    dv = np.zeros_like(dq)
-    rc = _load().oracle_bwd_f64(qb.ctypes.data, kb.ctypes.data, vb.ctypes.data, gb.ctypes.data,
-                                DTYPE_CODES[dt], B, H, N, d, float(np.float32(scale)),
-                                int(bool(causal)), dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
-                                int(threads or default_threads()))
+    B, H, Nq, d = (int(s) for s in qb.shape)
+    Hkv, Nk = int(kb.shape[1]), int(kb.shape[2])
+    dq = np.zeros((B, H, Nq, d), dtype=np.float64)
+    dk = np.zeros((B, Hkv, Nk, d), dtype=np.float64)
+    dv = np.zeros_like(dk)
+    rc = _load().oracle_bwd_gqa_f64(qb.ctypes.data, kb.ctypes.data, vb.ctypes.data,
+                                    gb.ctypes.data, DTYPE_CODES[dt], B, H, Hkv, Nq, Nk, d,
+                                    float(np.float32(scale)), int(bool(causal)), dq.ctypes.data,
+                                    dk.ctypes.data, dv.ctypes.data,
+                                    int(threads or default_threads()))
     if rc != 0:
-        raise RuntimeError(f"oracle_bwd_f64 failed with code {rc}")
+        raise RuntimeError(f"oracle_bwd_gqa_f64 failed with code {rc}")
     return dq, dk, dv
 
 
 def bwd_dq_rows(q, k, v, dout, scale: float, causal: bool, rows):
-    """dQ for the flat rows ``(b*H + h)*N + i`` only: [len(rows), d] float64."""
+    """dQ for the flat query rows ``(b*H + h)*N_q + i`` only: [len(rows), d] float64."""
     qb, kb, vb, gb, dt = _four(q, k, v, dout)
-    B, H, N, d = (int(s) for s in qb.shape)
+    B, H, Nq, d = (int(s) for s in qb.shape)
+    Hkv, Nk = int(kb.shape[1]), int(kb.shape[2])
     rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
     dq = np.zeros((rows_arr.size, d), dtype=np.float64)
-    rc = _load().oracle_bwd_dq_rows_f64(qb.ctypes.data, kb.ctypes.data, vb.ctypes.data,
-                                        gb.ctypes.data, DTYPE_CODES[dt], B, H, N, d,
-                                        float(np.float32(scale)), int(bool(causal)),
-                                        rows_arr.ctypes.data, rows_arr.size, dq.ctypes.data)
+    rc = _load().oracle_bwd_dq_rows_gqa_f64(qb.ctypes.data, kb.ctypes.data, vb.ctypes.data,
+                                            gb.ctypes.data, DTYPE_CODES[dt], B, H, Hkv, Nq, Nk,
+                                            d, float(np.float32(scale)), int(bool(causal)),
+                                            rows_arr.ctypes.data, rows_arr.size, dq.ctypes.data)
     if rc != 0:
-        raise RuntimeError(f"oracle_bwd_dq_rows_f64 failed with code {rc}")
+        raise RuntimeError(f"oracle_bwd_dq_rows_gqa_f64 failed with code {rc}")
     return dq
 
 

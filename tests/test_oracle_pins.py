@@ -486,3 +486,99 @@ def test_dq_rows_equal_full_gradient(oracle_lib):
         rows = np.array([0, 7, 29, 30, 59, 100, B * H * N - 1])
         got = oracle.bwd_dq_rows(q, k, v, g, 0.3, causal, rows)
         np.testing.assert_allclose(got, dq.reshape(-1, d)[rows], rtol=1e-14, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# Gradients with grouped K/V heads and N_q != N_kv
+# --------------------------------------------------------------------------
+
+def _autograd_gqa(q, k, v, g, scale, causal):
+    # Independent fp64 reference: K/V heads repeated to the query heads
+    # (repeat_interleave's backward sums each group), the end-aligned causal
+    # mask written out, and rows without a visible key zeroed explicitly.
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    q64, k64, v64 = (t.to(torch.float64).requires_grad_(True) for t in (q, k, v))
+    kk = k64.repeat_interleave(H // Hkv, dim=1)
+    vv = v64.repeat_interleave(H // Hkv, dim=1)
+    logits = float(np.float32(scale)) * torch.matmul(q64, kk.transpose(-1, -2))
+    i = torch.arange(Nq).view(-1, 1)
+    j = torch.arange(Nk).view(1, -1)
+    masked = (j > i + (Nk - Nq)) if causal else torch.zeros(Nq, Nk, dtype=torch.bool)
+    empty = masked.all(dim=1, keepdim=True)
+    logits = logits.masked_fill(masked | empty, float("-inf")).masked_fill(empty, 0.0)
+    w = torch.softmax(logits, -1) * (~empty).to(torch.float64)
+    o = torch.matmul(w, vv)
+    o.backward(g.to(torch.float64))
+    return q64.grad.numpy(), k64.grad.numpy(), v64.grad.numpy()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,Hkv,Nq,Nk", [(4, 2, 9, 9), (6, 2, 5, 13), (4, 1, 13, 5),
+                                         (4, 4, 7, 11), (2, 1, 1, 17)])
+def test_grouped_gradients_match_torch_autograd_fp64(oracle_lib, dtype, causal, H, Hkv, Nq, Nk):
+    B, d = 2, 8
+    q = _rand((B, H, Nq, d), dtype, seed=161)
+    k = _rand((B, Hkv, Nk, d), dtype, seed=162)
+    v = _rand((B, Hkv, Nk, d), dtype, seed=163)
+    g = _rand((B, H, Nq, d), dtype, seed=164)
+    dq, dk, dv = oracle.bwd(q, k, v, g, 0.35, causal)
+    assert dq.shape == (B, H, Nq, d) and dk.shape == dv.shape == (B, Hkv, Nk, d)
+    rq, rk, rv = _autograd_gqa(q, k, v, g, 0.35, causal)
+    for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+    if causal and Nq > Nk:  # the first Nq - Nk rows see no key
+        assert np.all(dq[:, :, : Nq - Nk] == 0.0)
+
+
+def test_grouped_gradients_match_finite_differences(oracle_lib):
+    # Central differences (exact step 2^-12) of the pinned grouped forward
+    # oracle, causal with N_q < N_kv and two query heads on one K/V head.
+    B, H, Hkv, Nq, Nk, d = 1, 2, 1, 3, 5, 4
+    q, g = (_eighths((B, H, Nq, d), s) for s in (171, 174))
+    k, v = (_eighths((B, Hkv, Nk, d), s) for s in (172, 173))
+    scale = 0.5
+    dq, dk, dv = oracle.bwd(q, k, v, g, scale, True)
+    h = 2.0 ** -12
+    gg = _f64(g)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.fwd_gqa(q_, k_, v_, scale, True)
+        return float((o * gg).sum())
+
+    worst = 0.0
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        base = (q, k, v)[which]
+        for idx in np.ndindex(*base.shape):
+            args_p = [q.clone(), k.clone(), v.clone()]
+            args_m = [q.clone(), k.clone(), v.clone()]
+            args_p[which][idx] += h
+            args_m[which][idx] -= h
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            worst = max(worst, abs(fd - grad[idx]))
+    assert worst <= 1e-6, worst
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_gradient_invariants(oracle_lib, causal):
+    # Per K/V head: key gradients sum to zero; value gradients sum to the sum
+    # of the dO rows of every query head in the group (every row sees a key).
+    B, H, Hkv, Nq, Nk, d = 2, 6, 2, 11, 20, 8
+    q, g = _rand((B, H, Nq, d), seed=181), _rand((B, H, Nq, d), seed=184)
+    k, v = _rand((B, Hkv, Nk, d), seed=182), _rand((B, Hkv, Nk, d), seed=183)
+    dq, dk, dv = oracle.bwd(q, k, v, g, 0.4, causal)
+    assert np.max(np.abs(dk.sum(axis=2))) <= 1e-12 * max(1.0, np.abs(dk).max())
+    gsum = _f64(g).sum(axis=2).reshape(B, Hkv, H // Hkv, d).sum(axis=2)
+    np.testing.assert_allclose(dv.sum(axis=2), gsum, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_dq_rows_equal_full_gradient(oracle_lib):
+    B, H, Hkv, Nq, Nk, d = 2, 4, 2, 9, 14, 8
+    q, g = _rand((B, H, Nq, d), seed=191), _rand((B, H, Nq, d), seed=194)
+    k, v = _rand((B, Hkv, Nk, d), seed=192), _rand((B, Hkv, Nk, d), seed=193)
+    for causal in (False, True):
+        dq, _, _ = oracle.bwd(q, k, v, g, 0.3, causal)
+        rows = np.array([0, 5, 8, 9, 20, 35, 40, B * H * Nq - 1])
+        got = oracle.bwd_dq_rows(q, k, v, g, 0.3, causal, rows)
+        np.testing.assert_allclose(got, dq.reshape(-1, d)[rows], rtol=1e-14, atol=1e-15)
