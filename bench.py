@@ -126,7 +126,8 @@ def cpu_baseline_bwd(w, q, k, v, dout, target_s: float):
     total = w.B * w.H * w.N
 
     def rows_flops(rows):
-        vis = (rows % w.N + 1) if w.causal else np.full(rows.shape, w.N)
+        nk = w.n_kv
+        vis = np.clip(rows % w.N + 1 + (nk - w.N), 0, nk) if w.causal else np.full(rows.shape, nk)
         return float(vis.sum()) * 8.0 * w.d
 
     calib = np.sort(rng.choice(total, size=min(16, total), replace=False)).astype(np.int64)
@@ -216,21 +217,28 @@ def main():
 
     splits, workspace = 1, None
     if args.which == "bwd":
-        if w.extended or w.dtype == "f32":
-            sys.exit("the backward pass runs on square bf16/fp16 workloads (C3, C4, C5)")
+        if w.dtype == "f32":
+            sys.exit("the backward pass runs on bf16/fp16 workloads (C3, C4, C5, G1, G2)")
         g = np.random.default_rng(w.seed + 100)
         dout = torch.from_numpy(g.standard_normal((w.B, w.H, w.N, w.d)).astype(np.float32)).to(
             qd.dtype).to(dev)
-        binding.fwd(qd, kd, vd, w.scale, w.causal, out=o, lse=lse, stream=stream)
-        grads = [torch.empty_like(qd) for _ in range(3)]
+        if w.extended:
+            binding.fwd_ex(qd, kd, vd, w.scale, w.causal, out=o, lse=lse, stream=stream)
+        else:
+            binding.fwd(qd, kd, vd, w.scale, w.causal, out=o, lse=lse, stream=stream)
+        grads = [torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)]
         delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
         dt_code = binding.FA_BF16 if w.dtype == "bf16" else binding.FA_F16
+        ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                lse.data_ptr(), *(t.data_ptr() for t in grads), delta.data_ptr())
 
         def step():
-            st = binding.fa_bwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
-                                dout.data_ptr(), lse.data_ptr(), *(t.data_ptr() for t in grads),
-                                delta.data_ptr(), w.B, w.H, w.N, w.d, w.scale, w.causal, dt_code,
-                                stream.cuda_stream)
+            if w.extended:
+                st = binding.fa_bwd_ex(*ptrs, w.B, w.H, w.h_kv, w.N, w.n_kv, w.d, w.scale,
+                                       w.causal, dt_code, stream.cuda_stream)
+            else:
+                st = binding.fa_bwd(*ptrs, w.B, w.H, w.N, w.d, w.scale, w.causal, dt_code,
+                                    stream.cuda_stream)
             if st != 0:
                 raise binding.FaError(st)
     elif w.extended:
@@ -303,7 +311,8 @@ def main():
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "algorithmic_bytes": w.io_bytes,
-                     "timed": ("fa_bwd call: row-dot, dK/dV and dQ kernels" if args.which == "bwd"
+                     "timed": (("fa_bwd_ex" if w.extended else "fa_bwd") +
+                               " call: row-dot, dK/dV and dQ kernels" if args.which == "bwd"
                                else "fa_fwd_ex call: split kernel + combine kernel" if splits > 1
                                else "one forward kernel"),
                      "kernel_ms_avg": round(avg_kernel_ms, 5),

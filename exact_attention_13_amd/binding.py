@@ -23,8 +23,8 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD
 _DTYPE_CODES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
 
 # Every symbol include/fa.h declares.
-EXPORTED = ("fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_ex_default_splits", "fa_fwd_ex_workspace_bytes",
-            "fa_lse_combine", "fa_strerror", "fa_version")
+EXPORTED = ("fa_bwd", "fa_bwd_ex", "fa_fwd", "fa_fwd_ex", "fa_fwd_ex_default_splits",
+            "fa_fwd_ex_workspace_bytes", "fa_lse_combine", "fa_strerror", "fa_version")
 
 _lib = None
 
@@ -63,6 +63,9 @@ def load() -> ctypes.CDLL:
             ctypes.c_void_p] * 2 + [ctypes.c_int, ctypes.c_void_p]
         lib.fa_bwd.restype = ctypes.c_int
         lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        lib.fa_bwd_ex.restype = ctypes.c_int
+        lib.fa_bwd_ex.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_strerror.argtypes = [ctypes.c_int]
@@ -244,35 +247,52 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, 
                              int(d), float(scale), int(bool(causal)), int(dtype), stream))
 
 
+def fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, N_q, N_kv, d, scale, causal,
+              dtype, stream) -> int:
+    """Raw C call with integer pointers; returns the fa_status code."""
+    return int(load().fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, int(B), int(H),
+                                int(H_kv), int(N_q), int(N_kv), int(d), float(scale),
+                                int(bool(causal)), int(dtype), stream))
+
+
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         lse: torch.Tensor, dout: torch.Tensor, scale: float | None = None,
         causal: bool = False, stream: torch.cuda.Stream | None = None):
-    """Gradients (dq, dk, dv) of the forward pass for [B, H, N, d] bf16/fp16 tensors.
+    """Gradients (dq, dk, dv) of the forward pass for bf16/fp16 tensors.
 
-    ``o`` and ``lse`` are what ``fwd`` returned for the same inputs.  Returns
-    ``(dq, dk, dv)`` of q's dtype; the row dot products D = rowsum(dO * O)
-    go to a scratch tensor allocated here.
+    q, o, dout: [B, H, N_q, d]; k, v: [B, H_kv, N_kv, d] with H_kv dividing H
+    (``fa_bwd`` when the shapes are all equal, else ``fa_bwd_ex``).  ``o`` and
+    ``lse`` are what ``fwd`` / ``fwd_ex`` returned for the same inputs.
+    Returns ``(dq, dk, dv)`` shaped like q, k, v; the row dot products
+    D = rowsum(dO * O) go to a scratch tensor allocated here.
     """
-    if q.dim() != 4 or not (q.shape == k.shape == v.shape == o.shape == dout.shape):
-        raise ValueError("q, k, v, o, dout must be [B, H, N, d] tensors of one shape")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or not (q.shape == o.shape == dout.shape):
+        raise ValueError("q, o, dout must be [B, H, N_q, d] and k, v [B, H_kv, N_kv, d]")
     if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype) or \
             q.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError("the backward pass takes bfloat16 or float16 tensors of one dtype")
     tensors = (q, k, v, o, dout, lse)
     if not all(t.is_cuda and t.is_contiguous() for t in tensors):
         raise ValueError("inputs must be contiguous GPU tensors")
-    B, H, N, d = q.shape
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
-        raise ValueError("lse must be a float32 [B, H, N] tensor")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("q and k must share B and d")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [B, H, N_q] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                B, H, N, d, scale, causal, _DTYPE_CODES[q.dtype], stream.cuda_stream)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr())
+    if k.shape == q.shape:
+        st = fa_bwd(*ptrs, B, H, Nq, d, scale, causal, _DTYPE_CODES[q.dtype], stream.cuda_stream)
+    else:
+        st = fa_bwd_ex(*ptrs, B, H, Hkv, Nq, Nk, d, scale, causal, _DTYPE_CODES[q.dtype],
+                       stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st)
     return dq, dk, dv

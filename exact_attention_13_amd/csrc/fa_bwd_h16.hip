@@ -125,7 +125,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (head, 128 keys)
+// dK, dV: one workgroup per (K/V head, 128 keys).  With grouped heads the
+// workgroup walks the query tiles of every query head of its group in turn
+// and sums their contributions in its registers (no atomics: deterministic).
 // ---------------------------------------------------------------------------
 template <bool BF16, bool CAUSAL, int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<D>))) void bwd_dkdv_kernel(BwdArgs a, int n_kt, int total) {
@@ -138,22 +140,19 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, grp = lane >> 5;
-  const int N = a.n;
+  const int nq = a.nq, nk = a.nk, off = a.off;
 
   const int L = xcd_remap(blockIdx.x, total);
-  const int bh = L / n_kt;
-  const int kt = L - bh * n_kt;  // causal: low key tiles see the most queries and go first
+  const int bkv = L / n_kt;
+  const int kt = L - bkv * n_kt;  // causal: low key tiles see the most queries and go first
   const int k0 = kt * kBwdRows;
   const int kw0 = k0 + wave * 32;  // this wave's first key
+  const int b = bkv / a.hkv;
+  const int bh0 = b * a.hq + (bkv - b * a.hkv) * a.hgrp;  // first query head of the group
 
-  const int64_t head = (int64_t)bh * N * D;
-  const int hb = N * D * 2;
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint16_t*)a.q + head, hb);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + head, hb);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.v + head, hb);
-  const __amdgpu_buffer_rsrc_t gr = make_rsrc((const uint16_t*)a.dout + head, hb);
-  const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.lse + (int64_t)bh * N, N * 4);
-  const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.delta + (int64_t)bh * N, N * 4);
+  const int64_t kvhead = (int64_t)bkv * nk * D;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + kvhead, nk * D * 2);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.v + kvhead, nk * D * 2);
 
   // K and V rows of this wave's keys as B operands: lane (col, grp) holds
   // row kw0 + col, columns 16 kc + 8 grp .. + 8 (zero past the end).
@@ -164,8 +163,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     vf[kc] = buf_load16(vr, ((kw0 + col) * D + kc * 16 + grp * 8) * 2);
   }
 
-  const int n_qt = (N + kBT - 1) / kBT;
-  const int qt_begin = CAUSAL ? k0 / kBT : 0;  // earlier queries see none of these keys
+  // Query tiles qt_begin .. n_qt - 1 of each of the hgrp query heads, walked
+  // as one sequence (head by head, tiles upward).  Causal: a query row i sees
+  // key k0 only if i + off >= k0, so earlier tiles see none of these keys.
+  const int n_qt = (nq + kBT - 1) / kBT;
+  const int qt_begin = CAUSAL ? max(0, (k0 - off) / kBT) : 0;
+  const int n_iter = max(0, n_qt - qt_begin);
+  const int total_it = n_iter * a.hgrp;
 
   // Staging of one query tile: (row pair, 8 columns) units of Q then dO,
   // plus the tile's 32 lse and 32 D values.  Part i of the units goes through
@@ -182,7 +186,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
   // Units are dealt by whole waves (kPairUnits is a multiple of 64), so the
   // Q-or-dO choice is wave-uniform and the buffer resource stays scalar.
   static_assert(T::kPairUnits % 64 == 0 && kUnits % kBwdThreads == 0, "unit split");
-  auto load_part = [&](int q0, int i0, int i1) {
+  auto load_part = [&](int hh, int q0, int i0, int i1) {
+    const int64_t bhq = bh0 + hh;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint16_t*)a.q + bhq * nq * D, nq * D * 2);
+    const __amdgpu_buffer_rsrc_t gr =
+        make_rsrc((const uint16_t*)a.dout + bhq * nq * D, nq * D * 2);
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
       const int u = tid + i * kBwdThreads;
@@ -195,6 +203,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
         load_pair<D>(gr, q0, p, cc, sx[sl], sy[sl]);
     }
     if (i0 == 0) {
+      const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.lse + bhq * nq, nq * 4);
+      const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.delta + bhq * nq, nq * 4);
       if (tid < kBT)
         st = __builtin_bit_cast(float,
                                 __builtin_amdgcn_raw_buffer_load_b32(lr, (q0 + tid) * 4, 0, 0));
@@ -225,23 +235,27 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dkT[db] = dvT[db] = (f32x16){};
 
-  load_part(qt_begin * kBT, 0, kFirst);
+  load_part(0, qt_begin * kBT, 0, kFirst);
   store_part(0, 0, kFirst);
   if (kHalves) {
-    load_part(qt_begin * kBT, 1, 2);
+    load_part(0, qt_begin * kBT, 1, 2);
     store_part(0, 1, 2);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int qt = qt_begin; qt < n_qt; ++qt) {
-    const int it = qt - qt_begin, buf = it & 1;
+  int hh = 0, qt = qt_begin;  // query head (within the group) and tile of step `it`
+  for (int it = 0; it < total_it; ++it) {
+    const int buf = it & 1;
     const int q0 = qt * kBT;
-    const bool more = qt + 1 < n_qt;
-    if (more) load_part(q0 + kBT, 0, kFirst);
+    const bool more = it + 1 < total_it;
+    const bool wrap = qt + 1 == n_qt;
+    const int hh_next = wrap ? hh + 1 : hh;
+    const int q0_next = (wrap ? qt_begin : qt + 1) * kBT;
+    if (more) load_part(hh_next, q0_next, 0, kFirst);
 
-    // causal: a tile whose last query comes before this wave's first key is empty
-    const bool active = !(CAUSAL && q0 + kBT - 1 < kw0);
+    // causal: a tile whose last query sees none of this wave's keys is empty
+    const bool active = !(CAUSAL && q0 + kBT - 1 + off < kw0);
     const uint16_t* qrm = lds + buf * kStage;
     const uint16_t* qtm = qrm + T::kRowElems;
     const uint16_t* grm = qtm + T::kTElems;
@@ -264,7 +278,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     }
 
     const int key = kw0 + col;
-    const bool edge = q0 + kBT > N || kw0 + 32 > N || (CAUSAL && q0 < kw0 + 31);
+    const bool edge = q0 + kBT > nq || kw0 + 32 > nk || (CAUSAL && q0 + off < kw0 + 31);
     // One 16-query chunk at a time (registers 8 ch .. 8 ch + 7): P, dS,
     // their packed pairs, then dV^T += dO^T P and dK^T += Q^T dS for the
     // chunk, so only one chunk's weights are live.
@@ -288,7 +302,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
           float p = fast_exp2(fmaf(s[r], c, -l4[e]));
           if (M == 1 || (M == 2 && edge)) {
             const int q = q0 + 8 * j + 4 * grp + e;
-            const bool ok = q < N && key < N && (!CAUSAL || key <= q);
+            const bool ok = q < nq && key < nk && (!CAUSAL || key <= q + off);
             p = ok ? p : 0.f;
           }
           pv[e] = p;
@@ -323,18 +337,20 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     if (active) chunk(0);
     if (kHalves && more) {
       store_part(buf ^ 1, 0, 1);
-      load_part(q0 + kBT, 1, 2);
+      load_part(hh_next, q0_next, 1, 2);
     }
     if (active) chunk(1);
     if (more) store_part(buf ^ 1, kHalves ? 1 : 0, kPer);
     __syncthreads();
+    hh = hh_next;
+    qt = wrap ? qt_begin : qt + 1;
   }
 
   // dK = scale * (Q^T dS)^T, dV = (dO^T P)^T; lane holds key kw0 + col.
   const int key = kw0 + col;
-  if (key < N) {
-    uint16_t* dkg = (uint16_t*)a.dk + head + (int64_t)key * D;
-    uint16_t* dvg = (uint16_t*)a.dv + head + (int64_t)key * D;
+  if (key < nk) {
+    uint16_t* dkg = (uint16_t*)a.dk + kvhead + (int64_t)key * D;
+    uint16_t* dvg = (uint16_t*)a.dv + kvhead + (int64_t)key * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -351,7 +367,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup per (head, 128 queries)
+// dQ: one workgroup per (query head, 128 queries)
 // ---------------------------------------------------------------------------
 template <bool BF16, bool CAUSAL, int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDqWaves<D>))) void bwd_dq_kernel(BwdArgs a, int n_qt, int total) {
@@ -363,7 +379,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, grp = lane >> 5;
-  const int N = a.n;
+  const int nq = a.nq, nk = a.nk, off = a.off;
 
   const int L = xcd_remap(blockIdx.x, total);
   const int bh = L / n_qt;
@@ -372,15 +388,16 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
   const int q0 = qt * kBwdRows;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + col;
+  const int b = bh / a.hq;
+  const int bkv = b * a.hkv + (bh - b * a.hq) / a.hgrp;  // this query head's K/V head
 
-  const int64_t head = (int64_t)bh * N * D;
-  const int hb = N * D * 2;
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint16_t*)a.q + head, hb);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + head, hb);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.v + head, hb);
-  const __amdgpu_buffer_rsrc_t gr = make_rsrc((const uint16_t*)a.dout + head, hb);
-  const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.lse + (int64_t)bh * N, N * 4);
-  const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.delta + (int64_t)bh * N, N * 4);
+  const int64_t qhead = (int64_t)bh * nq * D, kvhead = (int64_t)bkv * nk * D;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint16_t*)a.q + qhead, nq * D * 2);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + kvhead, nk * D * 2);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.v + kvhead, nk * D * 2);
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc((const uint16_t*)a.dout + qhead, nq * D * 2);
+  const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.lse + (int64_t)bh * nq, nq * 4);
+  const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.delta + (int64_t)bh * nq, nq * 4);
 
   // Q and dO rows of this lane's query as B operands.
   u32x4 qf[D / 16], gf[D / 16];
@@ -394,9 +411,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
   const float drow =
       __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dr, my_q * 4, 0, 0));
 
-  const int kv_end = CAUSAL ? min(q0 + kBwdRows, N) : N;
+  // causal: row i sees keys j <= i + off
+  const int kv_end = CAUSAL ? max(0, min(q0 + kBwdRows + off, nk)) : nk;
   const int n_kv = (kv_end + kBT - 1) / kBT;
-  const int wave_kv_end = CAUSAL ? min(qw0 + 32, N) : N;
+  const int wave_kv_end = CAUSAL ? max(0, min(qw0 + 32 + off, nk)) : nk;
 
   // Staging of one key tile: (row pair, 8 columns) units of K then V.
   constexpr int kUnits = 2 * T::kPairUnits;
@@ -476,7 +494,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
           float p = fast_exp2(fmaf(s[r], c, -lse2));
           if constexpr (decltype(masked)::value) {
             const int key = k0 + 8 * (r >> 2) + 4 * grp + (r & 3);
-            const bool ok = key < N && (!CAUSAL || key <= my_q);
+            const bool ok = key < nk && (!CAUSAL || key <= my_q + off);
             p = ok ? p : 0.f;
           }
           dsv[r] = p * (dp[r] - drow);
@@ -484,7 +502,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
 #pragma unroll
         for (int i = 0; i < 8; ++i) pd[i] = HH::pack(dsv[2 * i], dsv[2 * i + 1]);
       };
-      if (k0 + kBT > N || (CAUSAL && k0 + kBT - 1 > qw0))
+      if (k0 + kBT > nk || (CAUSAL && k0 + kBT - 1 > qw0 + off))
         weights(std::true_type{});
       else
         weights(std::false_type{});
@@ -504,8 +522,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
     __syncthreads();
   }
 
-  if (my_q < N) {
-    uint16_t* g = (uint16_t*)a.dq + head + (int64_t)my_q * D;
+  if (my_q < nq) {
+    uint16_t* g = (uint16_t*)a.dq + qhead + (int64_t)my_q * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -520,26 +538,40 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
 
 template <bool BF16, bool CAUSAL, int D>
 hipError_t launch_bwd(const BwdArgs& a, const void* o, float* delta, hipStream_t s) {
-  // D_i = dO_i . O_i for every row
-  const int64_t rows = (int64_t)a.bh * a.n;
-  constexpr int kRowsPerBlock = 256 / (D / 8);
-  const uint16_t* op = (const uint16_t*)o;
-  const uint16_t* gp = (const uint16_t*)a.dout;
-  int64_t rows_arg = rows;
-  void* p0[] = {&op, &gp, &delta, &rows_arg};
-  hipError_t e = hipLaunchKernel((const void*)&bwd_delta_kernel<BF16, D>,
-                                 dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
-                                 dim3(256), p0, 0, s);
-  if (e != hipSuccess) return e;
   BwdArgs args = a;
-  int n_t = (a.n + kBwdRows - 1) / kBwdRows;
-  int total = (int)((int64_t)n_t * a.bh);
-  void* p1[] = {&args, &n_t, &total};
-  e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<BF16, CAUSAL, D>, dim3(total),
-                      dim3(kBwdThreads), p1, 0, s);
-  if (e != hipSuccess) return e;
-  return hipLaunchKernel((const void*)&bwd_dq_kernel<BF16, CAUSAL, D>, dim3(total),
-                         dim3(kBwdThreads), p1, 0, s);
+  hipError_t e;
+  // D_i = dO_i . O_i for every query row
+  const int64_t rows = (int64_t)a.bh * a.nq;
+  if (rows > 0) {
+    constexpr int kRowsPerBlock = 256 / (D / 8);
+    const uint16_t* op = (const uint16_t*)o;
+    const uint16_t* gp = (const uint16_t*)a.dout;
+    int64_t rows_arg = rows;
+    void* p0[] = {&op, &gp, &delta, &rows_arg};
+    e = hipLaunchKernel((const void*)&bwd_delta_kernel<BF16, D>,
+                        dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(256),
+                        p0, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  // dK, dV over the K/V heads' key tiles (zero when there are no queries)
+  int n_kt = (a.nk + kBwdRows - 1) / kBwdRows;
+  int total_kv = (int)((int64_t)n_kt * a.bkv);
+  if (total_kv > 0) {
+    void* p1[] = {&args, &n_kt, &total_kv};
+    e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<BF16, CAUSAL, D>, dim3(total_kv),
+                        dim3(kBwdThreads), p1, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  // dQ over the query heads' row tiles (zero when there are no keys)
+  int n_qt = (a.nq + kBwdRows - 1) / kBwdRows;
+  int total_q = (int)((int64_t)n_qt * a.bh);
+  if (total_q > 0) {
+    void* p2[] = {&args, &n_qt, &total_q};
+    e = hipLaunchKernel((const void*)&bwd_dq_kernel<BF16, CAUSAL, D>, dim3(total_q),
+                        dim3(kBwdThreads), p2, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <bool BF16, int D>
@@ -559,8 +591,10 @@ hipError_t launch_bwd_h16(bool bf16, int d, bool causal, const BwdArgs& a, const
                  : launch_d<false, 128>(causal, a, o, delta, s);
 }
 
-int64_t bwd_grid_blocks(int64_t bh, int64_t n) {
-  return (n + kBwdRows - 1) / kBwdRows * bh;
+int64_t bwd_grid_blocks(int64_t bh, int64_t bkv, int64_t nq, int64_t nk) {
+  const int64_t kv = (nk + kBwdRows - 1) / kBwdRows * bkv;
+  const int64_t q = (nq + kBwdRows - 1) / kBwdRows * bh;
+  return kv > q ? kv : q;
 }
 
 }  // namespace fa_impl

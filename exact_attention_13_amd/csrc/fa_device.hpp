@@ -79,8 +79,14 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  int bh;          // B*H
-  int n;           // sequence length
+  int bh;          // B*H query heads
+  int hq;          // H, query heads per batch entry
+  int hkv;         // H_kv, K/V heads per batch entry; query head h uses K/V head h / hgrp
+  int hgrp;        // H / H_kv
+  int bkv;         // B*H_kv
+  int nq;          // query rows per head (q, o, dout, dq, lse, delta)
+  int nk;          // keys per K/V head (k, v, dk, dv)
+  int off;         // causal alignment N_kv - N_q: key j is visible to row i when j <= i + off
   float scale;     // multiplier of q.k
   float scale_log2;  // scale * log2(e)
 };
@@ -152,7 +158,9 @@ hipError_t launch_fwd_f32(int d, bool causal, bool split, const FwdArgs& a, hipS
 // Backward pass (bf16/fp16): delta, then dK/dV, then dQ on stream s.
 hipError_t launch_bwd_h16(bool bf16, int d, bool causal, const BwdArgs& a, const void* o,
                           float* delta, hipStream_t s);
-int64_t bwd_grid_blocks(int64_t bh, int64_t n);
+// Largest workgroup count of the backward launches (dK/dV over the K/V heads'
+// key tiles, dQ over the query heads' row tiles).
+int64_t bwd_grid_blocks(int64_t bh, int64_t bkv, int64_t nq, int64_t nk);
 
 // Merge `splits` partial results (fp32 O divided by its own row sum, and its
 // logsumexp) of `rows` rows of head size d into O of the I/O type and LSE.

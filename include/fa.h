@@ -211,6 +211,33 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int64_t H, int64_t N, int64_t d, float scale, int causal, fa_dtype dtype,
                  void* stream);
 
+/*
+ * fa_bwd_ex -- fa_bwd for grouped K/V heads and separate query and key
+ * lengths: the gradients of fa_fwd_ex (any num_splits; the split only changes
+ * how the forward computed O and LSE).
+ *
+ * q, o, dout, dq   device [B, H, N_q, d] of `dtype` (dq written in full).
+ * k, v, dk, dv     device [B, H_kv, N_kv, d] of `dtype` (dk, dv written in
+ *                  full); H_kv divides H and query head h uses K/V head
+ *                  h / (H / H_kv), as in fa_fwd_ex.
+ * lse, delta       device fp32 [B, H, N_q]: fa_fwd_ex's lse; caller-owned
+ *                  scratch for the row dot products.
+ * causal           the mask of fa_fwd_ex: key j is visible to query row i
+ *                  when j <= i + N_kv - N_q.
+ * Every query head of a group contributes to its K/V head: dK and dV are the
+ * sums of the per-query-head gradients (chain rule through the shared K/V
+ * head), formed in registers by one workgroup per (K/V head, 128 keys), so
+ * results stay bitwise reproducible.  A query row that sees no key gets a
+ * zero dQ row; with N_q = 0, dk and dv are zero-filled; with N_kv = 0, dq is
+ * zero-filled.  Pointers of an empty side (q, o, dout, lse, dq, delta when
+ * N_q = 0; k, v, dk, dv when N_kv = 0) may be NULL.  Validation and
+ * alignment as fa_bwd, plus FA_ERR_SHAPE when H_kv does not divide H.
+ */
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B,
+                    int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t d, float scale,
+                    int causal, fa_dtype dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(fa_status s);
 

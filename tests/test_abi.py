@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert libfa.version() == 200
+    assert libfa.version() == 300
     for code in range(10):
         msg = libfa.strerror(code)
         assert msg and "unknown" not in msg
@@ -238,3 +238,45 @@ def test_bwd_rejects(kw, status):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
 def test_bwd_empty_is_a_noop(kw):
     assert call_bwd(**kw) == 0
+
+
+# --------------------------------------------------------------------------
+# fa_bwd_ex (validation only, no launch)
+# --------------------------------------------------------------------------
+
+BWDX_ARGS = dict(q=Q, k=K, v=V, o=OB, dout=GB, lse=L, dq=DQ, dk=DK, dv=DV, delta=DL, B=1, H=4,
+                 H_kv=2, N_q=100, N_kv=300, d=128, scale=0.088, causal=1, dtype=libfa.FA_F16,
+                 stream=None)
+
+
+def call_bwd_ex(**kw):
+    a = dict(BWDX_ARGS)
+    a.update(kw)
+    return libfa.fa_bwd_ex(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                           a["dv"], a["delta"], a["B"], a["H"], a["H_kv"], a["N_q"], a["N_kv"],
+                           a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(dout=None), 1), (dict(lse=None), 1),
+    (dict(dq=None), 1), (dict(delta=None), 1), (dict(k=None), 1), (dict(v=None), 1),
+    (dict(dk=None), 1), (dict(dv=None), 1),
+    (dict(k=None, N_q=0), 1), (dict(q=None, N_kv=0), 1),
+    (dict(H_kv=-1), 2), (dict(N_q=-1), 2), (dict(N_kv=-2), 2), (dict(H_kv=3), 2),
+    (dict(H_kv=0), 2), (dict(N_kv=1 << 31), 2), (dict(N_q=1 << 31), 2),
+    (dict(d=96), 3), (dict(dtype=libfa.FA_F32), 4), (dict(scale=float("nan")), 5),
+    (dict(dk=DK + 8), 6), (dict(v=V + 2), 6), (dict(lse=L + 1), 6),
+    # dK/dV are [B, H_kv, N_kv, d] (300 * 128 * 2 * 2 bytes), dQ [B, H, N_q, d]
+    (dict(dk=K + 150_000), 7), (dict(dv=DK + 153_584), 7), (dict(dq=OB + 102_384), 7),
+    (dict(delta=L + 1596), 7),
+])
+def test_bwd_ex_rejects(kw, status):
+    assert call_bwd_ex(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=0), dict(H=0, H_kv=0), dict(N_q=0, N_kv=0),
+    dict(N_q=0, N_kv=0, q=None, o=None, dout=None, lse=None, dq=None, delta=None,
+         k=None, v=None, dk=None, dv=None)])
+def test_bwd_ex_empty_is_a_noop(kw):
+    assert call_bwd_ex(**kw) == 0

@@ -154,3 +154,111 @@ def test_bwd_workload_sampled_rows_and_invariants(name):
     sum_v = dv64.sum(dim=2)
     sum_g = dout.double().sum(dim=2)
     assert float((sum_v - sum_g).norm()) <= 5 * u * float(dv64.norm()), f"{name}: sum of dV rows"
+
+
+# --------------------------------------------------------------------------
+# Grouped K/V heads and N_q != N_kv (fa_bwd_ex)
+# --------------------------------------------------------------------------
+
+def run_bwd_ex(w, q, k, v, dout, splits=1):
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dout))
+    o, lse = binding.fwd_ex(qd, kd, vd, w.scale, w.causal, num_splits=splits)
+    dq, dk, dv = binding.bwd(qd, kd, vd, o, lse, gd, w.scale, w.causal)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+GROUPED = [  # (H, H_kv, N_q, N_kv)
+    (4, 2, 100, 100), (4, 1, 77, 300), (6, 2, 300, 77), (8, 8, 33, 65), (2, 1, 1, 1000),
+    (4, 4, 129, 129), (16, 2, 40, 257),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_grouped_shapes(dtype, d, causal):
+    for i, (H, Hkv, Nq, Nk) in enumerate(GROUPED):
+        w = Workload("case", dtype, 2 if i % 2 else 1, H, Nq, d, causal, 1700 + i, "normal", Hkv, Nk)
+        q, k, v = make_inputs(w)
+        dout = upstream(w, 1800 + i)
+        _note(f"bwd_ex {dtype} d={d} causal={causal} B={w.B} H={H} H_kv={Hkv} N_q={Nq} N_kv={Nk}")
+        dq, dk, dv = run_bwd_ex(w, q, k, v, dout)
+        rq, rk, rv = oracle.bwd(q, k, v, dout, w.scale, causal)
+        for got, ref, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+            assert_grad_close(got, ref, dtype, f"{(H, Hkv, Nq, Nk)} {name}")
+        if causal and Nq > Nk:
+            assert torch.all(dq[:, :, : Nq - Nk] == 0)
+
+
+def test_bwd_grouped_after_split_forward():
+    # the forward's key split changes only how O and LSE were formed
+    w = Workload("case", "bf16", 2, 8, 3, 128, False, 1900, "normal", 2, 4000)
+    q, k, v = make_inputs(w)
+    dout = upstream(w, 1901)
+    _note("bwd_ex after a split forward")
+    dq, dk, dv = run_bwd_ex(w, q, k, v, dout, splits=8)
+    rq, rk, rv = oracle.bwd(q, k, v, dout, w.scale, False)
+    for got, ref, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        assert_grad_close(got, ref, "bf16", name)
+
+
+def test_bwd_ex_empty_sides_are_zero_filled():
+    # N_q = 0: no query uses the keys, so dK = dV = 0; N_kv = 0: dQ = 0.
+    st = torch.cuda.current_stream().cuda_stream
+    kv = torch.randn((1, 2, 70, 64), device=DEV).to(torch.bfloat16)
+    dk = torch.full_like(kv, float("nan"))
+    dv = torch.full_like(kv, float("nan"))
+    _note("bwd_ex N_q = 0")
+    s = binding.fa_bwd_ex(0, kv.data_ptr(), kv.data_ptr(), 0, 0, 0, 0, dk.data_ptr(),
+                          dv.data_ptr(), 0, 1, 4, 2, 0, 70, 64, 0.125, True, binding.FA_BF16, st)
+    assert s == 0
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+    q = torch.randn((1, 4, 50, 64), device=DEV).to(torch.bfloat16)
+    o, g = torch.zeros_like(q), torch.randn_like(q)
+    lse = torch.full((1, 4, 50), float("-inf"), device=DEV)
+    dq = torch.full_like(q, float("nan"))
+    delta = torch.empty_like(lse)
+    _note("bwd_ex N_kv = 0")
+    s = binding.fa_bwd_ex(q.data_ptr(), 0, 0, o.data_ptr(), g.data_ptr(), lse.data_ptr(),
+                          dq.data_ptr(), 0, 0, delta.data_ptr(), 1, 4, 2, 50, 0, 64, 0.125, False,
+                          binding.FA_BF16, st)
+    assert s == 0
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0)
+
+
+def test_bwd_grouped_deterministic():
+    w = Workload("case", "f16", 1, 8, 600, 128, True, 1950, "normal", 2, 700)
+    q, k, v = make_inputs(w)
+    dout = upstream(w, 1951)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dout))
+    o, lse = binding.fwd_ex(qd, kd, vd, w.scale, True, num_splits=1)
+    _note("bwd_ex determinism")
+    r1 = binding.bwd(qd, kd, vd, o, lse, gd, w.scale, True)
+    r2 = binding.bwd(qd, kd, vd, o, lse, gd, w.scale, True)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+def test_bwd_workload_g2_sampled_rows_and_invariants():
+    # G2: bf16 B=8, 16 query heads on 2 K/V heads, N=4096, d=128, causal.
+    # dQ rows sampled against the oracle; per K/V head the key gradients sum
+    # to zero and the value gradients to the sum of its group's dO rows.
+    w = WORKLOADS["G2"]
+    q, k, v = make_inputs(w)
+    dout = upstream(w, 2000)
+    _note("bwd workload G2")
+    dq, dk, dv = run_bwd_ex(w, q, k, v, dout)
+    rows = sample_rows(w, 256)
+    ref = oracle.bwd_dq_rows(q, k, v, dout, w.scale, w.causal, rows)
+    got = dq.reshape(-1, w.d)[torch.from_numpy(rows)]
+    assert_grad_close(got, ref, w.dtype, "G2 dQ rows")
+    u = UNIT[w.dtype]
+    dk64, dv64 = dk.double(), dv.double()
+    assert float(dk64.sum(dim=2).norm()) <= 5 * u * float(dk64.norm()), "G2: sum of dK rows"
+    grp = w.H // w.h_kv
+    sum_g = dout.double().sum(dim=2).reshape(w.B, w.h_kv, grp, w.d).sum(dim=2)
+    assert float((dv64.sum(dim=2) - sum_g).norm()) <= 5 * u * float(dv64.norm()), "G2: dV rows"
