@@ -50,7 +50,7 @@ KERNEL_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_fwd_h16.hip", "fa_fwd_f32.h
                   "fa_api.hip", "fa_combine.hip"]
 
 
-BWD_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_bwd_h16.hip", "fa_api.hip"]
+BWD_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_bwd_h16.hip", "fa_bwd_f32.hip", "fa_api.hip"]
 
 
 def kernel_source_hash(names=KERNEL_SOURCES) -> str:
@@ -217,8 +217,6 @@ def main():
 
     splits, workspace = 1, None
     if args.which == "bwd":
-        if w.dtype == "f32":
-            sys.exit("the backward pass runs on bf16/fp16 workloads (C3, C4, C5, G1, G2)")
         g = np.random.default_rng(w.seed + 100)
         dout = torch.from_numpy(g.standard_normal((w.B, w.H, w.N, w.d)).astype(np.float32)).to(
             qd.dtype).to(dev)
@@ -228,7 +226,7 @@ def main():
             binding.fwd(qd, kd, vd, w.scale, w.causal, out=o, lse=lse, stream=stream)
         grads = [torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)]
         delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-        dt_code = binding.FA_BF16 if w.dtype == "bf16" else binding.FA_F16
+        dt_code = {"f32": binding.FA_F32, "bf16": binding.FA_BF16, "f16": binding.FA_F16}[w.dtype]
         ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), dout.data_ptr(),
                 lse.data_ptr(), *(t.data_ptr() for t in grads), delta.data_ptr())
 

@@ -258,7 +258,7 @@ def fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, N_q, N_kv, d
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         lse: torch.Tensor, dout: torch.Tensor, scale: float | None = None,
         causal: bool = False, stream: torch.cuda.Stream | None = None):
-    """Gradients (dq, dk, dv) of the forward pass for bf16/fp16 tensors.
+    """Gradients (dq, dk, dv) of the forward pass for fp32/bf16/fp16 tensors.
 
     q, o, dout: [B, H, N_q, d]; k, v: [B, H_kv, N_kv, d] with H_kv dividing H
     (``fa_bwd`` when the shapes are all equal, else ``fa_bwd_ex``).  ``o`` and
@@ -268,9 +268,8 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     """
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or not (q.shape == o.shape == dout.shape):
         raise ValueError("q, o, dout must be [B, H, N_q, d] and k, v [B, H_kv, N_kv, d]")
-    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype) or \
-            q.dtype not in (torch.bfloat16, torch.float16):
-        raise TypeError("the backward pass takes bfloat16 or float16 tensors of one dtype")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype) or q.dtype not in _DTYPE_CODES:
+        raise TypeError("the backward pass takes float32, bfloat16 or float16 tensors of one dtype")
     tensors = (q, k, v, o, dout, lse)
     if not all(t.is_cuda and t.is_contiguous() for t in tensors):
         raise ValueError("inputs must be contiguous GPU tensors")

@@ -274,21 +274,22 @@ extern "C" fa_status fa_bwd_ex(const void* q, const void* k, const void* v, cons
       (N_kv != 0 && (!k || !v || !dk || !dv)))
     return FA_ERR_NULL;
   if (B < 0 || H < 0 || H_kv < 0 || N_q < 0 || N_kv < 0) return FA_ERR_SHAPE;
-  if (!valid_dtype(dtype) || dtype == FA_F32) return FA_ERR_DTYPE;
+  if (!valid_dtype(dtype)) return FA_ERR_DTYPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
   if (H_kv == 0 ? H != 0 : H % H_kv != 0) return FA_ERR_SHAPE;
   if (B == 0 || H == 0 || (N_q == 0 && N_kv == 0)) return FA_OK;
+  const int64_t e = elem_bytes(dtype);
   if (N_q > INT32_MAX || N_kv > INT32_MAX || H > INT32_MAX || B > INT32_MAX / H)
     return FA_ERR_SHAPE;
   const int64_t bh = B * H, bkv = B * H_kv;
-  if (N_q > 0 && (bh > INT64_MAX / N_q || bh * N_q > INT64_MAX / (d * 2))) return FA_ERR_SHAPE;
-  if (N_kv > 0 && (bkv > INT64_MAX / N_kv || bkv * N_kv > INT64_MAX / (d * 2)))
+  if (N_q > 0 && (bh > INT64_MAX / N_q || bh * N_q > INT64_MAX / (d * e))) return FA_ERR_SHAPE;
+  if (N_kv > 0 && (bkv > INT64_MAX / N_kv || bkv * N_kv > INT64_MAX / (d * e)))
     return FA_ERR_SHAPE;
-  if ((N_q + kRowSlack) * d * 2 > INT32_MAX || (N_kv + kRowSlack) * d * 2 > INT32_MAX)
+  if ((N_q + kRowSlack) * d * e > INT32_MAX || (N_kv + kRowSlack) * d * e > INT32_MAX)
     return FA_ERR_SHAPE;
   if (fa_impl::bwd_grid_blocks(bh, bkv, N_q, N_kv) > INT32_MAX) return FA_ERR_SHAPE;
-  if ((bh * N_q + 255) / 256 * (d / 8) > INT32_MAX) return FA_ERR_SHAPE;  // row-dot grid
+  if ((bh * N_q + 255) / 256 * (d / 4) > INT32_MAX) return FA_ERR_SHAPE;  // row-dot grid
 
   if (N_q != 0) {
     const void* qs[4] = {q, o, dout, dq};
@@ -299,7 +300,7 @@ extern "C" fa_status fa_bwd_ex(const void* q, const void* k, const void* v, cons
   if (N_kv != 0 && (!aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) || !aligned(dv, 16)))
     return FA_ERR_ALIGN;
 
-  const int64_t qb = bh * N_q * d * 2, kvb = bkv * N_kv * d * 2, lb = bh * N_q * 4;
+  const int64_t qb = bh * N_q * d * e, kvb = bkv * N_kv * d * e, lb = bh * N_q * 4;
   const void* in[6] = {q, k, v, o, dout, lse};
   const int64_t in_bytes[6] = {qb, kvb, kvb, qb, qb, lb};
   void* out[4] = {dq, dk, dv, delta};
@@ -331,6 +332,9 @@ extern "C" fa_status fa_bwd_ex(const void* q, const void* k, const void* v, cons
   a.off = (int)(N_kv - N_q);
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  if (dtype == FA_F32)
+    return launch_status(
+        fa_impl::launch_bwd_f32((int)d, causal != 0, a, o, delta, (hipStream_t)stream));
   return launch_status(fa_impl::launch_bwd_h16(dtype == FA_BF16, (int)d, causal != 0, a, o, delta,
                                                (hipStream_t)stream));
 }

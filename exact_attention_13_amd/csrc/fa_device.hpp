@@ -158,6 +158,9 @@ hipError_t launch_fwd_f32(int d, bool causal, bool split, const FwdArgs& a, hipS
 // Backward pass (bf16/fp16): delta, then dK/dV, then dQ on stream s.
 hipError_t launch_bwd_h16(bool bf16, int d, bool causal, const BwdArgs& a, const void* o,
                           float* delta, hipStream_t s);
+// Backward pass for fp32 inputs (fp32 MFMA), same three kernels and arguments.
+hipError_t launch_bwd_f32(int d, bool causal, const BwdArgs& a, const void* o, float* delta,
+                          hipStream_t s);
 // Largest workgroup count of the backward launches (dK/dV over the K/V heads'
 // key tiles, dQ over the query heads' row tiles).
 int64_t bwd_grid_blocks(int64_t bh, int64_t bkv, int64_t nq, int64_t nk);

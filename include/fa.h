@@ -50,7 +50,7 @@ typedef enum {
   FA_ERR_NULL = 1,     /* a required pointer (q, k, v, o, partials) is NULL     */
   FA_ERR_SHAPE = 2,    /* a size negative, H not a multiple of H_kv, too large  */
   FA_ERR_HEAD_DIM = 3, /* d is not one of the supported head sizes (64, 128)    */
-  FA_ERR_DTYPE = 4,    /* dtype not an fa_dtype value (fa_bwd: FA_F32 too)      */
+  FA_ERR_DTYPE = 4,    /* dtype not an fa_dtype value                           */
   FA_ERR_SCALE = 5,    /* scale is not finite or not > 0                        */
   FA_ERR_ALIGN = 6,    /* a tensor not 16-byte aligned, lse not 4-byte          */
   FA_ERR_ALIAS = 7,    /* an output or the workspace overlaps another buffer    */
@@ -191,8 +191,9 @@ fa_status fa_lse_combine(const float* o_part, const float* lse_part, int64_t spl
  *     dQ_i = scale sum_j dS_ij k_j.
  *
  * q, k, v, o   the forward call's inputs and output: device, contiguous
- *              [B, H, N, d] of `dtype` (FA_BF16 or FA_F16; FA_F32 returns
- *              FA_ERR_DTYPE), read only.
+ *              [B, H, N, d] of `dtype` (FA_F32, FA_BF16 or FA_F16), read
+ *              only.  fp32 runs on fp32 MFMA with fp32 weights; bf16/fp16
+ *              round P and dS to the input type as MFMA operands.
  * dout         device [B, H, N, d] of `dtype`: dL/dO, read only.
  * lse          device fp32 [B, H, N]: the lse fa_fwd wrote for the same
  *              q, k, v, scale and causal flag, read only.

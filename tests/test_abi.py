@@ -226,7 +226,7 @@ def call_bwd(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(dout=None), 1), (dict(lse=None), 1), (dict(dv=None), 1),
     (dict(delta=None), 1), (dict(N=-1), 2), (dict(N=1 << 31), 2), (dict(d=32), 3),
-    (dict(dtype=libfa.FA_F32), 4), (dict(dtype=3), 4), (dict(scale=0.0), 5),
+    (dict(dtype=-1), 4), (dict(dtype=3), 4), (dict(scale=0.0), 5),
     (dict(dq=DQ + 8), 6), (dict(o=OB + 4), 6), (dict(delta=DL + 2), 6),
     (dict(dq=Q), 7), (dict(dk=DQ + 64), 7), (dict(dv=GB), 7), (dict(delta=L), 7),
     (dict(delta=DV + 128), 7), (dict(dk=K - 16), 7),
@@ -264,7 +264,7 @@ def call_bwd_ex(**kw):
     (dict(k=None, N_q=0), 1), (dict(q=None, N_kv=0), 1),
     (dict(H_kv=-1), 2), (dict(N_q=-1), 2), (dict(N_kv=-2), 2), (dict(H_kv=3), 2),
     (dict(H_kv=0), 2), (dict(N_kv=1 << 31), 2), (dict(N_q=1 << 31), 2),
-    (dict(d=96), 3), (dict(dtype=libfa.FA_F32), 4), (dict(scale=float("nan")), 5),
+    (dict(d=96), 3), (dict(dtype=7), 4), (dict(scale=float("nan")), 5),
     (dict(dk=DK + 8), 6), (dict(v=V + 2), 6), (dict(lse=L + 1), 6),
     # dK/dV are [B, H_kv, N_kv, d] (300 * 128 * 2 * 2 bytes), dQ [B, H, N_q, d]
     (dict(dk=K + 150_000), 7), (dict(dv=DK + 153_584), 7), (dict(dq=OB + 102_384), 7),

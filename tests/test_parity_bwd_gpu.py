@@ -15,6 +15,10 @@ and measured errors are about 1.3 u (rel-L2).  The bound is
 for every gradient G.  The absolute floor covers gradients that vanish in
 exact arithmetic (one key: the softmax is constant, so dQ = dK = 0, while
 the kernels carry rounding residues of the recomputed weights).
+
+fp32 inputs keep P and dS in fp32 (fp32 MFMA), so the error is the fp32
+accumulation over up to N terms (about sqrt(N) 2^-24 relative, 2^-17 for
+N = 16384) plus v_exp_f32's last-bit error: the same bound with u = 2^-17.
 """
 import sys
 
@@ -29,7 +33,8 @@ from exact_attention_13_amd.inputs import WORKLOADS, Workload, make_inputs, samp
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-UNIT = {"bf16": 2.0 ** -9, "f16": 2.0 ** -11}
+UNIT = {"bf16": 2.0 ** -9, "f16": 2.0 ** -11, "f32": 2.0 ** -17}
+TORCH = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 def _note(msg):
@@ -40,7 +45,7 @@ def _note(msg):
 def upstream(w, seed):
     g = np.random.default_rng(seed)
     x = g.standard_normal((w.B, w.H, w.N, w.d)).astype(np.float32)
-    return torch.from_numpy(x).to({"bf16": torch.bfloat16, "f16": torch.float16}[w.dtype])
+    return torch.from_numpy(x).to(TORCH[w.dtype])
 
 
 def run_bwd(w, q, k, v, dout):
@@ -67,7 +72,7 @@ def assert_grad_close(got, ref, dtype, what):
 SMALL_N = [1, 31, 32, 33, 100, 128, 129, 257, 512]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_small_shapes(dtype, d, causal):
@@ -83,7 +88,7 @@ def test_bwd_small_shapes(dtype, d, causal):
             assert_grad_close(got, ref, dtype, f"N={n} {name}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_bwd_large_logits(dtype):
     # scores with std ~ 9: most weights are tiny, a few dominate each row
     w = Workload("case", dtype, 1, 2, 333, 128, True, 1300, "large_logit")
@@ -132,7 +137,7 @@ def test_bwd_medium_full_oracle():
         assert_grad_close(got, ref, "bf16", name)
 
 
-@pytest.mark.parametrize("name", ["C3", "C4", "C5"])
+@pytest.mark.parametrize("name", ["C3", "C4", "C5", "C2", "C2r"])
 def test_bwd_workload_sampled_rows_and_invariants(name):
     # Full size: dQ rows sampled against the oracle (each row needs only its
     # own recomputed weights); dK and dV checked through what holds for any
@@ -174,7 +179,7 @@ GROUPED = [  # (H, H_kv, N_q, N_kv)
 ]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_grouped_shapes(dtype, d, causal):
@@ -262,3 +267,27 @@ def test_bwd_workload_g2_sampled_rows_and_invariants():
     grp = w.H // w.h_kv
     sum_g = dout.double().sum(dim=2).reshape(w.B, w.h_kv, grp, w.d).sum(dim=2)
     assert float((dv64.sum(dim=2) - sum_g).norm()) <= 5 * u * float(dv64.norm()), "G2: dV rows"
+
+
+def test_bwd_f32_deterministic_and_delta():
+    w = Workload("case", "f32", 2, 2, 333, 128, True, 2100)
+    q, k, v = make_inputs(w)
+    dout = upstream(w, 2101)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dout))
+    o, lse = binding.fwd(qd, kd, vd, w.scale, True)
+    _note("bwd f32 determinism")
+    r1 = binding.bwd(qd, kd, vd, o, lse, gd, w.scale, True)
+    r2 = binding.bwd(qd, kd, vd, o, lse, gd, w.scale, True)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+    delta = torch.empty((2, 2, 333), dtype=torch.float32, device=DEV)
+    outs = [torch.empty_like(qd) for _ in range(3)]
+    st = binding.fa_bwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), gd.data_ptr(),
+                        lse.data_ptr(), *(t.data_ptr() for t in outs), delta.data_ptr(),
+                        2, 2, 333, 128, w.scale, True, binding.FA_F32,
+                        torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    ref = (o.cpu().double() * dout.double()).sum(-1)
+    np.testing.assert_allclose(delta.cpu().double().numpy(), ref.numpy(), rtol=1e-5, atol=1e-5)
