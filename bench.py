@@ -47,10 +47,11 @@ METRIC = "fwd attention TFLOP/s & % MFMA peak, bf16 B=1 H=16 N=16384 d=64 (1 GPU
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_fwd_h16.hip", "fa_fwd_f32.hip",
-                  "fa_api.hip", "fa_combine.hip"]
+                  "fa_api.hip", "fa_api_util.hpp", "fa_combine.hip"]
 
 
-BWD_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_bwd_h16.hip", "fa_bwd_f32.hip", "fa_api.hip"]
+BWD_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_bwd.hpp", "fa_bwd_h16.hip", "fa_bwd_f32.hip",
+               "fa_api_bwd.hip", "fa_api_util.hpp"]
 
 
 def kernel_source_hash(names=KERNEL_SOURCES) -> str:

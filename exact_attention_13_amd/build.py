@@ -21,8 +21,8 @@ LIB = PKG / "libfa.so"
 BUILD_DIR = PKG / "_build"
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.hip", "fa_fwd_h16.hip", "fa_fwd_f32.hip", "fa_combine.hip", "fa_bwd_h16.hip",
-           "fa_bwd_f32.hip"]
+SOURCES = ["fa_api.hip", "fa_api_bwd.hip", "fa_fwd_h16.hip", "fa_fwd_f32.hip", "fa_combine.hip",
+           "fa_bwd_h16.hip", "fa_bwd_f32.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 are generated.
 HIPCC_FLAGS = [

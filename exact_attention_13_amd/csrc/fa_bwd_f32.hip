@@ -28,7 +28,7 @@
 //     transposed) and V (row-major) in LDS; dQ^T += K^T dS^T.
 // Causal masking (key j visible to row i when j <= i + N_kv - N_q), ragged
 // tails and rows without a visible key follow the bf16/fp16 backward.
-#include "fa_device.hpp"
+#include "fa_bwd.hpp"
 
 namespace fa_impl {
 namespace {

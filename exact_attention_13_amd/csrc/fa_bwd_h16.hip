@@ -27,6 +27,7 @@
 // Causal masking, ragged tails and the -inf guard follow the forward kernels.
 #include <type_traits>
 
+#include "fa_bwd.hpp"
 #include "fa_h16.hpp"
 
 namespace fa_impl {

@@ -68,29 +68,6 @@ struct FwdArgs {
   float scale_log2;  // scale * log2(e): scores enter exp2 in this unit
 };
 
-// Arguments of the backward kernels (square heads: [B, H, N, d] everywhere).
-struct BwdArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* dout;   // upstream gradient dO
-  const float* lse;   // the forward pass's logsumexp, natural log
-  const float* delta;  // D_i = dO_i . O_i, filled by the first backward kernel
-  void* dq;
-  void* dk;
-  void* dv;
-  int bh;          // B*H query heads
-  int hq;          // H, query heads per batch entry
-  int hkv;         // H_kv, K/V heads per batch entry; query head h uses K/V head h / hgrp
-  int hgrp;        // H / H_kv
-  int bkv;         // B*H_kv
-  int nq;          // query rows per head (q, o, dout, dq, lse, delta)
-  int nk;          // keys per K/V head (k, v, dk, dv)
-  int off;         // causal alignment N_kv - N_q: key j is visible to row i when j <= i + off
-  float scale;     // multiplier of q.k
-  float scale_log2;  // scale * log2(e)
-};
-
 // K/V head read by problem p.
 __device__ __forceinline__ int kv_head(const FwdArgs& a, int p) {
   return (p / a.hp) * a.hkv + (p % a.hp) / a.grp;
@@ -155,15 +132,6 @@ hipError_t launch_fwd_h16(bool bf16, int d, bool causal, bool split, const FwdAr
                           hipStream_t s);
 hipError_t launch_fwd_f32(int d, bool causal, bool split, const FwdArgs& a, hipStream_t s);
 
-// Backward pass (bf16/fp16): delta, then dK/dV, then dQ on stream s.
-hipError_t launch_bwd_h16(bool bf16, int d, bool causal, const BwdArgs& a, const void* o,
-                          float* delta, hipStream_t s);
-// Backward pass for fp32 inputs (fp32 MFMA), same three kernels and arguments.
-hipError_t launch_bwd_f32(int d, bool causal, const BwdArgs& a, const void* o, float* delta,
-                          hipStream_t s);
-// Largest workgroup count of the backward launches (dK/dV over the K/V heads'
-// key tiles, dQ over the query heads' row tiles).
-int64_t bwd_grid_blocks(int64_t bh, int64_t bkv, int64_t nq, int64_t nk);
 
 // Merge `splits` partial results (fp32 O divided by its own row sum, and its
 // logsumexp) of `rows` rows of head size d into O of the I/O type and LSE.
