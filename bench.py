@@ -25,6 +25,9 @@ visible pair).  Prints ONE JSON line with:
                         below the ridge point; ``traffic`` is the HBM bytes per launch
                         from the committed rocprofv3 counter summary when it
                         was taken on the current kernel source, else null;
+                        ``kernel_ms_cold_median`` times further calls made
+                        right after reading a 512 MiB buffer (L2 and MALL
+                        flushed), so K/V start from HBM;
   cpu_baseline          the fp64 oracle timed on the host cores on a bounded
                         row sample of the same workload (reported baseline).
 """
@@ -46,6 +49,7 @@ METRIC = "fwd attention TFLOP/s & % MFMA peak, bf16 B=1 H=16 N=16384 d=64 (1 GPU
 # MI355X published dense peaks (TFLOP/s) per input dtype, and HBM bandwidth.
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
+COLD_FLUSH_BYTES = 512 << 20
 KERNEL_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_fwd_h16.hip", "fa_fwd_f32.hip",
                   "fa_api.hip", "fa_api_util.hpp", "fa_combine.hip"]
 
@@ -164,6 +168,10 @@ def main():
     ap.add_argument("--splits", type=int, default=None,
                     help="key ranges for fa_fwd_ex workloads (default: the workload's, "
                          "0 = the library's choice)")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="calls after the timed steps, each preceded by a 512 MiB read that "
+                         "flushes the caches; "
+                         "their median duration is roofline.kernel_ms_cold_median (0: skip)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, run a plain device copy of this many bytes "
                          "(calibrates the HBM traffic counters)")
@@ -274,6 +282,26 @@ def main():
     avg_kernel_ms = sum(kernel_ms) / len(kernel_ms)
     ms_per_step = wall * 1e3 / args.steps
 
+    # Cold caches: reading a 512 MiB buffer between calls evicts the L2s and
+    # the MALL (a read leaves no dirty lines to write back during the next
+    # call), so K/V start from HBM; outside the timed steps.
+    cold_ms = None
+    if args.cold_steps > 0:
+        flush = torch.ones(COLD_FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+        sink = torch.empty((), dtype=torch.int64, device=dev)
+        cold = []
+        for i in range(args.cold_steps):
+            torch.sum(flush, dim=0, out=sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            cold.append((a, b))
+        torch.cuda.synchronize()
+        cold_sorted = sorted(a.elapsed_time(b) for a, b in cold)
+        cold_ms = round(cold_sorted[len(cold_sorted) // 2], 5)
+        del flush, sink
+
     flops = w.flops * (2.5 if args.which == "bwd" else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -316,7 +344,8 @@ def main():
                                else "one forward kernel"),
                      "kernel_ms_avg": round(avg_kernel_ms, 5),
                      "kernel_ms_min": round(kernel_ms[0], 5),
-                     "kernel_ms_median": round(kernel_ms[len(kernel_ms) // 2], 5)},
+                     "kernel_ms_median": round(kernel_ms[len(kernel_ms) // 2], 5),
+                     "kernel_ms_cold_median": cold_ms},
     }
     if not args.no_cpu_baseline:
         if args.which == "bwd":
