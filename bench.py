@@ -50,22 +50,31 @@ METRIC = "fwd attention TFLOP/s & % MFMA peak, bf16 B=1 H=16 N=16384 d=64 (1 GPU
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 COLD_FLUSH_BYTES = 512 << 20
-KERNEL_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_fwd_h16.hip", "fa_fwd_f32.hip",
-                  "fa_api.hip", "fa_api_util.hpp", "fa_combine.hip"]
+# Sources of the forward kernels of each input-type family (a committed
+# traffic summary counts only while these hash to the value it records).
+FWD_SOURCES = {
+    "h16": ["fa_device.hpp", "fa_h16.hpp", "fa_fwd_h16.hip", "fa_api.hip", "fa_api_util.hpp",
+            "fa_combine.hip"],
+    "f32": ["fa_device.hpp", "fa_fwd_f32.hip", "fa_api.hip", "fa_api_util.hpp", "fa_combine.hip"],
+}
 
 
 BWD_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_bwd.hpp", "fa_bwd_h16.hip", "fa_bwd_f32.hip",
                "fa_api_bwd.hip", "fa_api_util.hpp"]
 
 
-def kernel_source_hash(names=KERNEL_SOURCES) -> str:
+def fwd_sources(dtype: str):
+    return FWD_SOURCES["f32" if dtype == "f32" else "h16"]
+
+
+def kernel_source_hash(names=FWD_SOURCES["h16"]) -> str:
     h = hashlib.sha256()
     for name in names:
         h.update((ROOT / "exact_attention_13_amd" / "csrc" / name).read_bytes())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, dtype: str):
     """HBM bytes per launch from the committed counter summary, or None."""
     path = ROOT / "profiles" / f"fa_fwd_{workload}_hbm_traffic.txt"
     if not path.exists():
@@ -75,7 +84,7 @@ def read_traffic(workload: str):
         m = re.match(r"^([a-z_]+):\s*(\S+)", line)
         if m:
             fields[m.group(1)] = m.group(2)
-    if fields.get("kernel_source_sha") != kernel_source_hash():
+    if fields.get("kernel_source_sha") != kernel_source_hash(fwd_sources(dtype)):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -310,7 +319,7 @@ def main():
         achieved, peak, unit = w.io_bytes / (avg_kernel_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
     else:
         achieved, unit = flops / (avg_kernel_ms * 1e-3) / 1e12, "TFLOP/s"
-    traffic = read_traffic(w.name)
+    traffic = read_traffic(w.name, w.dtype) if args.which == "fwd" else None
 
     if args.which == "bwd":
         metric = f"bwd attention TFLOP/s (2.5x fwd FLOPs), workload {w.name}"

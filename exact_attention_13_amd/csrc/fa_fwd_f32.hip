@@ -260,8 +260,241 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
                          dim3(kThreads), params, 0, s);
 }
 
+// ---------------------------------------------------------------------------
+// Short grids (fewer workgroups than kShortGrid): each workgroup owns only 32
+// query rows and its four waves split the keys instead of the rows.  A step
+// stages KS = 4 KW keys in LDS (cooperatively, single-buffered); wave w runs
+// the online softmax over keys [k0 + w KW, k0 + (w+1) KW) of every step, and
+// at the end the four partial results (m_w, l_w, O_w) are merged through LDS
+// with the rescaling of the online softmax ("FlashAttention dissected",
+// "Tiling and Online Softmax"): O = sum_w e^(m_w - m) O_w / sum_w e^(m_w - m) l_w.
+// The serial chain of a row is then a quarter as long, which is what bounds a
+// latency-bound problem such as one 512-row head.
+// ---------------------------------------------------------------------------
+constexpr int kShortGrid = 128;
+
+template <int D>
+struct Short {
+  static constexpr int KW = D == 64 ? 64 : 32;  // keys per wave per step
+  static constexpr int KS = 4 * KW;             // keys per step
+  static constexpr int kKStride = D + 4;
+  static constexpr int kVStride = KS + 4;
+  static constexpr int kKFloats = KS * kKStride;
+  static constexpr int kVFloats = D * kVStride;
+  static constexpr int kLdsFloats = kKFloats + kVFloats;
+  static constexpr int kKChunks = KS * D / 4 / kThreads;         // float4 K chunks per thread
+  static constexpr int kVUnits = (KS / 4) * (D / 4) / kThreads;  // (4 keys, 4 columns) per thread
+  static_assert(kKChunks * kThreads * 4 == KS * D, "K tile split");
+  static_assert(kVUnits * kThreads * 16 == KS * D, "V tile split");
+  static_assert(4 * 32 * D + 2 * 4 * 32 <= kLdsFloats, "merge area");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fwd_f32_short_kernel(FwdArgs a, int n_qt, int total) {
+  using T = Short<D>;
+  constexpr int KW = T::KW, KS = T::KS;
+  __shared__ __attribute__((aligned(16))) float lds[T::kLdsFloats];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, grp = lane >> 5;
+  const int NQ = a.nq, NK = a.nk;
+
+  const int L = xcd_remap(blockIdx.x, total);
+  const int prob = L / n_qt;
+  int qt = L - prob * n_qt;
+  if (CAUSAL) qt = n_qt - 1 - qt;
+  const int q0 = qt * 32;
+  const int my_q = q0 + col;
+  const int off = a.causal_off;
+
+  const int64_t qhead = (int64_t)prob * NQ * D;
+  const int64_t kvhead = (int64_t)kv_head(a, prob) * NK * D;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc((const float*)a.q + qhead, NQ * D * 4);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc((const float*)a.k + kvhead, NK * D * 4);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc((const float*)a.v + kvhead, NK * D * 4);
+
+  f32x4 qf[D / 8];
+#pragma unroll
+  for (int j = 0; j < D / 8; ++j)
+    qf[j] = __builtin_bit_cast(f32x4, buf_load16(qr, (my_q * D + j * 8 + grp * 4) * 4));
+
+  // keys the workgroup's last row may see, and the keys of this wave's rows
+  int kstop = NK;
+  if (CAUSAL) kstop = max(0, min(kstop, q0 + 32 + off));
+  const int n_kv = (kstop + KS - 1) / KS;
+
+  const float c = a.scale_log2;
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = (f32x16){};
+
+  float* ks = lds;
+  float* vs = lds + T::kKFloats;
+  for (int t = 0; t < n_kv; ++t) {
+    const int k0 = t * KS;
+    {
+      f32x4 kst[T::kKChunks];
+      f32x4 vst[T::kVUnits][4];
+#pragma unroll
+      for (int i = 0; i < T::kKChunks; ++i) {
+        const int u = tid + i * kThreads;
+        const int row = u / (D / 4), cc = u % (D / 4);
+        kst[i] = __builtin_bit_cast(f32x4, buf_load16(kr, ((k0 + row) * D + cc * 4) * 4));
+      }
+#pragma unroll
+      for (int i = 0; i < T::kVUnits; ++i) {
+        const int u = tid + i * kThreads;
+        const int kq = u % (KS / 4), cc = u / (KS / 4);
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          vst[i][h] =
+              __builtin_bit_cast(f32x4, buf_load16(vr, ((k0 + 4 * kq + h) * D + cc * 4) * 4));
+      }
+      if (t > 0) __syncthreads();  // the previous step's LDS reads are done
+#pragma unroll
+      for (int i = 0; i < T::kKChunks; ++i) {
+        const int u = tid + i * kThreads;
+        const int row = u / (D / 4), cc = u % (D / 4);
+        *(f32x4*)(ks + row * T::kKStride + cc * 4) = kst[i];
+      }
+#pragma unroll
+      for (int i = 0; i < T::kVUnits; ++i) {
+        const int u = tid + i * kThreads;
+        const int kq = u % (KS / 4), cc = u / (KS / 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x4 w = {vst[i][0][e], vst[i][1][e], vst[i][2][e], vst[i][3][e]};
+          *(f32x4*)(vs + (cc * 4 + e) * T::kVStride + kq * 4) = w;
+        }
+      }
+      __syncthreads();
+    }
+
+    const int kw = k0 + wave * KW;  // this wave's first key of the step
+    if (kw < kstop && (!CAUSAL || kw <= q0 + 31 + off)) {
+      f32x16 s[KW / 32];
+#pragma unroll
+      for (int kb = 0; kb < KW / 32; ++kb) s[kb] = (f32x16){};
+#pragma unroll
+      for (int j = 0; j < D / 8; ++j)
+#pragma unroll
+        for (int kb = 0; kb < KW / 32; ++kb) {
+          const f32x4 ka =
+              *(const f32x4*)(ks + (wave * KW + kb * 32 + col) * T::kKStride + j * 8 + grp * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[kb] = mfma_f32(ka[e], qf[j][e], s[kb]);
+        }
+
+      if (kw + KW > NK || (CAUSAL && kw + KW - 1 > q0 + off)) {
+#pragma unroll
+        for (int kb = 0; kb < KW / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kw + kb * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
+            const bool masked = key >= NK || (CAUSAL && key > my_q + off);
+            s[kb][r] = masked ? kNegInf : s[kb][r];
+          }
+      }
+
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < KW / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = half_swap_max(mx);
+      const bool grow = (mx - m_run) * c > kRescaleLog2;
+      if (__any(grow)) {
+        const float alpha = grow ? fast_exp2((m_run - mx) * c) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        m_run = grow ? mx : m_run;
+      }
+      const float nmc = m_run == kNegInf ? 0.f : -m_run * c;
+#pragma unroll
+      for (int kb = 0; kb < KW / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s[kb][r], c, nmc));
+          s[kb][r] = p;
+          l_run += p;
+        }
+#pragma unroll
+      for (int kb = 0; kb < KW / 32; ++kb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const f32x4 va = *(const f32x4*)(vs + (db * 32 + col) * T::kVStride + wave * KW +
+                                             kb * 32 + g4 * 8 + grp * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oacc[db] = mfma_f32(va[e], s[kb][g4 * 4 + e], oacc[db]);
+          }
+    }
+  }
+
+  // Merge the four waves' partial results: O_w (unnormalised), l_w, m_w.
+  const float l_w = half_swap_sum(l_run);
+  __syncthreads();  // every wave is done with the K/V tiles
+  float* om = lds;                   // [wave][row][D]
+  float* st = lds + 4 * 32 * D;      // [wave][row]: m, then l
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jr = 0; jr < 4; ++jr)
+      *(f32x4*)(om + (wave * 32 + col) * D + db * 32 + 8 * jr + 4 * grp) =
+          (f32x4){oacc[db][4 * jr], oacc[db][4 * jr + 1], oacc[db][4 * jr + 2],
+                  oacc[db][4 * jr + 3]};
+  if (grp == 0) {
+    st[wave * 32 + col] = m_run;
+    st[4 * 32 + wave * 32 + col] = l_w;
+  }
+  __syncthreads();
+
+  // thread -> (row, 4-column group): D/4 groups per row, 32 rows
+  constexpr int kGroups = D / 4;
+#pragma unroll
+  for (int it = 0; it < 32 * kGroups / kThreads; ++it) {
+    const int u = tid + it * kThreads;
+    const int row = u / kGroups, cg = u % kGroups;
+    float m = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) m = fmaxf(m, st[w * 32 + row]);
+    float ltot = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = st[w * 32 + row];
+      const float wt = mw == kNegInf ? 0.f : fast_exp2((mw - m) * c);
+      ltot += wt * st[4 * 32 + w * 32 + row];
+      o += wt * *(const f32x4*)(om + (w * 32 + row) * D + cg * 4);
+    }
+    const int q = q0 + row;
+    if (q < NQ) {
+      const float inv = ltot > 0.f ? __builtin_amdgcn_rcpf(ltot) : 0.f;
+      *(f32x4*)((float*)a.o + ((int64_t)prob * NQ + q) * D + cg * 4) = o * inv;
+      if (cg == 0 && a.lse)
+        a.lse[(int64_t)prob * NQ + q] = ltot > 0.f ? (m * c + fast_log2(ltot)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_short(const FwdArgs& a, hipStream_t s) {
+  int n_qt = (a.nq + 31) / 32;
+  int total = (int)((int64_t)n_qt * a.problems);
+  FwdArgs args = a;
+  void* params[] = {&args, &n_qt, &total};
+  return hipLaunchKernel((const void*)&fwd_f32_short_kernel<D, CAUSAL>, dim3(total),
+                         dim3(kThreads), params, 0, s);
+}
+
 template <int D>
 hipError_t launch_d(bool causal, bool split, const FwdArgs& a, hipStream_t s) {
+  if (!split && (int64_t)((a.nq + kBM - 1) / kBM) * a.problems < kShortGrid)
+    return causal ? launch_short<D, true>(a, s) : launch_short<D, false>(a, s);
   if (causal) return split ? launch<D, true, true>(a, s) : launch<D, true, false>(a, s);
   return split ? launch<D, false, true>(a, s) : launch<D, false, false>(a, s);
 }

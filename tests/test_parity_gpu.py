@@ -83,6 +83,20 @@ def test_small_shapes(dtype, d, causal):
         assert_close(o, lse, o_ref, lse_ref, dtype, f"N={n}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_grid_sizes(d, causal):
+    # fp32 problems of fewer than 128 workgroups of 128 rows take the
+    # short-grid kernel (four waves splitting the keys of 32 rows); larger
+    # ones the 128-row kernel.  Both sides of the switch, ragged tails.
+    for B, H, N, seed in ((1, 1, 700, 1600), (2, 16, 1000, 1601), (1, 31, 513, 1602)):
+        w, (q, k, v) = small_case("f32", B, H, N, d, causal, seed=seed)
+        _note(f"f32 grid d={d} causal={causal} B={B} H={H} N={N}")
+        o, lse = run_gpu(q, k, v, w.scale, causal)
+        o_ref, lse_ref = oracle.fwd(q, k, v, w.scale, causal)
+        assert_close(o, lse, o_ref, lse_ref, "f32", f"B={B} H={H} N={N}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_logits_small(dtype, causal):
