@@ -199,11 +199,15 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
   const float c = a.scale_log2;
   float m_run[QB];  // running reference max of raw scores q.k, per query row
   float l_run[QB];  // this lane's share of the running sum of exp2 terms
+  // exp2 shift of the fast path, -m c (+inf while the row has no reference
+  // max: every weight is then inf and the tile takes the exact path)
+  float nmc[QB];
   f32x16 oacc[QB][D / 32];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = kNegInf;
     l_run[qb] = 0.f;
+    nmc[qb] = __builtin_inff();
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = (f32x16){};
   }
@@ -260,18 +264,18 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
       // P = exp2(S c - m c), rounded; the row sum adds the rounded pairs, so
       // the weights that multiply V sum exactly to l.
       uint32_t pk[QB][SB / 32][8];
-      auto exp_row = [&](int qb, const f32x16 (&sv)[SB / 32], float nmc) {
-        float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent sum chains
+      auto exp_row = [&](int qb, const f32x16 (&sv)[SB / 32], float shift) {
+        float ls[2];  // two independent sum chains, each started by its first pair
 #pragma unroll
         for (int kb = 0; kb < SB / 32; ++kb)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const float p0 = fast_exp2(fmaf(sv[kb][2 * j], c, nmc));
-            const float p1 = fast_exp2(fmaf(sv[kb][2 * j + 1], c, nmc));
+            const float p0 = fast_exp2(fmaf(sv[kb][2 * j], c, shift));
+            const float p1 = fast_exp2(fmaf(sv[kb][2 * j + 1], c, shift));
             pk[qb][kb][j] = HH::pack(p0, p1);
-            ls[j & 3] = HH::dot2(pk[qb][kb][j], ls[j & 3]);
+            ls[j & 1] = HH::dot2(pk[qb][kb][j], kb == 0 && j < 2 ? 0.f : ls[j & 1]);
           }
-        return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        return ls[0] + ls[1];
       };
       // Fast path: no row max.  P is formed against the current reference
       // max m, and the lane's partial sum bounds every weight it added; a sum
@@ -279,9 +283,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
       // rose well above m, or the row has no m yet: the shift is +inf and
       // the sum inf/NaN) take the exact max over both half-waves, rescale O
       // and l by exp2((m_old - m_new) c) and recompute P.
-      auto fast = [&](int qb, const f32x16 (&sv)[SB / 32]) {
-        return exp_row(qb, sv, m_run[qb] == kNegInf ? __builtin_inff() : -m_run[qb] * c);
-      };
+      auto fast = [&](int qb, const f32x16 (&sv)[SB / 32]) { return exp_row(qb, sv, nmc[qb]); };
       auto settle = [&](int qb, const f32x16 (&sv)[SB / 32], float lt) {
         if (__any(!(lt <= kFastSumLimit))) {
           float mx = tree_max<SB / 32>(sv);
@@ -292,7 +294,8 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
           m_run[qb] = m_new;
-          lt = exp_row(qb, sv, m_run[qb] == kNegInf ? 0.f : -m_run[qb] * c);
+          nmc[qb] = m_new == kNegInf ? __builtin_inff() : -m_new * c;
+          lt = exp_row(qb, sv, m_new == kNegInf ? 0.f : -m_new * c);
         }
         l_run[qb] += lt;
       };
