@@ -194,7 +194,7 @@ def main():
     import numpy as np
     import torch
     from exact_attention_13_amd import binding
-    from exact_attention_13_amd.inputs import WORKLOADS, make_inputs
+    from exact_attention_13_amd.inputs import WORKLOADS, make_inputs, make_upstream
 
     if args.copy_bytes:
         n = args.copy_bytes // 4
@@ -235,9 +235,7 @@ def main():
 
     splits, workspace = 1, None
     if args.which == "bwd":
-        g = np.random.default_rng(w.seed + 100)
-        dout = torch.from_numpy(g.standard_normal((w.B, w.H, w.N, w.d)).astype(np.float32)).to(
-            qd.dtype).to(dev)
+        dout = make_upstream(w, w.seed + 100).to(dev)
         if w.extended:
             binding.fwd_ex(qd, kd, vd, w.scale, w.causal, out=o, lse=lse, stream=stream)
         else:

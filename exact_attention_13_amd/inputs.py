@@ -130,6 +130,12 @@ def make_inputs(w: Workload):
                  for x in (q, k, v))
 
 
+def make_upstream(w: Workload, seed: int):
+    """A seeded upstream gradient dL/dO: [B, H, N, d] N(0, 1), rounded to the workload's dtype."""
+    x = np.random.default_rng(seed).standard_normal((w.B, w.H, w.N, w.d)).astype(np.float32)
+    return torch.from_numpy(x).to(TORCH_DTYPES[w.dtype])
+
+
 def sample_rows(w: Workload, count: int, seed: int = 12345) -> np.ndarray:
     """Deterministic sample of flat row indices (b*H + h)*N + i.
 

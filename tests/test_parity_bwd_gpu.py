@@ -28,7 +28,7 @@ import torch
 
 import oracle
 from exact_attention_13_amd import binding
-from exact_attention_13_amd.inputs import WORKLOADS, Workload, make_inputs, sample_rows
+from exact_attention_13_amd.inputs import WORKLOADS, Workload, make_inputs, make_upstream, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -43,9 +43,7 @@ def _note(msg):
 
 
 def upstream(w, seed):
-    g = np.random.default_rng(seed)
-    x = g.standard_normal((w.B, w.H, w.N, w.d)).astype(np.float32)
-    return torch.from_numpy(x).to(TORCH[w.dtype])
+    return make_upstream(w, seed)
 
 
 def run_bwd(w, q, k, v, dout):
