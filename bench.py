@@ -177,6 +177,9 @@ def main():
     ap.add_argument("--splits", type=int, default=None,
                     help="key ranges for fa_fwd_ex workloads (default: the workload's, "
                          "0 = the library's choice)")
+    ap.add_argument("--bwd-splits", type=int, default=None,
+                    help="head parts of the dK/dV pass for fa_bwd_ex workloads (default: "
+                         "the library's choice)")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="calls after the timed steps, each preceded by a 512 MiB read that "
                          "flushes the caches; "
@@ -246,10 +249,20 @@ def main():
         ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), dout.data_ptr(),
                 lse.data_ptr(), *(t.data_ptr() for t in grads), delta.data_ptr())
 
+        if w.extended:
+            splits = args.bwd_splits or binding.bwd_default_splits(
+                w.B, w.H, w.h_kv, w.N, w.n_kv, w.d, w.causal, dt_code)
+            need = binding.bwd_workspace_bytes(w.B, w.H, w.h_kv, w.N, w.n_kv, w.d, splits)
+            if need > 0:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() if workspace is not None else 0
+
         def step():
             if w.extended:
                 st = binding.fa_bwd_ex(*ptrs, w.B, w.H, w.h_kv, w.N, w.n_kv, w.d, w.scale,
-                                       w.causal, dt_code, stream.cuda_stream)
+                                       w.causal, dt_code, splits, ws_ptr, ws_bytes,
+                                       stream.cuda_stream)
             else:
                 st = binding.fa_bwd(*ptrs, w.B, w.H, w.N, w.d, w.scale, w.causal, dt_code,
                                     stream.cuda_stream)
@@ -338,7 +351,9 @@ def main():
         "data": f"synthetic: seeded ({w.dist}, numpy PCG64 seed {w.seed}) Q/K/V rounded to {w.dtype}",
         "config": {"workload": f"{w.name}: {w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} "
                                f"{'causal' if w.causal else 'non-causal'}" + (
-                                   f" H_kv={w.h_kv} N_kv={w.n_kv} splits={splits} (fa_fwd_ex)"
+                                   (f" H_kv={w.h_kv} N_kv={w.n_kv} head_parts={splits} (fa_bwd_ex)"
+                                    if args.which == "bwd" else
+                                    f" H_kv={w.h_kv} N_kv={w.n_kv} splits={splits} (fa_fwd_ex)")
                                    if w.extended else ""),
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "flops_per_step": flops, "parallelism": "single GPU"},
@@ -346,7 +361,9 @@ def main():
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "algorithmic_bytes": w.io_bytes,
                      "timed": (("fa_bwd_ex" if w.extended else "fa_bwd") +
-                               " call: row-dot, dK/dV and dQ kernels" if args.which == "bwd"
+                               (" call: row-dot, dK/dV, part-sum and dQ kernels" if splits > 1
+                                else " call: row-dot, dK/dV and dQ kernels")
+                               if args.which == "bwd"
                                else "fa_fwd_ex call: split kernel + combine kernel" if splits > 1
                                else "one forward kernel"),
                      "kernel_ms_avg": round(avg_kernel_ms, 5),

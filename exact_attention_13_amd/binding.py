@@ -23,8 +23,9 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD
 _DTYPE_CODES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
 
 # Every symbol include/fa.h declares.
-EXPORTED = ("fa_bwd", "fa_bwd_ex", "fa_fwd", "fa_fwd_ex", "fa_fwd_ex_default_splits",
-            "fa_fwd_ex_workspace_bytes", "fa_lse_combine", "fa_strerror", "fa_version")
+EXPORTED = ("fa_bwd", "fa_bwd_ex", "fa_bwd_ex_default_splits", "fa_bwd_ex_workspace_bytes",
+            "fa_fwd", "fa_fwd_ex", "fa_fwd_ex_default_splits", "fa_fwd_ex_workspace_bytes",
+            "fa_lse_combine", "fa_strerror", "fa_version")
 
 _lib = None
 
@@ -66,7 +67,12 @@ def load() -> ctypes.CDLL:
             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         lib.fa_bwd_ex.restype = ctypes.c_int
         lib.fa_bwd_ex.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 6 + [
-            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_void_p]
+        lib.fa_bwd_ex_workspace_bytes.restype = ctypes.c_int64
+        lib.fa_bwd_ex_workspace_bytes.argtypes = [ctypes.c_int64] * 7
+        lib.fa_bwd_ex_default_splits.restype = ctypes.c_int64
+        lib.fa_bwd_ex_default_splits.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_int]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_strerror.argtypes = [ctypes.c_int]
         lib.fa_version.restype = ctypes.c_int
@@ -248,23 +254,37 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, 
 
 
 def fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, H_kv, N_q, N_kv, d, scale, causal,
-              dtype, stream) -> int:
+              dtype, num_splits, workspace, workspace_bytes, stream) -> int:
     """Raw C call with integer pointers; returns the fa_status code."""
     return int(load().fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, int(B), int(H),
                                 int(H_kv), int(N_q), int(N_kv), int(d), float(scale),
-                                int(bool(causal)), int(dtype), stream))
+                                int(bool(causal)), int(dtype), int(num_splits), workspace,
+                                int(workspace_bytes), stream))
+
+
+def bwd_workspace_bytes(B, H, H_kv, N_q, N_kv, d, num_splits) -> int:
+    return int(load().fa_bwd_ex_workspace_bytes(int(B), int(H), int(H_kv), int(N_q), int(N_kv),
+                                                int(d), int(num_splits)))
+
+
+def bwd_default_splits(B, H, H_kv, N_q, N_kv, d, causal, dtype) -> int:
+    return int(load().fa_bwd_ex_default_splits(int(B), int(H), int(H_kv), int(N_q), int(N_kv),
+                                               int(d), int(bool(causal)), int(dtype)))
 
 
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         lse: torch.Tensor, dout: torch.Tensor, scale: float | None = None,
-        causal: bool = False, stream: torch.cuda.Stream | None = None):
+        causal: bool = False, stream: torch.cuda.Stream | None = None,
+        num_splits: int | None = None):
     """Gradients (dq, dk, dv) of the forward pass for fp32/bf16/fp16 tensors.
 
     q, o, dout: [B, H, N_q, d]; k, v: [B, H_kv, N_kv, d] with H_kv dividing H
     (``fa_bwd`` when the shapes are all equal, else ``fa_bwd_ex``).  ``o`` and
     ``lse`` are what ``fwd`` / ``fwd_ex`` returned for the same inputs.
-    Returns ``(dq, dk, dv)`` shaped like q, k, v; the row dot products
-    D = rowsum(dO * O) go to a scratch tensor allocated here.
+    ``num_splits`` is the number of parts each group's query heads are cut
+    into for dK/dV (None: ``fa_bwd_ex_default_splits``).  Returns
+    ``(dq, dk, dv)`` shaped like q, k, v; the row dot products
+    D = rowsum(dO * O) and the parts' workspace are allocated here.
     """
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or not (q.shape == o.shape == dout.shape):
         raise ValueError("q, o, dout must be [B, H, N_q, d] and k, v [B, H_kv, N_kv, d]")
@@ -287,11 +307,16 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         stream = torch.cuda.current_stream(q.device)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr())
-    if k.shape == q.shape:
-        st = fa_bwd(*ptrs, B, H, Nq, d, scale, causal, _DTYPE_CODES[q.dtype], stream.cuda_stream)
+    code = _DTYPE_CODES[q.dtype]
+    if k.shape == q.shape and num_splits is None:
+        st = fa_bwd(*ptrs, B, H, Nq, d, scale, causal, code, stream.cuda_stream)
     else:
-        st = fa_bwd_ex(*ptrs, B, H, Hkv, Nq, Nk, d, scale, causal, _DTYPE_CODES[q.dtype],
-                       stream.cuda_stream)
+        if num_splits is None:
+            num_splits = bwd_default_splits(B, H, Hkv, Nq, Nk, d, causal, code)
+        nbytes = bwd_workspace_bytes(B, H, Hkv, Nq, Nk, d, num_splits) if Hkv > 0 else 0
+        ws = torch.empty(max(nbytes, 0), dtype=torch.uint8, device=q.device) if nbytes > 0 else None
+        st = fa_bwd_ex(*ptrs, B, H, Hkv, Nq, Nk, d, scale, causal, code, num_splits,
+                       ws.data_ptr() if ws is not None else None, nbytes, stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st)
     return dq, dk, dv

@@ -28,6 +28,14 @@ struct BwdArgs {
   int off;         // causal alignment N_kv - N_q: key j is visible to row i when j <= i + off
   float scale;     // multiplier of q.k
   float scale_log2;  // scale * log2(e)
+  // Parts a group's query heads are divided into for dK/dV (1: one
+  // workgroup per key tile sums the whole group and writes dK, dV).  With
+  // hsplit > 1 each part writes fp32 partial sums, unscaled, to
+  // dk_part / dv_part ([hsplit][B*H_kv][N_kv][d]) and a reduce kernel adds
+  // the parts in order.
+  int hsplit;
+  float* dk_part;
+  float* dv_part;
 };
 
 // Backward pass (bf16/fp16): delta, then dK/dV, then dQ on stream s.
@@ -37,7 +45,9 @@ hipError_t launch_bwd_h16(bool bf16, int d, bool causal, const BwdArgs& a, const
 hipError_t launch_bwd_f32(int d, bool causal, const BwdArgs& a, const void* o, float* delta,
                           hipStream_t s);
 // Largest workgroup count of the backward launches (dK/dV over the K/V heads'
-// key tiles, dQ over the query heads' row tiles).
-int64_t bwd_grid_blocks(int64_t bh, int64_t bkv, int64_t nq, int64_t nk);
+// key tiles and head parts, dQ over the query heads' row tiles).
+int64_t bwd_grid_blocks(int64_t bh, int64_t bkv, int64_t nq, int64_t nk, int64_t hsplit);
+// Workgroups of the dK/dV launch without head parts (B*H_kv key-tile rows).
+int64_t bwd_dkdv_blocks(int64_t bkv, int64_t nk);
 
 }  // namespace fa_impl

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void bwd_delta_f32_kernel(const float* __restr
 // its group in registers.
 // ---------------------------------------------------------------------------
 template <bool CAUSAL, int D>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a, int n_kt, int total) {
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
   using T = Tile32<D>;
   constexpr int kStage = 2 * (T::kRowFloats + T::kTFloats);  // Qr, Qt, dOr, dOt
   constexpr int kPer = 2 * T::kUnits / kThreads;             // Q and dO units per thread
@@ -132,13 +132,17 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a, int n
   const int col = lane & 31, grp = lane >> 5;
   const int nq = a.nq, nk = a.nk, off = a.off;
 
-  const int L = xcd_remap(blockIdx.x, total);
-  const int bkv = L / n_kt;
-  const int kt = L - bkv * n_kt;
+  // workgroup -> (key tile, K/V head, part of the group's query heads), key
+  // tiles outermost (as in the bf16/fp16 kernel)
+  const int units = a.bkv * a.hsplit;
+  const int kt = blockIdx.x / units;
+  const int unit = blockIdx.x - kt * units;
+  const int bkv = unit / a.hsplit, sp = unit - bkv * a.hsplit;
   const int k0 = kt * kRows;
   const int kw0 = k0 + wave * 32;
   const int b = bkv / a.hkv;
-  const int bh0 = b * a.hq + (bkv - b * a.hkv) * a.hgrp;
+  const int h_lo = sp * a.hgrp / a.hsplit, h_hi = (sp + 1) * a.hgrp / a.hsplit;
+  const int bh0 = b * a.hq + (bkv - b * a.hkv) * a.hgrp + h_lo;
 
   const int64_t kvhead = (int64_t)bkv * nk * D;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc((const float*)a.k + kvhead, nk * D * 4);
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a, int n
   const int n_qt = (nq + kBT - 1) / kBT;
   const int qt_begin = CAUSAL ? max(0, (k0 - off) / kBT) : 0;
   const int n_iter = max(0, n_qt - qt_begin);
-  const int total_it = n_iter * a.hgrp;
+  const int total_it = n_iter * (h_hi - h_lo);
 
   // Units [0, kUnits) are Q's, [kUnits, 2 kUnits) dO's; whole waves take one
   // kind, so the buffer resource is wave-uniform.
@@ -280,15 +284,18 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a, int n
   // dK = scale (Q^T dS)^T, dV = (dO^T P)^T; lane holds key `key`, register r
   // the column db*32 + 8(r/4) + 4g + r%4.
   if (key < nk) {
-    float* dkg = (float*)a.dk + kvhead + (int64_t)key * D;
-    float* dvg = (float*)a.dv + kvhead + (int64_t)key * D;
+    const bool parts = a.hsplit > 1;  // this part's sums, unscaled, for the reduce kernel
+    const int64_t prow = ((int64_t)sp * a.bkv + bkv) * nk + key;
+    float* dkg = parts ? a.dk_part + prow * D : (float*)a.dk + kvhead + (int64_t)key * D;
+    float* dvg = parts ? a.dv_part + prow * D : (float*)a.dv + kvhead + (int64_t)key * D;
+    const float ks = parts ? 1.f : a.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int jr = 0; jr < 4; ++jr) {
         const int d0 = db * 32 + 8 * jr + 4 * grp;
-        const f32x4 wk = {dkT[db][4 * jr] * a.scale, dkT[db][4 * jr + 1] * a.scale,
-                          dkT[db][4 * jr + 2] * a.scale, dkT[db][4 * jr + 3] * a.scale};
+        const f32x4 wk = {dkT[db][4 * jr] * ks, dkT[db][4 * jr + 1] * ks,
+                          dkT[db][4 * jr + 2] * ks, dkT[db][4 * jr + 3] * ks};
         const f32x4 wv = {dvT[db][4 * jr], dvT[db][4 * jr + 1], dvT[db][4 * jr + 2],
                           dvT[db][4 * jr + 3]};
         *(f32x4*)(dkg + d0) = wk;
@@ -453,6 +460,25 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(BwdArgs a, int n_q
   }
 }
 
+// dK, dV from the parts of split head groups (sum in part order, dK times
+// scale), fp32.
+__global__ __launch_bounds__(256) void bwd_part_sum_f32_kernel(const float* __restrict__ dk_part,
+                                                               const float* __restrict__ dv_part,
+                                                               int parts, int64_t quads,
+                                                               float scale, float* __restrict__ dk,
+                                                               float* __restrict__ dv) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= quads) return;
+  f32x4 sk = *(const f32x4*)(dk_part + i * 4);
+  f32x4 sv = *(const f32x4*)(dv_part + i * 4);
+  for (int p = 1; p < parts; ++p) {
+    sk += *(const f32x4*)(dk_part + (p * quads + i) * 4);
+    sv += *(const f32x4*)(dv_part + (p * quads + i) * 4);
+  }
+  *(f32x4*)(dk + i * 4) = sk * scale;
+  *(f32x4*)(dv + i * 4) = sv;
+}
+
 template <bool CAUSAL, int D>
 hipError_t launch(const BwdArgs& a, const void* o, float* delta, hipStream_t s) {
   BwdArgs args = a;
@@ -470,12 +496,25 @@ hipError_t launch(const BwdArgs& a, const void* o, float* delta, hipStream_t s) 
     if (e != hipSuccess) return e;
   }
   int n_kt = (a.nk + kRows - 1) / kRows;
-  int total_kv = (int)((int64_t)n_kt * a.bkv);
+  int total_kv = (int)((int64_t)n_kt * a.bkv * a.hsplit);
   if (total_kv > 0) {
-    void* p1[] = {&args, &n_kt, &total_kv};
+    void* p1[] = {&args};
     e = hipLaunchKernel((const void*)&bwd_dkdv_f32_kernel<CAUSAL, D>, dim3(total_kv),
                         dim3(kThreads), p1, 0, s);
     if (e != hipSuccess) return e;
+    if (a.hsplit > 1) {
+      const float* kp = a.dk_part;
+      const float* vp = a.dv_part;
+      int parts = a.hsplit;
+      int64_t quads = (int64_t)a.bkv * a.nk * (D / 4);
+      float scale = a.scale;
+      float* dkp = (float*)a.dk;
+      float* dvp = (float*)a.dv;
+      void* p3[] = {&kp, &vp, &parts, &quads, &scale, &dkp, &dvp};
+      e = hipLaunchKernel((const void*)&bwd_part_sum_f32_kernel,
+                          dim3((unsigned)((quads + 255) / 256)), dim3(256), p3, 0, s);
+      if (e != hipSuccess) return e;
+    }
   }
   int n_qt = (a.nq + kRows - 1) / kRows;
   int total_q = (int)((int64_t)n_qt * a.bh);

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 // and sums their contributions in its registers (no atomics: deterministic).
 // ---------------------------------------------------------------------------
 template <bool BF16, bool CAUSAL, int D>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<D>))) void bwd_dkdv_kernel(BwdArgs a, int n_kt, int total) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<D>))) void bwd_dkdv_kernel(BwdArgs a) {
   using HH = Half<BF16>;
   using T = BwdTile<D>;
   constexpr int kStage = 2 * (T::kRowElems + T::kTElems);  // Qr, Qt, dOr, dOt
@@ -143,13 +143,20 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
   const int col = lane & 31, grp = lane >> 5;
   const int nq = a.nq, nk = a.nk, off = a.off;
 
-  const int L = xcd_remap(blockIdx.x, total);
-  const int bkv = L / n_kt;
-  const int kt = L - bkv * n_kt;  // causal: low key tiles see the most queries and go first
+  // Workgroup -> (key tile, K/V head, part of the group's query heads), key
+  // tiles outermost: under causal masking the low key tiles see the most
+  // queries, and dispatching them first lets the light ones fill in behind.
+  // Consecutive workgroups (same key tile) land on consecutive XCDs, so with
+  // a multiple of 8 (head, part) units each unit stays on one XCD.
+  const int units = a.bkv * a.hsplit;
+  const int kt = blockIdx.x / units;
+  const int unit = blockIdx.x - kt * units;
+  const int bkv = unit / a.hsplit, sp = unit - bkv * a.hsplit;
   const int k0 = kt * kBwdRows;
   const int kw0 = k0 + wave * 32;  // this wave's first key
   const int b = bkv / a.hkv;
-  const int bh0 = b * a.hq + (bkv - b * a.hkv) * a.hgrp;  // first query head of the group
+  const int h_lo = sp * a.hgrp / a.hsplit, h_hi = (sp + 1) * a.hgrp / a.hsplit;
+  const int bh0 = b * a.hq + (bkv - b * a.hkv) * a.hgrp + h_lo;  // first query head of the part
 
   const int64_t kvhead = (int64_t)bkv * nk * D;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc((const uint16_t*)a.k + kvhead, nk * D * 2);
@@ -170,7 +177,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
   const int n_qt = (nq + kBT - 1) / kBT;
   const int qt_begin = CAUSAL ? max(0, (k0 - off) / kBT) : 0;
   const int n_iter = max(0, n_qt - qt_begin);
-  const int total_it = n_iter * a.hgrp;
+  const int total_it = n_iter * (h_hi - h_lo);
 
   // Staging of one query tile: (row pair, 8 columns) units of Q then dO,
   // plus the tile's 32 lse and 32 D values.  Part i of the units goes through
@@ -349,7 +356,24 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 
   // dK = scale * (Q^T dS)^T, dV = (dO^T P)^T; lane holds key kw0 + col.
   const int key = kw0 + col;
-  if (key < nk) {
+  if (a.hsplit > 1) {
+    // this part's sums, fp32 and unscaled, for the reduce kernel
+    if (key < nk) {
+      const int64_t row = ((int64_t)sp * a.bkv + bkv) * nk + key;
+      float* dkp = a.dk_part + row * D;
+      float* dvp = a.dv_part + row * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d0 = db * 32 + 8 * j + 4 * grp;
+          *(f32x4*)(dkp + d0) = (f32x4){dkT[db][4 * j], dkT[db][4 * j + 1], dkT[db][4 * j + 2],
+                                        dkT[db][4 * j + 3]};
+          *(f32x4*)(dvp + d0) = (f32x4){dvT[db][4 * j], dvT[db][4 * j + 1], dvT[db][4 * j + 2],
+                                        dvT[db][4 * j + 3]};
+        }
+    }
+  } else if (key < nk) {
     uint16_t* dkg = (uint16_t*)a.dk + kvhead + (int64_t)key * D;
     uint16_t* dvg = (uint16_t*)a.dv + kvhead + (int64_t)key * D;
 #pragma unroll
@@ -537,6 +561,30 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
   }
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV from the parts of split head groups: the sum over parts in part
+// order (deterministic), dK times scale, rounded to the I/O type.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_part_sum_kernel(const float* __restrict__ dk_part,
+                                                           const float* __restrict__ dv_part,
+                                                           int parts, int64_t quads, float scale,
+                                                           uint16_t* __restrict__ dk,
+                                                           uint16_t* __restrict__ dv) {
+  using HH = Half<BF16>;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 4-float group
+  if (i >= quads) return;
+  f32x4 sk = *(const f32x4*)(dk_part + i * 4);
+  f32x4 sv = *(const f32x4*)(dv_part + i * 4);
+  for (int p = 1; p < parts; ++p) {
+    sk += *(const f32x4*)(dk_part + (p * quads + i) * 4);
+    sv += *(const f32x4*)(dv_part + (p * quads + i) * 4);
+  }
+  *(u32x2*)(dk + i * 4) = (u32x2){HH::pack(sk[0] * scale, sk[1] * scale),
+                                  HH::pack(sk[2] * scale, sk[3] * scale)};
+  *(u32x2*)(dv + i * 4) = (u32x2){HH::pack(sv[0], sv[1]), HH::pack(sv[2], sv[3])};
+}
+
 template <bool BF16, bool CAUSAL, int D>
 hipError_t launch_bwd(const BwdArgs& a, const void* o, float* delta, hipStream_t s) {
   BwdArgs args = a;
@@ -554,14 +602,28 @@ hipError_t launch_bwd(const BwdArgs& a, const void* o, float* delta, hipStream_t
                         p0, 0, s);
     if (e != hipSuccess) return e;
   }
-  // dK, dV over the K/V heads' key tiles (zero when there are no queries)
+  // dK, dV over the K/V heads' key tiles and head parts (zero when there are
+  // no queries), then the sum of the parts
   int n_kt = (a.nk + kBwdRows - 1) / kBwdRows;
-  int total_kv = (int)((int64_t)n_kt * a.bkv);
+  int total_kv = (int)((int64_t)n_kt * a.bkv * a.hsplit);
   if (total_kv > 0) {
-    void* p1[] = {&args, &n_kt, &total_kv};
+    void* p1[] = {&args};
     e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<BF16, CAUSAL, D>, dim3(total_kv),
                         dim3(kBwdThreads), p1, 0, s);
     if (e != hipSuccess) return e;
+    if (a.hsplit > 1) {
+      const float* kp = a.dk_part;
+      const float* vp = a.dv_part;
+      int parts = a.hsplit;
+      int64_t quads = (int64_t)a.bkv * a.nk * (D / 4);
+      float scale = a.scale;
+      uint16_t* dkp = (uint16_t*)a.dk;
+      uint16_t* dvp = (uint16_t*)a.dv;
+      void* p3[] = {&kp, &vp, &parts, &quads, &scale, &dkp, &dvp};
+      e = hipLaunchKernel((const void*)&bwd_part_sum_kernel<BF16>,
+                          dim3((unsigned)((quads + 255) / 256)), dim3(256), p3, 0, s);
+      if (e != hipSuccess) return e;
+    }
   }
   // dQ over the query heads' row tiles (zero when there are no keys)
   int n_qt = (a.nq + kBwdRows - 1) / kBwdRows;
@@ -592,10 +654,14 @@ hipError_t launch_bwd_h16(bool bf16, int d, bool causal, const BwdArgs& a, const
                  : launch_d<false, 128>(causal, a, o, delta, s);
 }
 
-int64_t bwd_grid_blocks(int64_t bh, int64_t bkv, int64_t nq, int64_t nk) {
-  const int64_t kv = (nk + kBwdRows - 1) / kBwdRows * bkv;
+int64_t bwd_grid_blocks(int64_t bh, int64_t bkv, int64_t nq, int64_t nk, int64_t hsplit) {
+  const int64_t kv = (nk + kBwdRows - 1) / kBwdRows * bkv * hsplit;
   const int64_t q = (nq + kBwdRows - 1) / kBwdRows * bh;
-  return kv > q ? kv : q;
+  const int64_t sum = hsplit > 1 ? (bkv * nk * 32 + 255) / 256 : 0;  // part-sum grid, d <= 128
+  const int64_t m = kv > q ? kv : q;
+  return m > sum ? m : sum;
 }
+
+int64_t bwd_dkdv_blocks(int64_t bkv, int64_t nk) { return (nk + kBwdRows - 1) / kBwdRows * bkv; }
 
 }  // namespace fa_impl

@@ -227,17 +227,49 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
  *                  when j <= i + N_kv - N_q.
  * Every query head of a group contributes to its K/V head: dK and dV are the
  * sums of the per-query-head gradients (chain rule through the shared K/V
- * head), formed in registers by one workgroup per (K/V head, 128 keys), so
- * results stay bitwise reproducible.  A query row that sees no key gets a
- * zero dQ row; with N_q = 0, dk and dv are zero-filled; with N_kv = 0, dq is
- * zero-filled.  Pointers of an empty side (q, o, dout, lse, dq, delta when
- * N_q = 0; k, v, dk, dv when N_kv = 0) may be NULL.  Validation and
- * alignment as fa_bwd, plus FA_ERR_SHAPE when H_kv does not divide H.
+ * head).  With num_splits = 1 one workgroup per (K/V head, 128 keys) forms
+ * the whole sum in registers.  With num_splits > 1 the group's query heads
+ * are cut into min(num_splits, H / H_kv) contiguous parts of near-equal
+ * size; each part's workgroups write fp32 partial sums to `workspace` and a
+ * second kernel adds the parts in part order, so the grid is larger (this
+ * evens out the causal mask's uneven work per key tile) and results stay
+ * bitwise reproducible for a given num_splits.  fa_bwd_ex_default_splits
+ * gives a count suited to 256 compute units.  A query row that sees no key
+ * gets a zero dQ row; with N_q = 0, dk and dv are zero-filled; with
+ * N_kv = 0, dq is zero-filled.  Pointers of an empty side (q, o, dout, lse,
+ * dq, delta when N_q = 0; k, v, dk, dv when N_kv = 0) may be NULL.
+ *
+ * workspace        device memory of at least
+ *                  fa_bwd_ex_workspace_bytes(B, H, H_kv, N_q, N_kv, d,
+ *                  num_splits) bytes, 16-byte aligned, caller-owned, not
+ *                  overlapping any other argument; contents on entry do not
+ *                  matter.  May be NULL when that size is 0 (one part).  Two
+ *                  calls that share a workspace must be ordered.
+ * Validation and alignment as fa_bwd, plus FA_ERR_SHAPE when H_kv does not
+ * divide H, FA_ERR_WORKSPACE when num_splits < 1 or, with more than one
+ * part, the workspace is NULL, short or misaligned, and FA_ERR_ALIAS when it
+ * overlaps another argument.
  */
 fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B,
                     int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t d, float scale,
-                    int causal, fa_dtype dtype, void* stream);
+                    int causal, fa_dtype dtype, int64_t num_splits, void* workspace,
+                    int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_bwd_ex needs for `num_splits` head parts:
+ * 2 * parts * B * H_kv * N_kv * d * 4 with parts = min(num_splits, H / H_kv),
+ * 0 when the call runs in one part (num_splits <= 1, H = H_kv, N_q = 0 or
+ * N_kv = 0) or the sizes are invalid, -1 when the size overflows int64. */
+int64_t fa_bwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv,
+                                  int64_t d, int64_t num_splits);
+
+/* A head-part count for fa_bwd_ex: 1 without grouped heads or when the
+ * unsplit dK/dV grid already holds enough workgroups for MI355X's 256
+ * compute units (two per workgroup slot without a mask, four under the
+ * causal mask, whose work per key tile is uneven); otherwise enough parts to
+ * reach that, at most H / H_kv (1 when the arguments are invalid). */
+int64_t fa_bwd_ex_default_splits(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv,
+                                 int64_t d, int causal, fa_dtype dtype);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(fa_status s);

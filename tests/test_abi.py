@@ -246,7 +246,9 @@ def test_bwd_empty_is_a_noop(kw):
 
 BWDX_ARGS = dict(q=Q, k=K, v=V, o=OB, dout=GB, lse=L, dq=DQ, dk=DK, dv=DV, delta=DL, B=1, H=4,
                  H_kv=2, N_q=100, N_kv=300, d=128, scale=0.088, causal=1, dtype=libfa.FA_F16,
-                 stream=None)
+                 num_splits=1, workspace=None, workspace_bytes=0, stream=None)
+# two head parts of the [1, 2, 300, 128] K/V heads: fp32 partial dK and dV
+BWDX_WS_BYTES = 2 * 2 * 1 * 2 * 300 * 128 * 4
 
 
 def call_bwd_ex(**kw):
@@ -254,7 +256,13 @@ def call_bwd_ex(**kw):
     a.update(kw)
     return libfa.fa_bwd_ex(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
                            a["dv"], a["delta"], a["B"], a["H"], a["H_kv"], a["N_q"], a["N_kv"],
-                           a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+                           a["d"], a["scale"], a["causal"], a["dtype"], a["num_splits"],
+                           a["workspace"], a["workspace_bytes"], a["stream"])
+
+
+def split2(**kw):
+    """Arguments of a two-part call with a workspace of the right size."""
+    return {**dict(num_splits=2, workspace=WS, workspace_bytes=BWDX_WS_BYTES), **kw}
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -269,9 +277,51 @@ def call_bwd_ex(**kw):
     # dK/dV are [B, H_kv, N_kv, d] (300 * 128 * 2 * 2 bytes), dQ [B, H, N_q, d]
     (dict(dk=K + 150_000), 7), (dict(dv=DK + 153_584), 7), (dict(dq=OB + 102_384), 7),
     (dict(delta=L + 1596), 7),
+    # head parts: count, workspace presence, size, alignment and overlap
+    (dict(num_splits=0), 9), (dict(num_splits=-3), 9), (dict(num_splits=0, H=2, H_kv=2), 9),
+    (dict(num_splits=2), 9), (split2(workspace=None), 9),
+    (split2(workspace_bytes=BWDX_WS_BYTES - 1), 9), (split2(workspace=WS + 8), 9),
+    # num_splits beyond the group size of 2 still needs only two parts
+    (dict(num_splits=9, workspace=WS, workspace_bytes=BWDX_WS_BYTES - 16), 9),
+    (split2(workspace=DK - 1024), 7), (split2(workspace=Q + 16), 7),
+    (split2(workspace=L + 512), 7), (split2(workspace=DL - BWDX_WS_BYTES + 16), 7),
+    # the workspace is checked after the other arguments
+    (split2(workspace=None, d=96), 3), (split2(workspace=None, dk=DK + 8), 6),
 ])
 def test_bwd_ex_rejects(kw, status):
     assert call_bwd_ex(**kw) == status
+
+
+def test_bwd_workspace_bytes():
+    # 2 * parts * B * H_kv * N_kv * d * 4 with parts = min(num_splits, H / H_kv)
+    assert libfa.bwd_workspace_bytes(1, 4, 2, 100, 300, 128, 2) == BWDX_WS_BYTES
+    assert libfa.bwd_workspace_bytes(1, 4, 2, 100, 300, 128, 9) == BWDX_WS_BYTES
+    assert libfa.bwd_workspace_bytes(2, 32, 8, 50, 1000, 64, 3) == 2 * 3 * 2 * 8 * 1000 * 64 * 4
+    # one part: no workspace
+    assert libfa.bwd_workspace_bytes(1, 4, 2, 100, 300, 128, 1) == 0
+    assert libfa.bwd_workspace_bytes(1, 4, 4, 100, 300, 128, 8) == 0
+    assert libfa.bwd_workspace_bytes(1, 4, 2, 0, 300, 128, 2) == 0
+    assert libfa.bwd_workspace_bytes(1, 4, 2, 100, 0, 128, 2) == 0
+    # invalid sizes give 0, overflow -1
+    assert libfa.bwd_workspace_bytes(1, 4, 2, 100, 300, 96, 2) == 0
+    assert libfa.bwd_workspace_bytes(-1, 4, 2, 100, 300, 128, 2) == 0
+    assert libfa.bwd_workspace_bytes(1 << 40, 4, 2, 1, 1 << 30, 128, 2) == -1
+
+
+def test_bwd_default_splits():
+    bf16, f32 = libfa.FA_BF16, libfa.FA_F32
+    # no grouping, or a full grid without a mask: one part
+    assert libfa.bwd_default_splits(1, 16, 16, 16384, 16384, 64, True, bf16) == 1
+    assert libfa.bwd_default_splits(8, 32, 8, 4096, 4096, 128, False, bf16) == 1
+    # a causal mask, or a short grid, asks for parts, at most the group size
+    s = libfa.bwd_default_splits(2, 32, 8, 8192, 8192, 128, True, bf16)
+    assert 1 < s <= 4
+    assert libfa.bwd_default_splits(1, 8, 1, 1024, 1024, 64, False, f32) == 8
+    assert libfa.bwd_default_splits(1, 8, 2, 4096, 4096, 64, False, f32) == 4
+    # invalid arguments: 1
+    assert libfa.bwd_default_splits(1, 4, 3, 100, 100, 64, True, bf16) == 1
+    assert libfa.bwd_default_splits(1, 4, 2, 100, 100, 96, True, bf16) == 1
+    assert libfa.bwd_default_splits(1, 4, 2, 0, 100, 64, True, bf16) == 1
 
 
 @pytest.mark.parametrize("kw", [

@@ -163,10 +163,12 @@ def test_bwd_workload_sampled_rows_and_invariants(name):
 # Grouped K/V heads and N_q != N_kv (fa_bwd_ex)
 # --------------------------------------------------------------------------
 
-def run_bwd_ex(w, q, k, v, dout, splits=1):
+def run_bwd_ex(w, q, k, v, dout, splits=1, parts=None):
+    # splits: the forward's key ranges; parts: the backward's head parts
+    # (None: the library's default)
     qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dout))
     o, lse = binding.fwd_ex(qd, kd, vd, w.scale, w.causal, num_splits=splits)
-    dq, dk, dv = binding.bwd(qd, kd, vd, o, lse, gd, w.scale, w.causal)
+    dq, dk, dv = binding.bwd(qd, kd, vd, o, lse, gd, w.scale, w.causal, num_splits=parts)
     torch.cuda.synchronize()
     return dq.cpu(), dk.cpu(), dv.cpu()
 
@@ -177,16 +179,21 @@ GROUPED = [  # (H, H_kv, N_q, N_kv)
 ]
 
 
+# Head parts per group: 1 (one workgroup sums the whole group) and 3, which
+# cuts groups of 4 into parts of 1, 1, 2 heads and groups of 8 into 2, 3, 3
+# (groups of 2 into 2 parts).
+@pytest.mark.parametrize("parts", [1, 3])
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_grouped_shapes(dtype, d, causal):
+def test_bwd_grouped_shapes(dtype, d, causal, parts):
     for i, (H, Hkv, Nq, Nk) in enumerate(GROUPED):
         w = Workload("case", dtype, 2 if i % 2 else 1, H, Nq, d, causal, 1700 + i, "normal", Hkv, Nk)
         q, k, v = make_inputs(w)
         dout = upstream(w, 1800 + i)
-        _note(f"bwd_ex {dtype} d={d} causal={causal} B={w.B} H={H} H_kv={Hkv} N_q={Nq} N_kv={Nk}")
-        dq, dk, dv = run_bwd_ex(w, q, k, v, dout)
+        _note(f"bwd_ex {dtype} d={d} causal={causal} B={w.B} H={H} H_kv={Hkv} N_q={Nq} "
+              f"N_kv={Nk} parts={parts}")
+        dq, dk, dv = run_bwd_ex(w, q, k, v, dout, parts=parts)
         rq, rk, rv = oracle.bwd(q, k, v, dout, w.scale, causal)
         for got, ref, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
             assert_grad_close(got, ref, dtype, f"{(H, Hkv, Nq, Nk)} {name}")
@@ -213,11 +220,15 @@ def test_bwd_ex_empty_sides_are_zero_filled():
     dk = torch.full_like(kv, float("nan"))
     dv = torch.full_like(kv, float("nan"))
     _note("bwd_ex N_q = 0")
-    s = binding.fa_bwd_ex(0, kv.data_ptr(), kv.data_ptr(), 0, 0, 0, 0, dk.data_ptr(),
-                          dv.data_ptr(), 0, 1, 4, 2, 0, 70, 64, 0.125, True, binding.FA_BF16, st)
-    assert s == 0
-    torch.cuda.synchronize()
-    assert torch.all(dk == 0) and torch.all(dv == 0)
+    for parts in (1, 2):  # no queries: one part whatever num_splits asks, no workspace
+        dk.fill_(float("nan"))
+        dv.fill_(float("nan"))
+        s = binding.fa_bwd_ex(0, kv.data_ptr(), kv.data_ptr(), 0, 0, 0, 0, dk.data_ptr(),
+                              dv.data_ptr(), 0, 1, 4, 2, 0, 70, 64, 0.125, True, binding.FA_BF16,
+                              parts, None, 0, st)
+        assert s == 0
+        torch.cuda.synchronize()
+        assert torch.all(dk == 0) and torch.all(dv == 0)
     q = torch.randn((1, 4, 50, 64), device=DEV).to(torch.bfloat16)
     o, g = torch.zeros_like(q), torch.randn_like(q)
     lse = torch.full((1, 4, 50), float("-inf"), device=DEV)
@@ -226,7 +237,7 @@ def test_bwd_ex_empty_sides_are_zero_filled():
     _note("bwd_ex N_kv = 0")
     s = binding.fa_bwd_ex(q.data_ptr(), 0, 0, o.data_ptr(), g.data_ptr(), lse.data_ptr(),
                           dq.data_ptr(), 0, 0, delta.data_ptr(), 1, 4, 2, 50, 0, 64, 0.125, False,
-                          binding.FA_BF16, st)
+                          binding.FA_BF16, 2, None, 0, st)
     assert s == 0
     torch.cuda.synchronize()
     assert torch.all(dq == 0)
@@ -238,12 +249,21 @@ def test_bwd_grouped_deterministic():
     dout = upstream(w, 1951)
     qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dout))
     o, lse = binding.fwd_ex(qd, kd, vd, w.scale, True, num_splits=1)
-    _note("bwd_ex determinism")
-    r1 = binding.bwd(qd, kd, vd, o, lse, gd, w.scale, True)
-    r2 = binding.bwd(qd, kd, vd, o, lse, gd, w.scale, True)
-    torch.cuda.synchronize()
-    for a, b in zip(r1, r2):
-        assert torch.equal(a, b)
+    for parts in (1, 2, 4):
+        _note(f"bwd_ex determinism parts={parts}")
+        r1 = binding.bwd(qd, kd, vd, o, lse, gd, w.scale, True, num_splits=parts)
+        r2 = binding.bwd(qd, kd, vd, o, lse, gd, w.scale, True, num_splits=parts)
+        torch.cuda.synchronize()
+        for a, b in zip(r1, r2):
+            assert torch.equal(a, b)
+        if parts == 1:
+            one = r1
+        else:
+            # dQ does not depend on the parts; dK, dV differ by summation order
+            assert torch.equal(r1[0], one[0])
+            for a, b in zip(r1[1:], one[1:]):
+                assert float((a.float() - b.float()).abs().max()) <= 4 * 2.0 ** -11 * float(
+                    b.float().abs().max())
 
 
 def test_bwd_workload_g2_sampled_rows_and_invariants():
@@ -253,7 +273,9 @@ def test_bwd_workload_g2_sampled_rows_and_invariants():
     w = WORKLOADS["G2"]
     q, k, v = make_inputs(w)
     dout = upstream(w, 2000)
-    _note("bwd workload G2")
+    parts = binding.bwd_default_splits(w.B, w.H, w.h_kv, w.N, w.n_kv, w.d, w.causal,
+                                       binding.FA_BF16)
+    _note(f"bwd workload G2, default head parts {parts}")
     dq, dk, dv = run_bwd_ex(w, q, k, v, dout)
     rows = sample_rows(w, 256)
     ref = oracle.bwd_dq_rows(q, k, v, dout, w.scale, w.causal, rows)
@@ -265,6 +287,11 @@ def test_bwd_workload_g2_sampled_rows_and_invariants():
     grp = w.H // w.h_kv
     sum_g = dout.double().sum(dim=2).reshape(w.B, w.h_kv, grp, w.d).sum(dim=2)
     assert float((dv64.sum(dim=2) - sum_g).norm()) <= 5 * u * float(dv64.norm()), "G2: dV rows"
+    # one part per group (a single workgroup sums the group) agrees to rounding
+    _note("bwd workload G2, one head part")
+    _, dk1, dv1 = run_bwd_ex(w, q, k, v, dout, parts=1)
+    for a, b, name in ((dk, dk1, "dK"), (dv, dv1, "dV")):
+        assert float((a.double() - b.double()).norm()) <= 2 * u * float(b.double().norm()), name
 
 
 def test_bwd_f32_deterministic_and_delta():
