@@ -241,7 +241,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
         }
       }
 
-      const bool edge = q0 + kBT > nq || kw0 + 32 > nk || (CAUSAL && q0 + off < kw0 + 31);
+      // Only the causal mask is applied: a query row past the end has zero
+      // Q and dO rows and a zero lse and D, so its weights add exact zeros,
+      // and a key past the end only touches its own dK/dV column, which is
+      // never stored.  key > query + off reads kq > 8 (r/4) + r%4.
+      const bool diag = CAUSAL && q0 + off < kw0 + 31;
+      const int kq = key - q0 - off - 4 * grp;
 #pragma unroll
       for (int jr = 0; jr < 4; ++jr) {
         const f32x4 l4 = *(const f32x4*)(&stat[buf][0][8 * jr + 4 * grp]);
@@ -250,11 +255,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * jr + e;
           float p = fast_exp2(fmaf(s[r], c, -l4[e]));
-          if (edge) {
-            const int q = q0 + 8 * jr + 4 * grp + e;
-            const bool ok = q < nq && key < nk && (!CAUSAL || key <= q + off);
-            p = ok ? p : 0.f;
-          }
+          if (diag) p = kq > 8 * jr + e ? 0.f : p;
           s[r] = p;                       // P
           dp[r] = p * (dp[r] - d4[e]);    // dS
         }

@@ -285,19 +285,25 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
       }
     }
 
-    const int key = kw0 + col;
-    const bool edge = q0 + kBT > nq || kw0 + 32 > nk || (CAUSAL && q0 + off < kw0 + 31);
+    // Only the causal mask is applied.  A query row past the end has zero Q
+    // and dO rows and a zero lse and D (the buffer range check), so its
+    // weights are finite and add exact zeros; a key past the end only
+    // touches its own dK/dV column, which is never stored.  Register r holds
+    // query q0 + 8 (r/4) + 4 grp + r%4, so key > query + off reads
+    // kq > 8 (r/4) + r%4 with one per-lane offset kq.
+    const bool diag = CAUSAL && q0 + off < kw0 + 31;  // the tile crosses this wave's diagonal
+    const int kq0 = kw0 + col - q0 - off - 4 * grp;
     // One 16-query chunk at a time (registers 8 ch .. 8 ch + 7): P, dS,
     // their packed pairs, then dV^T += dO^T P and dK^T += Q^T dS for the
     // chunk, so only one chunk's weights are live.
-    // Mask modes: 0 none, 1 always, 2 where `edge` holds.  At d = 64 the
-    // masked form is its own wave-uniform branch, taken only by diagonal and
-    // ragged tiles (as selects in every tile it costs four VALU instructions
-    // per score); at d = 128 the second copy of the code would cost more in
+    // Mask modes: 0 none, 1 always, 2 where `diag` holds.  At d = 64 the
+    // masked form is its own wave-uniform branch, taken only by diagonal
+    // tiles; at d = 128 the second copy of the code would cost more in
     // spilled registers than the selects, so mode 2 folds the test into
-    // every tile.
+    // every tile (an offset that masks nothing off the diagonal).
     auto weights = [&](auto mode, int ch, uint32_t* pp, uint32_t* pd) {
       constexpr int M = decltype(mode)::value;
+      const int kq = M == 2 && !diag ? INT32_MIN : kq0;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int j = 2 * ch + jj;
@@ -308,11 +314,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * j + e;
           float p = fast_exp2(fmaf(s[r], c, -l4[e]));
-          if (M == 1 || (M == 2 && edge)) {
-            const int q = q0 + 8 * j + 4 * grp + e;
-            const bool ok = q < nq && key < nk && (!CAUSAL || key <= q + off);
-            p = ok ? p : 0.f;
-          }
+          if (CAUSAL && M != 0) p = kq > 8 * j + e ? 0.f : p;
           pv[e] = p;
           dsv[e] = p * (dp[r] - d4[e]);
         }
@@ -324,8 +326,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     };
     auto chunk = [&](int ch) {
       uint32_t pp[4], pd[4];
-      if constexpr (D == 64) {
-        if (edge)
+      if constexpr (D == 64 || !CAUSAL) {
+        if (diag)
           weights(std::integral_constant<int, 1>{}, ch, pp, pd);
         else
           weights(std::integral_constant<int, 0>{}, ch, pp, pd);
