@@ -115,10 +115,10 @@ __global__ __launch_bounds__(256) void bwd_delta_f32_kernel(const float* __restr
 
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (K/V head, 128 keys), summing the query heads of
-// its group in registers.
+// its group in registers.  At d = 64 two waves share a SIMD.
 // ---------------------------------------------------------------------------
 template <bool CAUSAL, int D>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void bwd_dkdv_f32_kernel(BwdArgs a) {
   using T = Tile32<D>;
   constexpr int kStage = 2 * (T::kRowFloats + T::kTFloats);  // Qr, Qt, dOr, dOt
   constexpr int kPer = 2 * T::kUnits / kThreads;             // Q and dO units per thread
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
       float* rm = base + (wave * 64 + i * kThreads < T::kUnits ? 0 : T::kRowFloats + T::kTFloats);
       store_unit<D>(rm, rm + T::kRowFloats, rq, cc, sx[i]);
     }
-    if (tid < 2 * kBT) stat[buf][tid / kBT][tid % kBT] = tid < kBT ? lse2_of(st) : st;
+    if (tid < 2 * kBT) stat[buf][tid / kBT][tid % kBT] = tid < kBT ? lse2_of(st) : -st;
   };
 
   const float c = a.scale_log2;
@@ -227,9 +227,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
       const float* grm = qtm + T::kTFloats;
       const float* gtm = grm + T::kRowFloats;
 
-      // S = Q K^T, dP = dO V^T: lane holds key `key`, register r the query
-      // q0 + 8(r/4) + 4g + r%4.
-      f32x16 s = {}, dp = {};
+      // S = Q K^T, dP - D = dO V^T - D: lane holds key `key`, register r
+      // the query q0 + 8(r/4) + 4g + r%4; the dP product starts from -D.
+      f32x16 s = {}, dp;
+#pragma unroll
+      for (int jr = 0; jr < 4; ++jr) {
+        const f32x4 nd = *(const f32x4*)(&stat[buf][1][8 * jr + 4 * grp]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * jr + e] = nd[e];
+      }
 #pragma unroll
       for (int j = 0; j < D / 8; ++j) {
         const f32x4 qa = *(const f32x4*)(qrm + col * T::kRowStride + j * 8 + grp * 4);
@@ -250,14 +256,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(BwdArgs a) {
 #pragma unroll
       for (int jr = 0; jr < 4; ++jr) {
         const f32x4 l4 = *(const f32x4*)(&stat[buf][0][8 * jr + 4 * grp]);
-        const f32x4 d4 = *(const f32x4*)(&stat[buf][1][8 * jr + 4 * grp]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * jr + e;
           float p = fast_exp2(fmaf(s[r], c, -l4[e]));
           if (diag) p = kq > 8 * jr + e ? 0.f : p;
           s[r] = p;                       // P
-          dp[r] = p * (dp[r] - d4[e]);    // dS
+          dp[r] = p * dp[r];              // dS
         }
       }
 
@@ -351,6 +356,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(BwdArgs a, int n_q
       lse2_of(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, my_q * 4, 0, 0)));
   const float drow =
       __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dr, my_q * 4, 0, 0));
+  f32x16 ndrow;  // -D of the lane's row in every register: the start of dP - D
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndrow[r] = -drow;
 
   // causal: row i sees keys j <= i + off
   const int kv_end = CAUSAL ? max(0, min(q0 + kRows + off, nk)) : nk;
@@ -407,9 +415,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(BwdArgs a, int n_q
       const float* ktm = krm + T::kRowFloats;
       const float* vrm = ktm + T::kTFloats;
 
-      // S^T = K Q^T, dP^T = V dO^T: lane holds query my_q, register r the
-      // key k0 + 8(r/4) + 4g + r%4.
-      f32x16 s = {}, dp = {};
+      // S^T = K Q^T, dP^T - D = V dO^T - D: lane holds query my_q, register
+      // r the key k0 + 8(r/4) + 4g + r%4; the dP product starts from -D.
+      f32x16 s = {}, dp = ndrow;
 #pragma unroll
       for (int j = 0; j < D / 8; ++j) {
         const f32x4 ka = *(const f32x4*)(krm + col * T::kRowStride + j * 8 + grp * 4);
@@ -421,16 +429,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(BwdArgs a, int n_q
         }
       }
 
+      // Masked keys (past the end, or after the row's last visible key):
+      // register r holds key k0 + 8 (r/4) + 4 grp + r%4, masked when
+      // 8 (r/4) + r%4 exceeds one per-lane limit.
       const bool edge = k0 + kBT > nk || (CAUSAL && k0 + kBT - 1 > qw0 + off);
+      const int lim = (CAUSAL ? min(nk - 1, my_q + off) : nk - 1) - k0 - 4 * grp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(fmaf(s[r], c, -lse2));
-        if (edge) {
-          const int key = k0 + 8 * (r >> 2) + 4 * grp + (r & 3);
-          const bool ok = key < nk && (!CAUSAL || key <= my_q + off);
-          p = ok ? p : 0.f;
-        }
-        dp[r] = p * (dp[r] - drow);  // dS^T
+        if (edge) p = 8 * (r >> 2) + (r & 3) > lim ? 0.f : p;
+        dp[r] = p * dp[r];  // dS^T
       }
 
       // dQ^T += K^T dS^T: instruction r takes register r.

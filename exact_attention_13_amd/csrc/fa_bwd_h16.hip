@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
       store_rows<D>(rm, p, cc, sx[sl], sy[sl]);
       store_cols<D>(rm + T::kRowElems, p, cc, sx[sl], sy[sl]);
     }
-    if (i0 == 0 && tid < 2 * kBT) stat[buf][tid / kBT][tid % kBT] = tid < kBT ? lse_log2(st) : st;
+    if (i0 == 0 && tid < 2 * kBT) stat[buf][tid / kBT][tid % kBT] = tid < kBT ? lse_log2(st) : -st;
   };
   constexpr int kFirst = kHalves ? 1 : kPer;  // parts loaded at the top of an iteration
 
@@ -269,10 +269,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     const uint16_t* grm = qtm + T::kTElems;
     const uint16_t* gtm = grm + T::kRowElems;
 
-    // S = Q K^T and dP = dO V^T: lane holds key kw0 + col of the queries
-    // q0 + 8 (r/4) + 4 grp + r%4.
+    // S = Q K^T and dP - D = dO V^T - D: lane holds key kw0 + col of the
+    // queries q0 + 8 (r/4) + 4 grp + r%4; the dP product starts from -D, so
+    // that dS = P (dP - D) is one multiply per score.
     f32x16 s = {}, dp = {};
     if (active) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 nd = *(const f32x4*)(&stat[buf][1][8 * j + 4 * grp]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * j + e] = nd[e];
+      }
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
         const u32x4 qa = *(const u32x4*)(qrm + col * T::kRowStride + kc * 16 + grp * 8);
@@ -308,7 +315,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
       for (int jj = 0; jj < 2; ++jj) {
         const int j = 2 * ch + jj;
         const f32x4 l4 = *(const f32x4*)(&stat[buf][0][8 * j + 4 * grp]);
-        const f32x4 d4 = *(const f32x4*)(&stat[buf][1][8 * j + 4 * grp]);
         float pv[4], dsv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
           float p = fast_exp2(fmaf(s[r], c, -l4[e]));
           if (CAUSAL && M != 0) p = kq > 8 * j + e ? 0.f : p;
           pv[e] = p;
-          dsv[e] = p * (dp[r] - d4[e]);
+          dsv[e] = p * dp[r];
         }
         pp[2 * jj] = HH::pack(pv[0], pv[1]);
         pp[2 * jj + 1] = HH::pack(pv[2], pv[3]);
@@ -437,6 +443,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
       lse_log2(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, my_q * 4, 0, 0)));
   const float drow =
       __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dr, my_q * 4, 0, 0));
+  f32x16 ndrow;  // -D of the lane's row in every register: the start of dP - D
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndrow[r] = -drow;
 
   // causal: row i sees keys j <= i + off
   const int kv_end = CAUSAL ? max(0, min(q0 + kBwdRows + off, nk)) : nk;
@@ -496,9 +505,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
       const uint16_t* ktm = krm + T::kRowElems;
       const uint16_t* vrm = ktm + T::kTElems;
 
-      // S^T = K Q^T, dP^T = V dO^T: lane holds query my_q, keys
-      // k0 + 8 (r/4) + 4 grp + r%4.
-      f32x16 s = {}, dp = {};
+      // S^T = K Q^T, dP^T - D = V dO^T - D: lane holds query my_q, keys
+      // k0 + 8 (r/4) + 4 grp + r%4; the dP product starts from -D.
+      f32x16 s = {}, dp = ndrow;
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
         const u32x4 ka = *(const u32x4*)(krm + col * T::kRowStride + kc * 16 + grp * 8);
@@ -511,20 +520,20 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
       }
 
       // dS^T = P^T (dP^T - D).  The masked form runs only on diagonal and
-      // ragged tiles, as its own wave-uniform branch: folded into every tile
-      // as selects it would add four VALU instructions per score.
+      // ragged tiles, as its own wave-uniform branch.  Register r holds key
+      // k0 + 8 (r/4) + 4 grp + r%4, so the key is masked (past the end, or
+      // after the row's last visible key) when 8 (r/4) + r%4 exceeds one
+      // per-lane limit.
       uint32_t pd[8];
       auto weights = [&](auto masked) {
+        const int last = CAUSAL ? min(nk - 1, my_q + off) : nk - 1;
+        const int lim = last - k0 - 4 * grp;
         float dsv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = fast_exp2(fmaf(s[r], c, -lse2));
-          if constexpr (decltype(masked)::value) {
-            const int key = k0 + 8 * (r >> 2) + 4 * grp + (r & 3);
-            const bool ok = key < nk && (!CAUSAL || key <= my_q + off);
-            p = ok ? p : 0.f;
-          }
-          dsv[r] = p * (dp[r] - drow);
+          if constexpr (decltype(masked)::value) p = 8 * (r >> 2) + (r & 3) > lim ? 0.f : p;
+          dsv[r] = p * dp[r];
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) pd[i] = HH::pack(dsv[2 * i], dsv[2 * i + 1]);
