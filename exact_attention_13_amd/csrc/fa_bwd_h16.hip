@@ -15,15 +15,16 @@
 //   * bwd_delta_kernel: D_i, one row per d/8 lanes, v_dot2 on the stored pairs;
 //   * bwd_dkdv_kernel: a workgroup owns 128 keys (four waves x 32), keeps its
 //     K and V fragments in registers and streams 32-query tiles of Q and dO
-//     through double-buffered LDS, each tile stored twice: row-major (for
-//     S = Q K^T and dP = dO V^T, whose accumulators give every lane one key)
-//     and transposed with the query order permuted inside 16-row chunks (bits
-//     2 and 3 swapped), so that the P and dS accumulators are, unchanged, the
-//     B operands of dV^T += dO^T P and dK^T += Q^T dS;
+//     through double-buffered LDS, row-major: S = Q K^T and dP = dO V^T read
+//     them as A operands (their accumulators give every lane one key), and
+//     dV^T += dO^T P, dK^T += Q^T dS read the transposed operands straight
+//     from the same rows with the LDS transpose load, in the query order in
+//     which the P and dS accumulators are, unchanged, the B operands;
 //   * bwd_dq_kernel: the forward kernel's shape: a workgroup owns 128 queries
 //     (Q and dO fragments in registers, one query per lane in S^T = K Q^T and
-//     dP^T = V dO^T) and streams 32-key tiles of K (row-major and transposed)
-//     and V (row-major); dS^T is the B operand of dQ^T += K^T dS^T.
+//     dP^T = V dO^T) and streams 32-key tiles of K and V (row-major); dS^T is
+//     the B operand of dQ^T += K^T dS^T, whose K^T operand comes from the K
+//     rows through the transpose load.
 // Causal masking, ragged tails and the -inf guard follow the forward kernels.
 #include <type_traits>
 
@@ -54,15 +55,9 @@ template <int D> constexpr int kDqWaves = D == 128 ? 2 : 3;
 template <int D>
 struct BwdTile {
   static constexpr int kRowStride = D + 8;  // row-major tile (+16 B per row)
-  static constexpr int kTStride = kBT + 8;  // transposed tile (+16 B per row)
   static constexpr int kRowElems = kBT * kRowStride;
-  static constexpr int kTElems = D * kTStride;
   static constexpr int kPairUnits = (kBT / 2) * (D / 8);  // (row pair, 8 columns)
 };
-
-// Position of row rr of a tile in the transposed layout (bits 2, 3 swapped
-// inside each 16-row chunk; see swap23).
-__device__ __forceinline__ int tpos(int rr) { return (rr & ~15) | swap23(rr & 15); }
 
 // Rows 2p and 2p+1, columns 8cc .. 8cc+7, of a [rows, D] array.
 template <int D>
@@ -79,19 +74,27 @@ __device__ __forceinline__ void store_rows(uint16_t* rm, int p, int cc, u32x4 x,
   *(u32x4*)(rm + (2 * p + 1) * T::kRowStride + cc * 8) = y;
 }
 
-// Transposed store: one 32-bit word holds the pair (row 2p, row 2p+1) of a
-// column; rows 2p, 2p+1 stay adjacent under tpos.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// A operand of a 32x32x16 MFMA that contracts over tile rows, read from the
+// row-major tile with gfx950's LDS transpose load (ds_read_b64_tr_b16):
+// lane (col, grp) receives column c0 + col of rows r0 + 4 grp + 0..3 and
+// r0 + 8 + 4 grp + 0..3, the row order in which the weights' registers hold
+// them (register r of a score tile is row 8 (r/4) + 4 grp + r%4).  Within
+// each 16-lane group the instruction hands lane j element j % 4 of the 8-byte
+// chunks supplied by lanes j/4, 4 + j/4, 8 + j/4 and 12 + j/4, so lane i
+// supplies row i/4, columns 4 (i%4) .. +3 of the group's 4 x 16 block.
 template <int D>
-__device__ __forceinline__ void store_cols(uint16_t* tm, int p, int cc, u32x4 x, u32x4 y) {
+__device__ __forceinline__ u32x4 lds_tr_operand(const uint16_t* tile, int r0, int c0, int lane) {
   using T = BwdTile<D>;
-  const int pos = tpos(2 * p);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t lo = __builtin_amdgcn_perm(y[j], x[j], 0x05040100u);
-    const uint32_t hi = __builtin_amdgcn_perm(y[j], x[j], 0x07060302u);
-    *(uint32_t*)(tm + (cc * 8 + 2 * j) * T::kTStride + pos) = lo;
-    *(uint32_t*)(tm + (cc * 8 + 2 * j + 1) * T::kTStride + pos) = hi;
-  }
+  const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int colx = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const uint16_t* p = tile + row * T::kRowStride + colx;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * T::kRowStride));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return (u32x4){a[0], a[1], b[0], b[1]};
 }
 
 // logsumexp in exp2 units; a row without a visible key (LSE = -inf) gets +inf
@@ -134,7 +137,7 @@ template <bool BF16, bool CAUSAL, int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<D>))) void bwd_dkdv_kernel(BwdArgs a) {
   using HH = Half<BF16>;
   using T = BwdTile<D>;
-  constexpr int kStage = 2 * (T::kRowElems + T::kTElems);  // Qr, Qt, dOr, dOt
+  constexpr int kStage = 2 * T::kRowElems;  // Q rows, dO rows
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
   __shared__ __attribute__((aligned(16))) float stat[2][2][kBT];  // [stage][lse2, D][query]
 
@@ -230,9 +233,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
       const int p = w % (kBT / 2), cc = w / (kBT / 2);
       const int sl = kHalves ? 0 : i;
       const bool first = wave * 64 + i * kBwdThreads < T::kPairUnits;
-      uint16_t* rm = base + (first ? 0 : T::kRowElems + T::kTElems);
-      store_rows<D>(rm, p, cc, sx[sl], sy[sl]);
-      store_cols<D>(rm + T::kRowElems, p, cc, sx[sl], sy[sl]);
+      store_rows<D>(base + (first ? 0 : T::kRowElems), p, cc, sx[sl], sy[sl]);
     }
     if (i0 == 0 && tid < 2 * kBT) stat[buf][tid / kBT][tid % kBT] = tid < kBT ? lse_log2(st) : -st;
   };
@@ -265,9 +266,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     // causal: a tile whose last query sees none of this wave's keys is empty
     const bool active = !(CAUSAL && q0 + kBT - 1 + off < kw0);
     const uint16_t* qrm = lds + buf * kStage;
-    const uint16_t* qtm = qrm + T::kRowElems;
-    const uint16_t* grm = qtm + T::kTElems;
-    const uint16_t* gtm = grm + T::kRowElems;
+    const uint16_t* grm = qrm + T::kRowElems;
 
     // S = Q K^T and dP - D = dO V^T - D: lane holds key kw0 + col of the
     // queries q0 + 8 (r/4) + 4 grp + r%4; the dP product starts from -D, so
@@ -344,8 +343,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
       const u32x4 bd = {pd[0], pd[1], pd[2], pd[3]};
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const u32x4 ga = *(const u32x4*)(gtm + (db * 32 + col) * T::kTStride + ch * 16 + grp * 8);
-        const u32x4 qa = *(const u32x4*)(qtm + (db * 32 + col) * T::kTStride + ch * 16 + grp * 8);
+        const u32x4 ga = lds_tr_operand<D>(grm, ch * 16, db * 32, lane);
+        const u32x4 qa = lds_tr_operand<D>(qrm, ch * 16, db * 32, lane);
         dvT[db] = HH::mfma(ga, bp, dvT[db]);
         dkT[db] = HH::mfma(qa, bd, dkT[db]);
       }
@@ -406,7 +405,7 @@ template <bool BF16, bool CAUSAL, int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDqWaves<D>))) void bwd_dq_kernel(BwdArgs a, int n_qt, int total) {
   using HH = Half<BF16>;
   using T = BwdTile<D>;
-  constexpr int kStage = 2 * T::kRowElems + T::kTElems;  // Kr, Kt, Vr
+  constexpr int kStage = 2 * T::kRowElems;  // K rows, V rows
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -477,10 +476,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
       const int w = u % T::kPairUnits;
       const int p = w % (kBT / 2), cc = w / (kBT / 2);
       if (wave * 64 + i * kBwdThreads < T::kPairUnits) {
-        store_rows<D>(base, p, cc, sx[i], sy[i]);                 // Kr
-        store_cols<D>(base + T::kRowElems, p, cc, sx[i], sy[i]);  // Kt
+        store_rows<D>(base, p, cc, sx[i], sy[i]);
       } else {
-        store_rows<D>(base + T::kRowElems + T::kTElems, p, cc, sx[i], sy[i]);  // Vr
+        store_rows<D>(base + T::kRowElems, p, cc, sx[i], sy[i]);
       }
     }
   };
@@ -502,8 +500,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
 
     if (k0 < wave_kv_end) {
       const uint16_t* krm = lds + buf * kStage;
-      const uint16_t* ktm = krm + T::kRowElems;
-      const uint16_t* vrm = ktm + T::kTElems;
+      const uint16_t* vrm = krm + T::kRowElems;
 
       // S^T = K Q^T, dP^T - D = V dO^T - D: lane holds query my_q, keys
       // k0 + 8 (r/4) + 4 grp + r%4; the dP product starts from -D.
@@ -549,7 +546,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
           const u32x4 bd = {pd[4 * ch], pd[4 * ch + 1], pd[4 * ch + 2], pd[4 * ch + 3]};
-          const u32x4 ka = *(const u32x4*)(ktm + (db * 32 + col) * T::kTStride + ch * 16 + grp * 8);
+          const u32x4 ka = lds_tr_operand<D>(krm, ch * 16, db * 32, lane);
           dqT[db] = HH::mfma(ka, bd, dqT[db]);
         }
     }
