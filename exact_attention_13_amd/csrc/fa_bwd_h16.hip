@@ -74,29 +74,6 @@ __device__ __forceinline__ void store_rows(uint16_t* rm, int p, int cc, u32x4 x,
   *(u32x4*)(rm + (2 * p + 1) * T::kRowStride + cc * 8) = y;
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// A operand of a 32x32x16 MFMA that contracts over tile rows, read from the
-// row-major tile with gfx950's LDS transpose load (ds_read_b64_tr_b16):
-// lane (col, grp) receives column c0 + col of rows r0 + 4 grp + 0..3 and
-// r0 + 8 + 4 grp + 0..3, the row order in which the weights' registers hold
-// them (register r of a score tile is row 8 (r/4) + 4 grp + r%4).  Within
-// each 16-lane group the instruction hands lane j element j % 4 of the 8-byte
-// chunks supplied by lanes j/4, 4 + j/4, 8 + j/4 and 12 + j/4, so lane i
-// supplies row i/4, columns 4 (i%4) .. +3 of the group's 4 x 16 block.
-template <int D>
-__device__ __forceinline__ u32x4 lds_tr_operand(const uint16_t* tile, int r0, int c0, int lane) {
-  using T = BwdTile<D>;
-  const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
-  const int colx = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const uint16_t* p = tile + row * T::kRowStride + colx;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * T::kRowStride));
-  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
-  return (u32x4){a[0], a[1], b[0], b[1]};
-}
-
 // logsumexp in exp2 units; a row without a visible key (LSE = -inf) gets +inf
 // so that every weight exp2(s c - lse2) is 0 instead of inf.
 __device__ __forceinline__ float lse_log2(float lse) {
@@ -343,8 +320,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
       const u32x4 bd = {pd[0], pd[1], pd[2], pd[3]};
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const u32x4 ga = lds_tr_operand<D>(grm, ch * 16, db * 32, lane);
-        const u32x4 qa = lds_tr_operand<D>(qrm, ch * 16, db * 32, lane);
+        const u32x4 ga = lds_tr_operand(grm, T::kRowStride, ch * 16, db * 32, lane);
+        const u32x4 qa = lds_tr_operand(qrm, T::kRowStride, ch * 16, db * 32, lane);
         dvT[db] = HH::mfma(ga, bp, dvT[db]);
         dkT[db] = HH::mfma(qa, bd, dkT[db]);
       }
@@ -546,7 +523,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
           const u32x4 bd = {pd[4 * ch], pd[4 * ch + 1], pd[4 * ch + 2], pd[4 * ch + 3]};
-          const u32x4 ka = lds_tr_operand<D>(krm, ch * 16, db * 32, lane);
+          const u32x4 ka = lds_tr_operand(krm, T::kRowStride, ch * 16, db * 32, lane);
           dqT[db] = HH::mfma(ka, bd, dqT[db]);
         }
     }

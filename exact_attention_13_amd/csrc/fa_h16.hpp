@@ -1,4 +1,4 @@
-// fa_h16.hpp -- helpers shared by the bf16/fp16 forward kernels (gfx950).
+// fa_h16.hpp -- helpers shared by the bf16/fp16 forward and backward kernels (gfx950).
 #pragma once
 
 #include "fa_device.hpp"
@@ -51,6 +51,30 @@ struct Half<false> {
                                   acc, false);
   }
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// A operand of a 32x32x16 MFMA that contracts over the rows of a row-major
+// LDS tile (`stride` elements per row), read with gfx950's LDS transpose load
+// (ds_read_b64_tr_b16): lane (col, grp) receives column c0 + col of rows
+// r0 + 4 grp + 0..3 and r0 + 8 + 4 grp + 0..3, the row order in which a score
+// tile's registers hold them (register r is row 8 (r/4) + 4 grp + r%4), so
+// P or dS packed from those registers is the matching B operand.  Within each
+// 16-lane group the instruction hands lane j element j % 4 of the 8-byte
+// chunks supplied by lanes j/4, 4 + j/4, 8 + j/4 and 12 + j/4, so lane i
+// supplies row i/4, columns 4 (i%4) .. +3 of the group's 4 x 16 block.
+// Addresses must be 8-byte aligned (stride and c0 multiples of 4).
+__device__ __forceinline__ u32x4 lds_tr_operand(const uint16_t* tile, int stride, int r0, int c0,
+                                                int lane) {
+  const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int colx = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const uint16_t* p = tile + row * stride + colx;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * stride));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return (u32x4){a[0], a[1], b[0], b[1]};
+}
 
 // Maximum of the KB x 16 scores held by a lane, as a tree of v_max3.
 template <int KB>
