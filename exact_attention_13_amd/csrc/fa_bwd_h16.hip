@@ -46,10 +46,9 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // than half the register file, and letting the compiler spill those few (two
 // reloads per query tile) so that two waves share a SIMD is worth +37-51 %,
 // because one wave's exponentials and packing then hide under the other's
-// MFMAs.  At d = 64 the dQ kernel runs three waves per SIMD; the dK/dV kernel
-// stays at two, where its separate unmasked branch (below) fits without
-// spills.
-template <int D> constexpr int kDkdvWaves = 2;
+// MFMAs.  At d = 64 both kernels run three waves per SIMD (the causal dK/dV
+// instance spills two registers).
+template <int D> constexpr int kDkdvWaves = D == 64 ? 3 : 2;
 template <int D> constexpr int kDqWaves = D == 128 ? 2 : 3;
 
 template <int D>
