@@ -51,9 +51,19 @@ constexpr float kLog2e = 1.44269504088896340736f;
 template <int D> constexpr int kDkdvWaves = D == 64 ? 3 : 2;
 template <int D> constexpr int kDqWaves = D == 128 ? 2 : 3;
 
+// Row padding of the LDS tiles, for 64 banks of 4 bytes.  Two access
+// patterns read the same rows: 16-byte row reads (16 lanes at the same
+// column of 16 consecutive rows: conflict-free when the row stride is an odd
+// multiple of 4 banks) and transpose loads (32 lanes over 4 consecutive rows
+// x 64 bytes: conflict-free only for a stride of an odd multiple of 16 banks).
+// No stride serves both; 12 or 20 banks (mod 64) keep the row reads
+// conflict-free and the transpose loads 2-way: d = 128 pads by 24 elements
+// (76 banks), d = 64 by 8 (36 banks).  Measured against a pad of 8 at
+// d = 128: 3-4 % faster backward (C3, C5, G2); a pad of 40 (84 banks) is no
+// faster.
 template <int D>
 struct BwdTile {
-  static constexpr int kRowStride = D + 8;  // row-major tile (+16 B per row)
+  static constexpr int kRowStride = D + (D == 128 ? 24 : 8);  // elements per padded row
   static constexpr int kRowElems = kBT * kRowStride;
   static constexpr int kPairUnits = (kBT / 2) * (D / 8);  // (row pair, 8 columns)
 };
