@@ -109,12 +109,18 @@ def cpu_baseline(w, q, k, v, target_s: float):
 
     rng = np.random.default_rng(99)
     total = w.B * w.H * w.N
-    calib = np.sort(rng.choice(total, size=min(256, total), replace=False)).astype(np.int64)
-    t0 = time.perf_counter()
-    oracle.fwd_gqa(q, k, v, w.scale, w.causal, rows=calib, threads=threads)
-    dt = max(time.perf_counter() - t0, 1e-3)
-    rate = rows_flops(calib) / max(dt, 1e-9)
-    per_row = max(rows_flops(calib) / len(calib), 1.0)
+    # Rate from two calibration samples: a small one, then one of about 1.5 s
+    # (the small one's fixed start-up cost would understate the rate).
+    size = min(256, total)
+    for target in (None, 1.5):
+        if target is not None:
+            size = int(min(total, max(256, target * rate / per_row)))
+        calib = np.sort(rng.choice(total, size=size, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.fwd_gqa(q, k, v, w.scale, w.causal, rows=calib, threads=threads)
+        dt = max(time.perf_counter() - t0, 1e-3)
+        rate = rows_flops(calib) / dt
+        per_row = max(rows_flops(calib) / len(calib), 1.0)
     want = int(min(total, max(256, target_s * rate / per_row)))
     rows = np.sort(rng.choice(total, size=want, replace=False)).astype(np.int64)
     t0 = time.perf_counter()
