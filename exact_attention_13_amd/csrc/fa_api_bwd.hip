@@ -13,8 +13,12 @@ using namespace fa_api;
 
 namespace {
 
-// dK/dV workgroups a CU holds at once (two at either head size).
-constexpr int64_t kDkdvSlots = 2 * 256;
+// dK/dV workgroups the 256 CUs hold at once: one per wave a SIMD holds
+// (bf16/fp16: three at d = 64, two at d = 128; fp32: two, one).
+int64_t dkdv_slots(int64_t d, fa_dtype dtype) {
+  const int64_t waves = dtype == FA_F32 ? (d == 64 ? 2 : 1) : (d == 64 ? 3 : 2);
+  return waves * 256;
+}
 
 // Parts a call's head groups are actually split into: at most the group
 // size, and 1 when there is nothing to split (no keys or no queries).
@@ -50,14 +54,19 @@ extern "C" int64_t fa_bwd_ex_default_splits(int64_t B, int64_t H, int64_t H_kv, 
   const int64_t grp = H / H_kv;
   if (grp == 1) return 1;
   const int64_t blocks = fa_impl::bwd_dkdv_blocks(B * H_kv, N_kv);
+  const int64_t slots = dkdv_slots(d, dtype);
   // Without a mask every dK/dV workgroup has the same work: split a grid of
   // less than two workgroups per slot (one wave of equal workgroups ends on
   // its slowest CU).  Under the causal mask the first key tiles carry the
   // most work; four workgroups per slot let the light ones fill in behind.
   const int64_t per_slot = causal ? 4 : 2;
-  int64_t want = blocks >= per_slot * kDkdvSlots ? 1 : (per_slot * kDkdvSlots + blocks - 1) / blocks;
-  if (want < 1) want = 1;
-  return want < grp ? want : grp;
+  int64_t want = blocks >= per_slot * slots ? 1 : (per_slot * slots + blocks - 1) / blocks;
+  // Parts of equal size only (a group of 4 cut in 3 leaves one part with two
+  // heads, and the grid waits for it): the smallest divisor of the group
+  // size that reaches `want`.
+  for (int64_t p = want < 1 ? 1 : want; p < grp; ++p)
+    if (grp % p == 0) return p;
+  return grp;
 }
 
 extern "C" fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,

@@ -266,8 +266,9 @@ int64_t fa_bwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t N_
 /* A head-part count for fa_bwd_ex: 1 without grouped heads or when the
  * unsplit dK/dV grid already holds enough workgroups for MI355X's 256
  * compute units (two per workgroup slot without a mask, four under the
- * causal mask, whose work per key tile is uneven); otherwise enough parts to
- * reach that, at most H / H_kv (1 when the arguments are invalid). */
+ * causal mask, whose work per key tile is uneven); otherwise the smallest
+ * divisor of H / H_kv that reaches that (parts of equal size), at most
+ * H / H_kv (1 when the arguments are invalid). */
 int64_t fa_bwd_ex_default_splits(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv,
                                  int64_t d, int causal, fa_dtype dtype);
 

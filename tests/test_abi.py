@@ -318,6 +318,10 @@ def test_bwd_default_splits():
     assert 1 < s <= 4
     assert libfa.bwd_default_splits(1, 8, 1, 1024, 1024, 64, False, f32) == 8
     assert libfa.bwd_default_splits(1, 8, 2, 4096, 4096, 64, False, f32) == 4
+    # parts of equal size only: 512 d = 64 workgroups want 3 parts (two per
+    # slot of 768), and a group of 4 takes 4 rather than 1 + 1 + 2 heads
+    assert libfa.bwd_default_splits(1, 16, 4, 16384, 16384, 64, False, bf16) == 4
+    assert libfa.bwd_default_splits(1, 12, 4, 4096, 4096, 64, False, bf16) == 3
     # invalid arguments: 1
     assert libfa.bwd_default_splits(1, 4, 3, 100, 100, 64, True, bf16) == 1
     assert libfa.bwd_default_splits(1, 4, 2, 100, 100, 96, True, bf16) == 1
