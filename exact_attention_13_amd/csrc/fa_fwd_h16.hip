@@ -59,6 +59,13 @@ constexpr float kFastSumLimit = 32768.f;
 // Tile configuration: NW wave64s per workgroup, each owning QB blocks of 32
 // query rows; K/V tiles of BN keys.  The instance table below picks one
 // configuration per (dtype, d, causal).
+// Cache policy of the K/V loads of one-wave (decoding) workgroups: every
+// K/V byte is read exactly once there, and the non-temporal hint (nt) keeps
+// that stream from displacing cached lines: 96.5 -> 85.2 us per call on the
+// one-row decoding step (8 x 32 query heads on 8 K/V heads of 16384 keys,
+// d = 128).  The multi-wave kernels re-read K/V tiles across workgroups
+// through L2 and the MALL and keep the default policy.
+constexpr int kStreamAux = 2;  // buffer-load cache policy bit: nt
 template <int D_, int QB_, int BN_, int NW_>
 struct Cfg {
   static constexpr int D = D_, QB = QB_, BN = BN_, NW = NW_;
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
       const int u = tid + i * C::kThreads;
       if (C::kKUnits % C::kThreads == 0 || u < C::kKUnits) {
         const int row = u / (D / 8), cc = u % (D / 8);
-        kst[i] = buf_load16(kr, ((k0 + row) * D + cc * 8) * 2);
+        kst[i] = buf_load16<C::NW == 1 ? kStreamAux : 0>(kr, ((k0 + row) * D + cc * 8) * 2);
       }
     }
 #pragma unroll
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
         const int pr = u % (BN / 2), cc = u / (BN / 2);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          vst[i][h] = buf_load16(vr, ((k0 + 2 * pr + h) * D + cc * 8) * 2);
+          vst[i][h] = buf_load16<C::NW == 1 ? kStreamAux : 0>(vr, ((k0 + 2 * pr + h) * D + cc * 8) * 2);
       }
     }
   };
