@@ -316,3 +316,51 @@ def test_bwd_f32_deterministic_and_delta():
     torch.cuda.synchronize()
     ref = (o.cpu().double() * dout.double()).sum(-1)
     np.testing.assert_allclose(delta.cpu().double().numpy(), ref.numpy(), rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("dtype,d,parts", [("bf16", 128, 2), ("f16", 64, 4), ("f32", 64, 2)])
+def test_bwd_canaries_untouched_and_not_read(dtype, d, parts):
+    # Every buffer (inputs, gradients, delta, the head-part workspace) sits at
+    # the front of a larger allocation whose tail is NaN.  Writes must leave
+    # the tails alone, and reads must not reach them (a read would put NaN
+    # into a gradient).
+    B, H, Hkv, Nq, Nk = 1, 4, 1, 150, 333
+    w = Workload("case", dtype, B, H, Nq, d, True, 2300, "normal", Hkv, Nk)
+    q, k, v = make_inputs(w)
+    dout = upstream(w, 2301)
+    tdt = TORCH[dtype]
+    pad = 4096
+    nq, nk, nl = B * H * Nq * d, B * Hkv * Nk * d, B * H * Nq
+
+    def fenced(n, dt, src=None):
+        buf = torch.full((n + pad,), float("nan"), dtype=dt, device=DEV)
+        if src is not None:
+            buf[:n] = src.reshape(-1).to(DEV)
+        return buf
+
+    qb, gb = fenced(nq, tdt, q), fenced(nq, tdt, dout)
+    kb, vb = fenced(nk, tdt, k), fenced(nk, tdt, v)
+    ob, lb = fenced(nq, tdt), fenced(nl, torch.float32)
+    shape_q, shape_k = (B, H, Nq, d), (B, Hkv, Nk, d)
+    binding.fwd_ex(qb[:nq].view(shape_q), kb[:nk].view(shape_k), vb[:nk].view(shape_k), w.scale,
+                   True, num_splits=1, out=ob[:nq].view(shape_q), lse=lb[:nl].view(B, H, Nq))
+    dqb, dkb, dvb, deltab = fenced(nq, tdt), fenced(nk, tdt), fenced(nk, tdt), fenced(nl, torch.float32)
+    wsn = binding.bwd_workspace_bytes(B, H, Hkv, Nq, Nk, d, parts)
+    assert wsn == 2 * parts * nk * 4
+    wsb = torch.full((wsn + 4 * pad,), 0xFF, dtype=torch.uint8, device=DEV)  # NaN as fp32
+    code = {"f32": binding.FA_F32, "bf16": binding.FA_BF16, "f16": binding.FA_F16}[dtype]
+    _note(f"bwd canaries {dtype} d={d} parts={parts}")
+    st = binding.fa_bwd_ex(qb.data_ptr(), kb.data_ptr(), vb.data_ptr(), ob.data_ptr(),
+                           gb.data_ptr(), lb.data_ptr(), dqb.data_ptr(), dkb.data_ptr(),
+                           dvb.data_ptr(), deltab.data_ptr(), B, H, Hkv, Nq, Nk, d, w.scale, True,
+                           code, parts, wsb.data_ptr(), wsn,
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    for buf, n, name in ((dqb, nq, "dq"), (dkb, nk, "dk"), (dvb, nk, "dv"), (deltab, nl, "delta")):
+        assert torch.isnan(buf[n:]).all(), f"{name}: tail written"
+    assert bool((wsb[wsn:] == 0xFF).all()), "workspace: tail written"
+    rq, rk, rv = oracle.bwd(q, k, v, dout, w.scale, True)
+    for buf, n, shape, ref, name in ((dqb, nq, shape_q, rq, "dQ"), (dkb, nk, shape_k, rk, "dK"),
+                                     (dvb, nk, shape_k, rv, "dV")):
+        assert_grad_close(buf[:n].view(shape).cpu(), ref, dtype, name)
