@@ -46,10 +46,16 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // than half the register file, and letting the compiler spill those few (two
 // reloads per query tile) so that two waves share a SIMD is worth +37-51 %,
 // because one wave's exponentials and packing then hide under the other's
-// MFMAs.  At d = 64 both kernels run three waves per SIMD (the causal dK/dV
+// MFMAs.  At d = 64 the dK/dV kernel runs three waves per SIMD (the causal
 // instance spills two registers).
 template <int D> constexpr int kDkdvWaves = D == 64 ? 3 : 2;
-template <int D> constexpr int kDqWaves = D == 128 ? 2 : 3;
+template <int D> constexpr int kDqWaves = 2;
+// 32-query blocks per wave in the dQ kernel, and queries per workgroup.  At
+// d = 64 two blocks share every K and V operand read from LDS (half the LDS
+// reads per MFMA, like the forward's two row blocks) at two waves per SIMD
+// instead of three: 1-1.5 % faster backward (C4, G1).
+template <int D> constexpr int kDqBlocks = D == 64 ? 2 : 1;
+template <int D> constexpr int kDqRows = 32 * kBwdWaves * kDqBlocks<D>;
 
 // Row padding of the LDS tiles, for 64 banks of 4 bytes.  Two access
 // patterns read the same rows: 16-byte row reads (16 lanes at the same
@@ -385,12 +391,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup per (query head, 128 queries)
+// dQ: one workgroup per (query head, kDqRows queries)
 // ---------------------------------------------------------------------------
 template <bool BF16, bool CAUSAL, int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDqWaves<D>))) void bwd_dq_kernel(BwdArgs a, int n_qt, int total) {
   using HH = Half<BF16>;
   using T = BwdTile<D>;
+  constexpr int QB = kDqBlocks<D>;
+  constexpr int kRows = kDqRows<D>;
   constexpr int kStage = 2 * T::kRowElems;  // K rows, V rows
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
 
@@ -403,9 +411,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
   const int bh = L / n_qt;
   int qt = L - bh * n_qt;
   if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
-  const int q0 = qt * kBwdRows;
-  const int qw0 = q0 + wave * 32;
-  const int my_q = qw0 + col;
+  const int q0 = qt * kRows;
+  const int qw0 = q0 + wave * 32 * QB;  // block qb: queries qw0 + 32 qb .. + 31
   const int b = bh / a.hq;
   const int bkv = b * a.hkv + (bh - b * a.hq) / a.hgrp;  // this query head's K/V head
 
@@ -417,25 +424,34 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
   const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.lse + (int64_t)bh * nq, nq * 4);
   const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.delta + (int64_t)bh * nq, nq * 4);
 
-  // Q and dO rows of this lane's query as B operands.
-  u32x4 qf[D / 16], gf[D / 16];
+  // Q and dO rows of this lane's queries as B operands.
+  u32x4 qf[QB][D / 16], gf[QB][D / 16];
+  float lse2[QB], drow[QB];
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
-    qf[kc] = buf_load16(qr, (my_q * D + kc * 16 + grp * 8) * 2);
-    gf[kc] = buf_load16(gr, (my_q * D + kc * 16 + grp * 8) * 2);
+  for (int qb = 0; qb < QB; ++qb) {
+    const int my_q = qw0 + 32 * qb + col;
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      qf[qb][kc] = buf_load16(qr, (my_q * D + kc * 16 + grp * 8) * 2);
+      gf[qb][kc] = buf_load16(gr, (my_q * D + kc * 16 + grp * 8) * 2);
+    }
+    lse2[qb] = lse_log2(
+        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, my_q * 4, 0, 0)));
+    drow[qb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dr, my_q * 4, 0, 0));
   }
-  const float lse2 =
-      lse_log2(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, my_q * 4, 0, 0)));
-  const float drow =
-      __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dr, my_q * 4, 0, 0));
-  f32x16 ndrow;  // -D of the lane's row in every register: the start of dP - D
+  // With one block per wave the dP product starts from -D of the lane's row
+  // (16 registers), so that dS = P (dP - D) is one multiply; with two blocks
+  // the registers go to the second block and dS takes a subtract as well.
+  f32x16 ndrow = {};
+  if constexpr (QB == 1) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) ndrow[r] = -drow;
+    for (int r = 0; r < 16; ++r) ndrow[r] = -drow[0];
+  }
 
   // causal: row i sees keys j <= i + off
-  const int kv_end = CAUSAL ? max(0, min(q0 + kBwdRows + off, nk)) : nk;
+  const int kv_end = CAUSAL ? max(0, min(q0 + kRows + off, nk)) : nk;
   const int n_kv = (kv_end + kBT - 1) / kBT;
-  const int wave_kv_end = CAUSAL ? max(0, min(qw0 + 32 + off, nk)) : nk;
+  const int wave_kv_end = CAUSAL ? max(0, min(qw0 + 32 * QB + off, nk)) : nk;
 
   // Staging of one key tile: (row pair, 8 columns) units of K then V.
   constexpr int kUnits = 2 * T::kPairUnits;
@@ -470,9 +486,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
   };
 
   const float c = a.scale_log2;
-  f32x16 dqT[D / 32];  // dQ^T: lane holds query my_q
+  f32x16 dqT[QB][D / 32];  // dQ^T: lane holds query qw0 + 32 qb + col
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) dqT[db] = (f32x16){};
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dqT[qb][db] = (f32x16){};
 
   load_tile(0);
   store_tile(0);
@@ -488,18 +506,26 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
       const uint16_t* krm = lds + buf * kStage;
       const uint16_t* vrm = krm + T::kRowElems;
 
-      // S^T = K Q^T, dP^T - D = V dO^T - D: lane holds query my_q, keys
-      // k0 + 8 (r/4) + 4 grp + r%4; the dP product starts from -D.
-      f32x16 s = {}, dp = ndrow;
+      // S^T = K Q^T and dP^T (- D) = V dO^T (- D) for every block: lane
+      // holds query qw0 + 32 qb + col, keys k0 + 8 (r/4) + 4 grp + r%4.  Each
+      // K or V operand read from LDS feeds the products of all blocks.
+      f32x16 s[QB], dp[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        s[qb] = (f32x16){};
+        dp[qb] = QB == 1 ? ndrow : (f32x16){};
+      }
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
         const u32x4 ka = *(const u32x4*)(krm + col * T::kRowStride + kc * 16 + grp * 8);
-        s = HH::mfma(ka, qf[kc], s);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb] = HH::mfma(ka, qf[qb][kc], s[qb]);
       }
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
         const u32x4 va = *(const u32x4*)(vrm + col * T::kRowStride + kc * 16 + grp * 8);
-        dp = HH::mfma(va, gf[kc], dp);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) dp[qb] = HH::mfma(va, gf[qb][kc], dp[qb]);
       }
 
       // dS^T = P^T (dP^T - D).  The masked form runs only on diagonal and
@@ -507,33 +533,42 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
       // k0 + 8 (r/4) + 4 grp + r%4, so the key is masked (past the end, or
       // after the row's last visible key) when 8 (r/4) + r%4 exceeds one
       // per-lane limit.
-      uint32_t pd[8];
-      auto weights = [&](auto masked) {
+      uint32_t pd[QB][8];
+      auto weights = [&](auto masked, int qb) {
+        const int my_q = qw0 + 32 * qb + col;
         const int last = CAUSAL ? min(nk - 1, my_q + off) : nk - 1;
         const int lim = last - k0 - 4 * grp;
         float dsv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(s[r], c, -lse2));
+          float p = fast_exp2(fmaf(s[qb][r], c, -lse2[qb]));
           if constexpr (decltype(masked)::value) p = 8 * (r >> 2) + (r & 3) > lim ? 0.f : p;
-          dsv[r] = p * dp[r];
+          dsv[r] = QB == 1 ? p * dp[qb][r] : p * (dp[qb][r] - drow[qb]);
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pd[i] = HH::pack(dsv[2 * i], dsv[2 * i + 1]);
+        for (int i = 0; i < 8; ++i) pd[qb][i] = HH::pack(dsv[2 * i], dsv[2 * i + 1]);
       };
-      if (k0 + kBT > nk || (CAUSAL && k0 + kBT - 1 > qw0 + off))
-        weights(std::true_type{});
-      else
-        weights(std::false_type{});
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (k0 + kBT > nk || (CAUSAL && k0 + kBT - 1 > qw0 + 32 * qb + off))
+          weights(std::true_type{}, qb);
+        else
+          weights(std::false_type{}, qb);
+      }
 
-      // dQ^T += K^T dS^T over the two 16-key chunks.
+      // dQ^T += K^T dS^T over the two 16-key chunks; each K^T operand feeds
+      // every block.
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-          const u32x4 bd = {pd[4 * ch], pd[4 * ch + 1], pd[4 * ch + 2], pd[4 * ch + 3]};
           const u32x4 ka = lds_tr_operand(krm, T::kRowStride, ch * 16, db * 32, lane);
-          dqT[db] = HH::mfma(ka, bd, dqT[db]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const u32x4 bd = {pd[qb][4 * ch], pd[qb][4 * ch + 1], pd[qb][4 * ch + 2],
+                              pd[qb][4 * ch + 3]};
+            dqT[qb][db] = HH::mfma(ka, bd, dqT[qb][db]);
+          }
         }
     }
 
@@ -541,17 +576,22 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
     __syncthreads();
   }
 
-  if (my_q < nq) {
-    uint16_t* g = (uint16_t*)a.dq + qhead + (int64_t)my_q * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int my_q = qw0 + 32 * qb + col;
+    if (my_q < nq) {
+      uint16_t* g = (uint16_t*)a.dq + qhead + (int64_t)my_q * D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = db * 32 + 8 * j + 4 * grp;
-        const u32x2 w = {HH::pack(dqT[db][4 * j] * a.scale, dqT[db][4 * j + 1] * a.scale),
-                         HH::pack(dqT[db][4 * j + 2] * a.scale, dqT[db][4 * j + 3] * a.scale)};
-        *(u32x2*)(g + d0) = w;
-      }
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d0 = db * 32 + 8 * j + 4 * grp;
+          const u32x2 w = {
+              HH::pack(dqT[qb][db][4 * j] * a.scale, dqT[qb][db][4 * j + 1] * a.scale),
+              HH::pack(dqT[qb][db][4 * j + 2] * a.scale, dqT[qb][db][4 * j + 3] * a.scale)};
+          *(u32x2*)(g + d0) = w;
+        }
+    }
   }
 }
 
@@ -620,7 +660,7 @@ hipError_t launch_bwd(const BwdArgs& a, const void* o, float* delta, hipStream_t
     }
   }
   // dQ over the query heads' row tiles (zero when there are no keys)
-  int n_qt = (a.nq + kBwdRows - 1) / kBwdRows;
+  int n_qt = (a.nq + kDqRows<D> - 1) / kDqRows<D>;
   int total_q = (int)((int64_t)n_qt * a.bh);
   if (total_q > 0) {
     void* p2[] = {&args, &n_qt, &total_q};
