@@ -328,9 +328,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(BwdArgs a, int n_q
   const int nq = a.nq, nk = a.nk, off = a.off;
 
   const int L = xcd_remap(blockIdx.x, total);
-  const int bh = L / n_qt;
-  int qt = L - bh * n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
+  int bh, qt;
+  tile_of<CAUSAL>(L, total, n_qt, bh, qt);
   const int q0 = qt * kRows;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + col;

@@ -408,9 +408,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
   const int nq = a.nq, nk = a.nk, off = a.off;
 
   const int L = xcd_remap(blockIdx.x, total);
-  const int bh = L / n_qt;
-  int qt = L - bh * n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
+  int bh, qt;
+  tile_of<CAUSAL>(L, total, n_qt, bh, qt);
   const int q0 = qt * kRows;
   const int qw0 = q0 + wave * 32 * QB;  // block qb: queries qw0 + 32 qb .. + 31
   const int b = bh / a.hq;

@@ -60,9 +60,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
 
   // logical tile -> (problem, key range, query tile)
   const int L = xcd_remap(blockIdx.x, total);
-  const int pr_sp = L / n_qt;
-  int qt = L - pr_sp * n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;
+  int pr_sp, qt;
+  tile_of<CAUSAL>(L, total, n_qt, pr_sp, qt);
   const int split = SPLIT ? pr_sp % a.splits : 0;
   const int prob = SPLIT ? pr_sp / a.splits : pr_sp;
 
@@ -301,9 +300,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_short_kernel(FwdArgs a, int 
   const int NQ = a.nq, NK = a.nk;
 
   const int L = xcd_remap(blockIdx.x, total);
-  const int prob = L / n_qt;
-  int qt = L - prob * n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;
+  int prob, qt;
+  tile_of<CAUSAL>(L, total, n_qt, prob, qt);
   const int q0 = qt * 32;
   const int my_q = q0 + col;
   const int off = a.causal_off;

@@ -56,6 +56,7 @@ namespace {
 // Largest lane partial row sum accepted without an exact max (see the softmax).
 constexpr float kFastSumLimit = 32768.f;
 
+
 // Tile configuration: NW wave64s per workgroup, each owning QB blocks of 32
 // query rows; K/V tiles of BN keys.  The instance table below picks one
 // configuration per (dtype, d, causal).
@@ -106,9 +107,8 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
 
   // logical tile -> (problem, key range, query tile)
   const int L = xcd_remap(blockIdx.x, total);
-  const int pr_sp = L / n_qt;
-  int qt = L - pr_sp * n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
+  int pr_sp, qt;
+  tile_of<CAUSAL>(L, total, n_qt, pr_sp, qt);
   const int split = SPLIT ? pr_sp % a.splits : 0;
   const int prob = SPLIT ? pr_sp / a.splits : pr_sp;
 
