@@ -42,11 +42,11 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 // Waves per SIMD that the register allocation must leave room for.  Both
 // kernels keep a wave's rows (K and V, or Q and dO) and its gradient
-// accumulators in registers; at d = 128 the dK/dV kernel needs a few more
-// than half the register file, and letting the compiler spill those few (two
-// reloads per query tile) so that two waves share a SIMD is worth +37-51 %,
-// because one wave's exponentials and packing then hide under the other's
-// MFMAs.  At d = 64 the dK/dV kernel runs three waves per SIMD (the causal
+// accumulators in registers.  At d = 128 the dK/dV kernel would need a few
+// more than half the register file; its V rows wait in LDS instead, so that
+// two waves share a SIMD without spills (two waves instead of one are worth
+// +37-51 %: one wave's exponentials and packing hide under the other's
+// MFMAs).  At d = 64 the dK/dV kernel runs three waves per SIMD (the causal
 // instance spills two registers).
 template <int D> constexpr int kDkdvWaves = D == 64 ? 3 : 2;
 template <int D> constexpr int kDqWaves = 2;
@@ -158,12 +158,23 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
   const __amdgpu_buffer_rsrc_t vr = make_rsrc((const uint16_t*)a.v + kvhead, nk * D * 2);
 
   // K and V rows of this wave's keys as B operands: lane (col, grp) holds
-  // row kw0 + col, columns 16 kc + 8 grp .. + 8 (zero past the end).
-  u32x4 kf[D / 16], vf[D / 16];
+  // row kw0 + col, columns 16 kc + 8 grp .. + 8 (zero past the end).  At
+  // d = 128 the V rows wait in LDS instead (each wave reads back only its own
+  // rows, so no barrier is needed): 32 registers fewer, which keeps the
+  // kernel from spilling at two waves per SIMD.
+  constexpr bool kVLds = D == 128;
+  constexpr int kVStride = D + 8;  // 16 consecutive rows at one column: conflict-free
+  __shared__ __attribute__((aligned(16))) uint16_t vlds[kVLds ? kBwdRows * kVStride : 8];
+  uint16_t* vrow = vlds + (kVLds ? (wave * 32 + col) * kVStride + grp * 8 : 0);
+  u32x4 kf[D / 16], vf[kVLds ? 1 : D / 16];
 #pragma unroll
   for (int kc = 0; kc < D / 16; ++kc) {
     kf[kc] = buf_load16(kr, ((kw0 + col) * D + kc * 16 + grp * 8) * 2);
-    vf[kc] = buf_load16(vr, ((kw0 + col) * D + kc * 16 + grp * 8) * 2);
+    const u32x4 x = buf_load16(vr, ((kw0 + col) * D + kc * 16 + grp * 8) * 2);
+    if constexpr (kVLds)
+      *(u32x4*)(vrow + kc * 16) = x;
+    else
+      vf[kc] = x;
   }
 
   // Query tiles qt_begin .. n_qt - 1 of each of the hgrp query heads, walked
@@ -279,7 +290,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
         const u32x4 ga = *(const u32x4*)(grm + col * T::kRowStride + kc * 16 + grp * 8);
-        dp = HH::mfma(ga, vf[kc], dp);
+        u32x4 vb;
+        if constexpr (kVLds)
+          vb = *(const u32x4*)(vrow + kc * 16);
+        else
+          vb = vf[kc];
+        dp = HH::mfma(ga, vb, dp);
       }
     }
 
@@ -288,20 +304,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     // weights are finite and add exact zeros; a key past the end only
     // touches its own dK/dV column, which is never stored.  Register r holds
     // query q0 + 8 (r/4) + 4 grp + r%4, so key > query + off reads
-    // kq > 8 (r/4) + r%4 with one per-lane offset kq.
+    // kq0 > 8 (r/4) + r%4 with one per-lane offset kq0.
     const bool diag = CAUSAL && q0 + off < kw0 + 31;  // the tile crosses this wave's diagonal
     const int kq0 = kw0 + col - q0 - off - 4 * grp;
     // One 16-query chunk at a time (registers 8 ch .. 8 ch + 7): P, dS,
     // their packed pairs, then dV^T += dO^T P and dK^T += Q^T dS for the
     // chunk, so only one chunk's weights are live.
-    // Mask modes: 0 none, 1 always, 2 where `diag` holds.  At d = 64 the
-    // masked form is its own wave-uniform branch, taken only by diagonal
-    // tiles; at d = 128 the second copy of the code would cost more in
-    // spilled registers than the selects, so mode 2 folds the test into
-    // every tile (an offset that masks nothing off the diagonal).
-    auto weights = [&](auto mode, int ch, uint32_t* pp, uint32_t* pd) {
-      constexpr int M = decltype(mode)::value;
-      const int kq = M == 2 && !diag ? INT32_MIN : kq0;
+    // The masked form is its own wave-uniform branch, taken only by diagonal
+    // tiles (folded into every tile, the test would add two VALU
+    // instructions per score).
+    auto weights = [&](auto masked, int ch, uint32_t* pp, uint32_t* pd) {
+      constexpr bool M = decltype(masked)::value;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int j = 2 * ch + jj;
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * j + e;
           float p = fast_exp2(fmaf(s[r], c, -l4[e]));
-          if (CAUSAL && M != 0) p = kq > 8 * j + e ? 0.f : p;
+          if (CAUSAL && M) p = kq0 > 8 * j + e ? 0.f : p;
           pv[e] = p;
           dsv[e] = p * dp[r];
         }
@@ -323,14 +336,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     };
     auto chunk = [&](int ch) {
       uint32_t pp[4], pd[4];
-      if constexpr (D == 64 || !CAUSAL) {
-        if (diag)
-          weights(std::integral_constant<int, 1>{}, ch, pp, pd);
-        else
-          weights(std::integral_constant<int, 0>{}, ch, pp, pd);
-      } else {
-        weights(std::integral_constant<int, 2>{}, ch, pp, pd);
-      }
+      if (diag)
+        weights(std::true_type{}, ch, pp, pd);
+      else
+        weights(std::false_type{}, ch, pp, pd);
       const u32x4 bp = {pp[0], pp[1], pp[2], pp[3]};
       const u32x4 bd = {pd[0], pd[1], pd[2], pd[3]};
 #pragma unroll
