@@ -15,7 +15,7 @@
 #include "fa_device.hpp"
 
 #define LIBFA_VERSION_MAJOR 0
-#define LIBFA_VERSION_MINOR 3
+#define LIBFA_VERSION_MINOR 4
 #define LIBFA_VERSION_PATCH 0
 
 using namespace fa_api;

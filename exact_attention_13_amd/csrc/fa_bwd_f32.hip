@@ -16,9 +16,10 @@
 // (rows 8(r/4) + 4g + r%4) is, unchanged, the B operand of instruction r of
 // the next product:
 //   * bwd_delta_f32_kernel: D_i, d/4 lanes per row;
-//   * bwd_dkdv_f32_kernel: one workgroup per (K/V head, 128 keys), four waves
-//     of 32 keys holding their K and V rows in registers; 32-query tiles of Q
-//     and dO of every query head of the group pass through double-buffered
+//   * bwd_dkdv_f32_kernel: one workgroup per (128 keys, K/V head, part of
+//     the group's query heads), four waves of 32 keys holding their K and V
+//     rows in registers; 32-query tiles of Q and dO of every query head of
+//     the part pass through double-buffered
 //     LDS row-major (S = Q K^T, dP = dO V^T: each lane holds one key) and
 //     transposed (Q^T, dO^T: the A operands of dK^T += Q^T dS and
 //     dV^T += dO^T P);
@@ -114,8 +115,9 @@ __global__ __launch_bounds__(256) void bwd_delta_f32_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (K/V head, 128 keys), summing the query heads of
-// its group in registers.  At d = 64 two waves share a SIMD.
+// dK, dV: one workgroup per (128 keys, K/V head, head part), summing the
+// query heads of its part in registers (the whole group with one part).  At
+// d = 64 two waves share a SIMD.
 // ---------------------------------------------------------------------------
 template <bool CAUSAL, int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void bwd_dkdv_f32_kernel(BwdArgs a) {

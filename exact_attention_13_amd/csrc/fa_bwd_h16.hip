@@ -121,9 +121,11 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (K/V head, 128 keys).  With grouped heads the
-// workgroup walks the query tiles of every query head of its group in turn
-// and sums their contributions in its registers (no atomics: deterministic).
+// dK, dV: one workgroup per (128 keys, K/V head, head part).  With grouped
+// heads the workgroup walks the query tiles of every query head of its part
+// (the whole group with one part) in turn and sums their contributions in
+// its registers; several parts write fp32 partials that bwd_part_sum_kernel
+// adds in part order (no atomics: deterministic).
 // ---------------------------------------------------------------------------
 template <bool BF16, bool CAUSAL, int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<D>))) void bwd_dkdv_kernel(BwdArgs a) {

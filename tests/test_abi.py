@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert libfa.version() == 300
+    assert libfa.version() == 400
     for code in range(10):
         msg = libfa.strerror(code)
         assert msg and "unknown" not in msg
