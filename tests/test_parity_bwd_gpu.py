@@ -364,3 +364,19 @@ def test_bwd_canaries_untouched_and_not_read(dtype, d, parts):
     for buf, n, shape, ref, name in ((dqb, nq, shape_q, rq, "dQ"), (dkb, nk, shape_k, rk, "dK"),
                                      (dvb, nk, shape_k, rv, "dV")):
         assert_grad_close(buf[:n].view(shape).cpu(), ref, dtype, name)
+
+
+# The dQ kernel takes the same grouped heavy-first causal order: shapes whose
+# grid splits evenly over the eight dies (d = 64 dQ tiles hold 256 rows,
+# d = 128 and fp32 ones 128), 3, 5 and 2 units per die.
+@pytest.mark.parametrize("dtype,B,H,N,d", [("bf16", 2, 12, 520, 64), ("bf16", 2, 20, 300, 128),
+                                           ("f32", 1, 16, 260, 64)])
+def test_bwd_causal_tile_order_groups(dtype, B, H, N, d):
+    w = Workload("case", dtype, B, H, N, d, True, 2400 + H)
+    q, k, v = make_inputs(w)
+    dout = upstream(w, 2401 + H)
+    _note(f"bwd causal order {dtype} B={B} H={H} N={N} d={d}")
+    dq, dk, dv = run_bwd(w, q, k, v, dout)
+    rq, rk, rv = oracle.bwd(q, k, v, dout, w.scale, True)
+    for got, ref, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        assert_grad_close(got, ref, dtype, f"{(dtype, B, H, N, d)} {name}")

@@ -235,3 +235,24 @@ def test_library_is_the_hip_build():
     with open("/proc/self/maps") as f:
         maps = f.read()
     assert str(binding.library_path()) in maps
+
+
+# Causal launches whose grid splits evenly over the eight dies take the
+# grouped heavy-first tile order (groups of up to 4 units inside each die's
+# range, a shorter last group, or fewer units than a group); every tile must
+# still be computed exactly once.  Cases: (dtype, B, H, N, d) chosen so that
+# each die holds 1, 3, 6 or 5 units (d = 64 tiles hold 512 rows, d = 128 and
+# fp32 tiles 128), with ragged last tiles in some.
+ORDER_CASES = [("bf16", 2, 4, 1024, 64), ("bf16", 2, 12, 1024, 64), ("f16", 4, 12, 600, 64),
+               ("bf16", 2, 20, 500, 128), ("f16", 1, 16, 256, 128), ("f32", 2, 20, 384, 64)]
+
+
+@pytest.mark.parametrize("dtype,B,H,N,d", ORDER_CASES)
+def test_causal_tile_order_groups(dtype, B, H, N, d):
+    w, (q, k, v) = small_case(dtype, B, H, N, d, True, seed=41 + H + N)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    print(f"causal order {dtype} B={B} H={H} N={N} d={d}", flush=True)
+    o, lse = binding.fwd(qd, kd, vd, w.scale, True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.fwd(q, k, v, w.scale, True)
+    assert_close(o.cpu(), lse.cpu(), o_ref, lse_ref, dtype, f"{(dtype, B, H, N, d)}")
