@@ -380,3 +380,31 @@ def test_bwd_causal_tile_order_groups(dtype, B, H, N, d):
     rq, rk, rv = oracle.bwd(q, k, v, dout, w.scale, True)
     for got, ref, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
         assert_grad_close(got, ref, dtype, f"{(dtype, B, H, N, d)} {name}")
+
+
+# Gradients of tensors past 4 GiB (head offsets beyond 2^31 and 2^32 bytes):
+# the inputs and dO repeat a seeded block of 97 heads along H; the first
+# block is checked against the oracle and every later head must equal its
+# image in the first block bitwise (97 does not divide the 2^32-byte head
+# count, so an offset wrapped at 32 bits would read other data).
+def test_bwd_tensors_past_4gib():
+    P, H, N, d = 97, 33000, 512, 128
+    w = Workload("big", "bf16", 1, P, N, d, True, 2500)
+    q, k, v = make_inputs(w)
+    dout = upstream(w, 2501)
+    assert H * N * d * 2 > 2 ** 32
+    _note(f"bwd past 4 GiB H={H} N={N} d={d}")
+
+    def periodic(x):
+        reps = -(-H // P)
+        return x.to(DEV).repeat(1, reps, 1, 1)[:, :H].contiguous()
+
+    qd, kd, vd, gd = periodic(q), periodic(k), periodic(v), periodic(dout)
+    o, lse = binding.fwd(qd, kd, vd, w.scale, True)
+    dq, dk, dv = binding.bwd(qd, kd, vd, o, lse, gd, w.scale, True)
+    torch.cuda.synchronize()
+    del qd, kd, vd, gd, o, lse
+    rq, rk, rv = oracle.bwd(q, k, v, dout, w.scale, True)
+    for got, ref, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        assert_grad_close(got[:, :P].cpu(), ref, "bf16", f"first block {name}")
+        assert torch.equal(got, periodic(got[:, :P])), f"{name}: a head past the first block differs"

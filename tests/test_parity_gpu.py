@@ -256,3 +256,34 @@ def test_causal_tile_order_groups(dtype, B, H, N, d):
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.fwd(q, k, v, w.scale, True)
     assert_close(o.cpu(), lse.cpu(), o_ref, lse_ref, dtype, f"{(dtype, B, H, N, d)}")
+
+
+# Tensors past 4 GiB: head base offsets beyond 2^31 and 2^32 bytes.  The
+# inputs repeat a seeded block of 97 heads along H on the device (97 does not
+# divide the 2^31 / 2^32-byte head counts, so an offset that wrapped at 32
+# bits would land on a head with other data).  The first block is checked
+# against the full oracle; every later head must equal its image in the first
+# block bitwise (a head's result depends only on its own data).
+PERIOD = 97
+
+
+def periodic(base, H):
+    reps = -(-H // base.shape[1])
+    return base.to(DEV).repeat(1, reps, 1, 1)[:, :H].contiguous()
+
+
+@pytest.mark.parametrize("dtype,H,d", [("bf16", 65600, 64), ("f32", 33000, 64)])
+def test_tensors_past_4gib(dtype, H, d):
+    N = 512
+    w, (q, k, v) = small_case(dtype, 1, PERIOD, N, d, False, seed=61)
+    e = 4 if dtype == "f32" else 2
+    assert H * N * d * e > 2 ** 32
+    _note(f"past 4 GiB {dtype} H={H} N={N} d={d}")
+    qd, kd, vd = periodic(q, H), periodic(k, H), periodic(v, H)
+    o, lse = binding.fwd(qd, kd, vd, w.scale, False)
+    torch.cuda.synchronize()
+    del qd, kd, vd
+    o_ref, lse_ref = oracle.fwd(q, k, v, w.scale, False)
+    assert_close(o[:, :PERIOD].cpu(), lse[:, :PERIOD].cpu(), o_ref, lse_ref, dtype, "first block")
+    assert torch.equal(o, periodic(o[:, :PERIOD], H)), "a head past the first block differs"
+    assert torch.equal(lse, periodic(lse[:, :PERIOD].unsqueeze(-1), H).squeeze(-1))
