@@ -89,6 +89,14 @@ def version() -> int:
     return int(load().fa_version())
 
 
+def _launch_stream(stream, device) -> torch.cuda.Stream:
+    """The stream a call runs on; tensors the binding allocates for the call are
+    allocated under it, so the caching allocator hands their memory to later
+    work only behind the call's kernels (a scratch tensor allocated under
+    another stream could be reused while the kernels still read it)."""
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
 def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream) -> int:
     """Raw C call with integer pointers; returns the fa_status code."""
     return int(load().fa_fwd(q, k, v, o, lse, int(B), int(H), int(N), int(d), float(scale),
@@ -115,16 +123,16 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None =
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor of q's shape and dtype")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
     st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                 B, H, N, d, scale, causal, _DTYPE_CODES[q.dtype], stream.cuda_stream)
     if st != FA_OK:
@@ -186,10 +194,12 @@ def fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | Non
         scale = 1.0 / math.sqrt(d)
     if num_splits is None:
         num_splits = default_splits(B, H, H_kv, N_q, N_kv, d, causal, dt)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.stream(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
     if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor of q's shape and dtype")
     if lse.shape != (B, H, N_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -198,11 +208,10 @@ def fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | Non
     if need < 0:
         raise FaError(2)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        with torch.cuda.stream(stream):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
     st = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                    B, H, H_kv, N_q, N_kv, d, scale, causal, dt, num_splits, ws_ptr, ws_len,
                    stream.cuda_stream)
@@ -229,16 +238,16 @@ def lse_combine(o_part: torch.Tensor, lse_part: torch.Tensor, dtype: torch.dtype
     if dtype not in _DTYPE_CODES:
         raise TypeError("dtype must be float32, bfloat16 or float16")
     S, rows, d = o_part.shape
-    if out is None:
-        out = torch.empty((rows, d), dtype=dtype, device=o_part.device)
-    if lse is None:
-        lse = torch.empty((rows,), dtype=torch.float32, device=o_part.device)
+    stream = _launch_stream(stream, o_part.device)
+    with torch.cuda.stream(stream):
+        if out is None:
+            out = torch.empty((rows, d), dtype=dtype, device=o_part.device)
+        if lse is None:
+            lse = torch.empty((rows,), dtype=torch.float32, device=o_part.device)
     if out.shape != (rows, d) or out.dtype != dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous [rows, d] tensor of dtype")
     if lse.shape != (rows,) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [rows] tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(o_part.device)
     st = fa_lse_combine(o_part.data_ptr(), lse_part.data_ptr(), S, rows, d, out.data_ptr(),
                         lse.data_ptr(), _DTYPE_CODES[dtype], stream.cuda_stream)
     if st != FA_OK:
@@ -301,10 +310,10 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         raise ValueError("lse must be a float32 [B, H, N_q] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.stream(stream):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr())
     code = _DTYPE_CODES[q.dtype]
@@ -314,7 +323,10 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         if num_splits is None:
             num_splits = bwd_default_splits(B, H, Hkv, Nq, Nk, d, causal, code)
         nbytes = bwd_workspace_bytes(B, H, Hkv, Nq, Nk, d, num_splits) if Hkv > 0 else 0
-        ws = torch.empty(max(nbytes, 0), dtype=torch.uint8, device=q.device) if nbytes > 0 else None
+        ws = None
+        if nbytes > 0:
+            with torch.cuda.stream(stream):
+                ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
         st = fa_bwd_ex(*ptrs, B, H, Hkv, Nq, Nk, d, scale, causal, code, num_splits,
                        ws.data_ptr() if ws is not None else None, nbytes, stream.cuda_stream)
     if st != FA_OK:

@@ -408,3 +408,31 @@ def test_bwd_tensors_past_4gib():
     for got, ref, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
         assert_grad_close(got[:, :P].cpu(), ref, "bf16", f"first block {name}")
         assert torch.equal(got, periodic(got[:, :P])), f"{name}: a head past the first block differs"
+
+
+# Calls on a side stream while the current stream at once allocates and
+# fills memory: the scratch the binding allocates for a call (the forward's
+# key-range workspace, the backward's row dot products and head-part
+# workspace) is allocated under the call's stream, so the caching allocator
+# cannot hand it to the current stream's work while the kernels still use it.
+def test_side_stream_scratch_is_not_reused_early():
+    w = Workload("side", "bf16", 2, 8, 2000, 128, True, 2600, Hkv=2)
+    q, k, v = make_inputs(w)
+    dout = upstream(w, 2601)
+    _note("side-stream scratch")
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, dout))
+    o_ref, lse_ref = binding.fwd_ex(qd, kd, vd, w.scale, True, num_splits=4)
+    g_ref = binding.bwd(qd, kd, vd, o_ref, lse_ref, gd, w.scale, True, num_splits=4)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o, lse = binding.fwd_ex(qd, kd, vd, w.scale, True, num_splits=4, stream=side)
+    junk = [torch.full((1 << 22,), float("nan"), device=DEV) for _ in range(8)]
+    g = binding.bwd(qd, kd, vd, o, lse, gd, w.scale, True, stream=side, num_splits=4)
+    junk += [torch.full((1 << 22,), float("nan"), device=DEV) for _ in range(8)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert len(junk) == 16
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+    for a, b, name in zip(g, g_ref, ("dQ", "dK", "dV")):
+        assert torch.equal(a, b), f"{name} on the side stream differs"
