@@ -1,6 +1,6 @@
 /*
- * fa.h -- libfa: exact FlashAttention forward pass for AMD Instinct MI355X
- * (gfx950), C ABI.
+ * fa.h -- libfa: exact FlashAttention forward and backward passes for AMD
+ * Instinct MI355X (gfx950), C ABI.
  *
  * The operation.  For each batch b, head h and query row i,
  *     O_i   = sum_j softmax_j(scale * q_i . k_j) * v_j
@@ -73,7 +73,8 @@ typedef enum {
  *          zero is a valid empty problem and returns FA_OK with no launch.
  *          Limits (else FA_ERR_SHAPE): B*H <= 2^31-1, one head's N x d
  *          array (plus 1024 rows) below 2^31 bytes, and the launch grid
- *          (B*H*ceil(N/128) workgroups) below 2^31.
+ *          (B*H*ceil(N/R) workgroups, where a workgroup takes R = 32 to 512
+ *          query rows by dtype, d and mask) below 2^31.
  * d        head dimension: 64 or 128.
  * scale    multiplier of the dot products (usually 1/sqrt(d)); finite, > 0.
  * causal   nonzero: key j is masked for query i when j > i.
