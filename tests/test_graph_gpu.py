@@ -1,4 +1,5 @@
-"""The forward and backward entry points inside a captured HIP graph (MI355X only).
+"""The entry points inside a captured HIP graph, and from several host
+threads at once (MI355X only).
 
 libfa's calls allocate nothing, clear nothing and never synchronise, so a
 caller can capture them (with the buffers torch allocates around them) into
@@ -88,3 +89,42 @@ def test_graph_replays_match_eager(name, w, splits, parts):
             assert float(np.max(np.abs(o - o_ref))) <= 2e-2
             rel = np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref)
             assert rel <= 5e-3, f"{name}: rel-L2 {rel:.2e}"
+
+
+def test_concurrent_host_threads():
+    # The library holds no mutable global state: calls from several host
+    # threads at once, each on its own stream with its own buffers (split
+    # forward with a workspace, backward with head parts), give the results
+    # of one thread calling alone, bitwise.
+    import threading
+
+    w = Workload("threads", "bf16", 1, 8, 600, 64, True, 75, Hkv=2, Nkv=900)
+    q, k, v = make_inputs(w)
+    g = make_upstream(w, 76)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    ref = _step(w, qd, kd, vd, gd, 3, 2)
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(t):
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.default_stream())
+            with torch.cuda.stream(s):
+                outs = [_step(w, qd, kd, vd, gd, 3, 2) for _ in range(4)]
+            s.synchronize()
+            results[t] = outs
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    assert not errors, errors
+    assert sorted(results) == [0, 1, 2, 3]
+    for t, outs in results.items():
+        for got in outs:
+            for a, b, what in zip(got, ref, ("O", "LSE", "dQ", "dK", "dV")):
+                assert torch.equal(a, b), f"thread {t}: {what} differs"
