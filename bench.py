@@ -9,8 +9,9 @@ non-causal.  Workloads with grouped K/V heads, their own key length or a key
 split (C1s, D1, G1, G2) run through ``fa_fwd_ex`` instead: one step is then
 the whole call (the split kernel and, when split, the combine kernel), with
 its workspace allocated before timing.  ``--pass bwd`` times the backward
-pass instead (``fa_bwd``: row dot products, dK/dV, dQ) on a square bf16/fp16
-workload, after one forward call that provides O and LSE; its FLOPs follow
+pass instead (``fa_bwd``: row dot products, dK/dV, dQ; for grouped K/V heads
+``fa_bwd_ex`` with its default head parts, plus their part sum) on the same
+workloads, after one forward call that provides O and LSE; its FLOPs follow
 the usual convention of 2.5x the forward's (five products of 2*d FLOPs per
 visible pair).  Prints ONE JSON line with:
 
