@@ -318,6 +318,12 @@ typedef struct {
   int causal;
   double *dq, *dk, *dv;  /* dq: [B*H, Nq, d]; dk, dv: [B*Hkv, Nk, d] */
   int64_t first, last;   /* this worker's K/V heads, b * Hkv + g */
+  /* Query rows of this worker: i with i % row_parts == row_part.  With more
+   * than one part, the worker adds its share of dK and dV of its single K/V
+   * head into the private [Nk, d] arrays pdk, pdv (the caller sums the parts
+   * in part order). */
+  int64_t row_part, row_parts;
+  double *pdk, *pdv;
 } bjob_t;
 
 /* Probabilities of query row i (q rows at element offset qhead) against the
@@ -356,14 +362,15 @@ static void* bwd_worker(void* arg) {
   for (int64_t bg = J->first; bg < J->last; ++bg) {
     const int64_t b = bg / J->Hkv, g = bg % J->Hkv;
     const int64_t kvhead = bg * Nk * d;
-    double *dk = J->dk + kvhead, *dv = J->dv + kvhead;
+    double* dk = J->row_parts > 1 ? J->pdk : J->dk + kvhead;
+    double* dv = J->row_parts > 1 ? J->pdv : J->dv + kvhead;
     for (int64_t e = 0; e < Nk * d; ++e) dk[e] = dv[e] = 0.0;
     for (int64_t hh = 0; hh < grp; ++hh) {
       const int64_t h = g * grp + hh;
       const int64_t qhead = (b * J->H + h) * Nq * d;
       double* dq = J->dq + qhead;
-      for (int64_t e = 0; e < Nq * d; ++e) dq[e] = 0.0;
-      for (int64_t i = 0; i < Nq; ++i) {
+      for (int64_t i = J->row_part; i < Nq; i += J->row_parts) {
+        for (int64_t c = 0; c < d; ++c) dq[i * d + c] = 0.0;
         const int64_t nvis = row_probs(J->q, J->k, J->dtype, Nq, Nk, d, J->scale, J->causal,
                                        qhead, kvhead, i, p);
         if (nvis == 0) continue;
@@ -398,12 +405,72 @@ static void* bwd_worker(void* arg) {
   return NULL;
 }
 
+/* One K/V head bg with its query rows split over nthreads workers: each
+ * worker sums its rows' dK, dV contributions privately, then the parts are
+ * added in part order (deterministic for a given thread count). */
+static int bwd_rows_parallel(const void* q, const void* k, const void* v, const void* dout,
+                             int dtype, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                             double scale, int causal, double* dq, double* dk, double* dv,
+                             int64_t bg, int nthreads) {
+  if (nthreads > Nq) nthreads = (int)Nq;
+  const size_t n = (size_t)(Nk * d);
+  bjob_t* jobs = (bjob_t*)calloc((size_t)nthreads, sizeof(bjob_t));
+  pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  double* priv = (double*)malloc(sizeof(double) * (n > 0 ? n : 1) * 2 * (size_t)nthreads);
+  if (!jobs || !tids || !priv) {
+    free(jobs); free(tids); free(priv);
+    return -2;
+  }
+  int rc = 0;
+  int* started = (int*)calloc((size_t)nthreads, sizeof(int));
+  if (!started) {
+    free(jobs); free(tids); free(priv);
+    return -2;
+  }
+  for (int t = 0; t < nthreads; ++t) {
+    bjob_t* J = &jobs[t];
+    J->q = q; J->k = k; J->v = v; J->dout = dout; J->dtype = dtype;
+    J->H = H; J->Hkv = Hkv; J->Nq = Nq; J->Nk = Nk; J->d = d;
+    J->scale = scale; J->causal = causal;
+    J->dq = dq; J->dk = dk; J->dv = dv;
+    J->first = bg;
+    J->last = bg + 1;
+    J->row_part = t;
+    J->row_parts = nthreads;
+    J->pdk = priv + 2 * n * (size_t)t;
+    J->pdv = J->pdk + n;
+    if (pthread_create(&tids[t], NULL, bwd_worker, J) == 0) {
+      started[t] = 1;
+    } else if (bwd_worker(J)) {
+      rc = -2;
+    }
+  }
+  for (int t = 0; t < nthreads; ++t) {
+    if (!started[t]) continue;
+    void* ret = NULL;
+    pthread_join(tids[t], &ret);
+    if (ret) rc = -2;
+  }
+  if (rc == 0) {
+    double *hk = dk + (size_t)bg * n, *hv = dv + (size_t)bg * n;
+    for (size_t e = 0; e < n; ++e) hk[e] = hv[e] = 0.0;
+    for (int t = 0; t < nthreads; ++t)
+      for (size_t e = 0; e < n; ++e) {
+        hk[e] += jobs[t].pdk[e];
+        hv[e] += jobs[t].pdv[e];
+      }
+  }
+  free(started); free(jobs); free(tids); free(priv);
+  return rc;
+}
+
 /*
  * oracle_bwd_gqa_f64 -- q, dout: contiguous [B, H, Nq, d]; k, v: [B, Hkv,
  * Nk, d], all of `dtype`; H a multiple of Hkv.  dq: [B, H, Nq, d] and dk,
  * dv: [B, Hkv, Nk, d] doubles, written in full.  Threads work on whole K/V
- * heads (and so on whole groups of query heads).  Returns 0, -1 on a bad
- * argument, -2 when out of memory.
+ * heads (and so on whole groups of query heads), or, with fewer K/V heads
+ * than threads, on the query rows of one head at a time.  Returns 0, -1 on a
+ * bad argument, -2 when out of memory.
  */
 int oracle_bwd_gqa_f64(const void* q, const void* k, const void* v, const void* dout, int dtype,
                        int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
@@ -416,6 +483,16 @@ int oracle_bwd_gqa_f64(const void* q, const void* k, const void* v, const void* 
   if (heads == 0 || (Nq == 0 && Nk == 0)) return 0;
   if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
   if (nthreads < 1) nthreads = 1;
+  /* Fewer K/V heads than threads: each head in turn, its query rows dealt
+   * round-robin to the threads (same sums, in another order). */
+  if (heads < nthreads && Nq > 1) {
+    for (int64_t bg = 0; bg < heads; ++bg) {
+      const int rc = bwd_rows_parallel(q, k, v, dout, dtype, H, Hkv, Nq, Nk, d, scale, causal,
+                                       dq, dk, dv, bg, nthreads);
+      if (rc) return rc;
+    }
+    return 0;
+  }
   if (nthreads > heads) nthreads = (int)heads;
   bjob_t* jobs = (bjob_t*)calloc((size_t)nthreads, sizeof(bjob_t));
   pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
@@ -433,6 +510,8 @@ int oracle_bwd_gqa_f64(const void* q, const void* k, const void* v, const void* 
     J->dq = dq; J->dk = dk; J->dv = dv;
     J->first = heads * t / nthreads;
     J->last = heads * (t + 1) / nthreads;
+    J->row_part = 0;
+    J->row_parts = 1;
     if (pthread_create(&tids[t], NULL, bwd_worker, J) != 0) {
       if (bwd_worker(J)) rc = -2;
       continue;

@@ -467,6 +467,29 @@ def test_gradients_match_torch_autograd_fp64(oracle_lib, dtype, causal, N, d):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_gradients_one_head_rows_split_over_threads(oracle_lib, causal):
+    # One K/V head with fewer heads than threads: the oracle deals the query
+    # rows of the head to its threads (each sums its own dK, dV share, the
+    # shares are added in order).  Against fp64 autograd, and against the
+    # one-thread result (same sums, another order).
+    B, H, N, d = 1, 1, 300, 16
+    q, k, v, g = (_rand((B, H, N, d), torch.bfloat16, seed=s) for s in (141, 142, 143, 144))
+    scale = 0.25
+    dq, dk, dv = oracle.bwd(q, k, v, g, scale, causal, threads=7)
+    q64, k64, v64 = (t.to(torch.float64).requires_grad_(True) for t in (q, k, v))
+    logits = scale * torch.matmul(q64, k64.transpose(-1, -2))
+    if causal:
+        logits = logits.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    o = torch.matmul(torch.softmax(logits, -1), v64)
+    o.backward(g.to(torch.float64))
+    for got, ref in ((dq, q64.grad), (dk, k64.grad), (dv, v64.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-11, atol=1e-12)
+    one = oracle.bwd(q, k, v, g, scale, causal, threads=1)
+    for a, b in zip((dq, dk, dv), one):
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_gradient_invariants(oracle_lib, causal):
     # Softmax rows are shift-invariant, so every dS row sums to zero and the
     # key gradients of a head sum to zero; the weights of a row sum to one,
