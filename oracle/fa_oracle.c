@@ -86,11 +86,23 @@ static double widen_f16(uint16_t bits) {
   return sign ? -mag : mag;
 }
 
+/* widen_f16 of every 16-bit pattern, filled once: the decode above costs an
+ * ldexp per element, and the passes below widen each K/V element once per
+ * query row. */
+static double f16_table[1 << 16];
+static pthread_once_t f16_once = PTHREAD_ONCE_INIT;
+
+static void fill_f16_table(void) {
+  for (uint32_t u = 0; u < (1u << 16); ++u) f16_table[u] = widen_f16((uint16_t)u);
+}
+
+static void widen_tables_ready(void) { pthread_once(&f16_once, fill_f16_table); }
+
 static double load_elem(const void* base, int dtype, int64_t idx) {
   switch (dtype) {
     case ORACLE_F32: return (double)((const float*)base)[idx];
     case ORACLE_BF16: return widen_bf16(((const uint16_t*)base)[idx]);
-    default: return widen_f16(((const uint16_t*)base)[idx]);
+    default: return f16_table[((const uint16_t*)base)[idx]];
   }
 }
 
@@ -119,7 +131,7 @@ typedef struct {
 } job_t;
 
 static void one_row(const job_t* J, int64_t flat, double* o_out, double* lse_out,
-                    double* s /* scratch, Nk doubles */) {
+                    double* s /* scratch, Nk doubles */, double* qi /* scratch, d doubles */) {
   const int64_t Nq = J->Nq, Nk = J->Nk, d = J->d;
   const int64_t bh = flat / Nq, i = flat % Nq;
   const int64_t b = bh / J->H, h = bh % J->H;
@@ -137,12 +149,11 @@ static void one_row(const job_t* J, int64_t flat, double* o_out, double* lse_out
   }
 
   /* pass 1: scaled scores and their maximum */
+  for (c = 0; c < d; ++c) qi[c] = load_elem(J->q, J->dtype, qhead + i * d + c);
   double m = -INFINITY;
   for (int64_t j = 0; j < nvis; ++j) {
     double dot = 0.0;
-    for (c = 0; c < d; ++c)
-      dot += load_elem(J->q, J->dtype, qhead + i * d + c) *
-             load_elem(J->k, J->dtype, kvhead + j * d + c);
+    for (c = 0; c < d; ++c) dot += qi[c] * load_elem(J->k, J->dtype, kvhead + j * d + c);
     s[j] = J->scale * dot;
     if (s[j] > m) m = s[j];
   }
@@ -161,11 +172,11 @@ static void one_row(const job_t* J, int64_t flat, double* o_out, double* lse_out
 
 static void* worker(void* arg) {
   const job_t* J = (const job_t*)arg;
-  double* s = (double*)malloc(sizeof(double) * (size_t)(J->Nk > 0 ? J->Nk : 1));
+  double* s = (double*)malloc(sizeof(double) * (size_t)((J->Nk > 0 ? J->Nk : 1) + J->d));
   if (!s) return (void*)1;
   for (int64_t r = J->first; r < J->last; ++r) {
     int64_t flat = J->rows ? J->rows[r] : r;
-    one_row(J, flat, J->o + r * J->d, J->lse + r, s);
+    one_row(J, flat, J->o + r * J->d, J->lse + r, s, s + (J->Nk > 0 ? J->Nk : 1));
   }
   free(s);
   return NULL;
@@ -182,6 +193,7 @@ int oracle_fwd_gqa_f64(const void* q, const void* k, const void* v, int dtype, i
                        int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, double scale,
                        int causal, const int64_t* rows, int64_t nrows, double* o, double* lse,
                        int nthreads) {
+  widen_tables_ready();
   if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return -1;
   if (B < 0 || H < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d <= 0 || nrows < 0) return -1;
   if (Hkv == 0 ? H != 0 : H % Hkv != 0) return -1;
@@ -329,16 +341,15 @@ typedef struct {
 /* Probabilities of query row i (q rows at element offset qhead) against the
  * keys at element offset kvhead, into p[0..nvis); returns nvis (0 when the
  * row sees no key). */
-static int64_t row_probs(const void* q, const void* k, int dtype, int64_t Nq, int64_t Nk,
-                         int64_t d, double scale, int causal, int64_t qhead, int64_t kvhead,
-                         int64_t i, double* p) {
+static int64_t row_probs(const double* qi /* query row i, widened */, const void* k, int dtype,
+                         int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
+                         int64_t kvhead, int64_t i, double* p) {
   const int64_t nvis = causal ? i + 1 + (Nk - Nq) : Nk;
   if (nvis <= 0) return 0;
   double m = -INFINITY;
   for (int64_t j = 0; j < nvis; ++j) {
     double dot = 0.0;
-    for (int64_t c = 0; c < d; ++c)
-      dot += load_elem(q, dtype, qhead + i * d + c) * load_elem(k, dtype, kvhead + j * d + c);
+    for (int64_t c = 0; c < d; ++c) dot += qi[c] * load_elem(k, dtype, kvhead + j * d + c);
     p[j] = scale * dot;
     if (p[j] > m) m = p[j];
   }
@@ -354,11 +365,13 @@ static void* bwd_worker(void* arg) {
   const int64_t grp = J->H / J->Hkv;
   double* p = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
   double* ds = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
-  double* o = (double*)malloc(sizeof(double) * (size_t)d);
+  double* o = (double*)malloc(sizeof(double) * (size_t)d * 3);
   if (!p || !ds || !o) {
     free(p); free(ds); free(o);
     return (void*)1;
   }
+  double* qi = o + d; /* query row i and its dO row, widened once per row */
+  double* gi = o + 2 * d;
   for (int64_t bg = J->first; bg < J->last; ++bg) {
     const int64_t b = bg / J->Hkv, g = bg % J->Hkv;
     const int64_t kvhead = bg * Nk * d;
@@ -370,9 +383,13 @@ static void* bwd_worker(void* arg) {
       const int64_t qhead = (b * J->H + h) * Nq * d;
       double* dq = J->dq + qhead;
       for (int64_t i = J->row_part; i < Nq; i += J->row_parts) {
-        for (int64_t c = 0; c < d; ++c) dq[i * d + c] = 0.0;
-        const int64_t nvis = row_probs(J->q, J->k, J->dtype, Nq, Nk, d, J->scale, J->causal,
-                                       qhead, kvhead, i, p);
+        for (int64_t c = 0; c < d; ++c) {
+          dq[i * d + c] = 0.0;
+          qi[c] = load_elem(J->q, J->dtype, qhead + i * d + c);
+          gi[c] = load_elem(J->dout, J->dtype, qhead + i * d + c);
+        }
+        const int64_t nvis = row_probs(qi, J->k, J->dtype, Nq, Nk, d, J->scale, J->causal,
+                                       kvhead, i, p);
         if (nvis == 0) continue;
         /* O_i and D_i = dO_i . O_i */
         for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
@@ -380,15 +397,13 @@ static void* bwd_worker(void* arg) {
           for (int64_t c = 0; c < d; ++c)
             o[c] += p[j] * load_elem(J->v, J->dtype, kvhead + j * d + c);
         double D = 0.0;
-        for (int64_t c = 0; c < d; ++c)
-          D += load_elem(J->dout, J->dtype, qhead + i * d + c) * o[c];
+        for (int64_t c = 0; c < d; ++c) D += gi[c] * o[c];
         /* dP_ij, dS_ij; dV_j += P_ij dO_i */
         for (int64_t j = 0; j < nvis; ++j) {
           double dp = 0.0;
           for (int64_t c = 0; c < d; ++c) {
-            const double g = load_elem(J->dout, J->dtype, qhead + i * d + c);
-            dp += g * load_elem(J->v, J->dtype, kvhead + j * d + c);
-            dv[j * d + c] += p[j] * g;
+            dp += gi[c] * load_elem(J->v, J->dtype, kvhead + j * d + c);
+            dv[j * d + c] += p[j] * gi[c];
           }
           ds[j] = p[j] * (dp - D);
         }
@@ -396,7 +411,7 @@ static void* bwd_worker(void* arg) {
         for (int64_t j = 0; j < nvis; ++j)
           for (int64_t c = 0; c < d; ++c) {
             dq[i * d + c] += J->scale * ds[j] * load_elem(J->k, J->dtype, kvhead + j * d + c);
-            dk[j * d + c] += J->scale * ds[j] * load_elem(J->q, J->dtype, qhead + i * d + c);
+            dk[j * d + c] += J->scale * ds[j] * qi[c];
           }
       }
     }
@@ -476,6 +491,7 @@ int oracle_bwd_gqa_f64(const void* q, const void* k, const void* v, const void* 
                        int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                        double scale, int causal, double* dq, double* dk, double* dv,
                        int nthreads) {
+  widen_tables_ready();
   if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return -1;
   if (B < 0 || H < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d <= 0) return -1;
   if ((H == 0) != (Hkv == 0) || (Hkv > 0 && H % Hkv != 0)) return -1;
@@ -546,6 +562,7 @@ int oracle_bwd_dq_rows_gqa_f64(const void* q, const void* k, const void* v, cons
                                int dtype, int64_t B, int64_t H, int64_t Hkv, int64_t Nq,
                                int64_t Nk, int64_t d, double scale, int causal,
                                const int64_t* rows, int64_t nrows, double* dq) {
+  widen_tables_ready();
   if (dtype < ORACLE_F32 || dtype > ORACLE_F16) return -1;
   if (B < 0 || H < 0 || Hkv <= 0 || Nq < 0 || Nk < 0 || d <= 0 || nrows < 0) return -1;
   if (H % Hkv != 0) return -1;
@@ -554,18 +571,22 @@ int oracle_bwd_dq_rows_gqa_f64(const void* q, const void* k, const void* v, cons
   for (int64_t r = 0; r < nrows; ++r)
     if (rows[r] < 0 || rows[r] >= B * H * Nq) return -1;
   double* p = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
-  double* o = (double*)malloc(sizeof(double) * (size_t)d);
+  double* o = (double*)malloc(sizeof(double) * (size_t)d * 2);
   if (!p || !o) {
     free(p); free(o);
     return -2;
   }
+  double* qi = o + d;
   for (int64_t r = 0; r < nrows; ++r) {
     const int64_t bh = rows[r] / Nq, i = rows[r] % Nq;
     const int64_t b = bh / H, h = bh % H;
     const int64_t qhead = bh * Nq * d, kvhead = (b * Hkv + h / (H / Hkv)) * Nk * d;
     double* out = dq + r * d;
-    for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
-    const int64_t nvis = row_probs(q, k, dtype, Nq, Nk, d, scale, causal, qhead, kvhead, i, p);
+    for (int64_t c = 0; c < d; ++c) {
+      out[c] = 0.0;
+      qi[c] = load_elem(q, dtype, qhead + i * d + c);
+    }
+    const int64_t nvis = row_probs(qi, k, dtype, Nq, Nk, d, scale, causal, kvhead, i, p);
     if (nvis == 0) continue;
     for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
     for (int64_t j = 0; j < nvis; ++j)

@@ -21,12 +21,12 @@ MUTANTS = {
     "causal_offset_sign": ("J->causal ? i + 1 + (Nk - Nq) : Nk",
                            "J->causal ? i + 1 - (Nk - Nq) : Nk"),
     "dropped_scale": ("s[j] = J->scale * dot;", "s[j] = dot;"),
-    "key_row_index": ("*\n             load_elem(J->k, J->dtype, kvhead + j * d + c)",
-                      "*\n             load_elem(J->k, J->dtype, kvhead + i * d + c)"),
+    "key_row_index": ("qi[c] * load_elem(J->k, J->dtype, kvhead + j * d + c)",
+                      "qi[c] * load_elem(J->k, J->dtype, kvhead + i * d + c)"),
     "value_row_index": ("o_out[c] += p * load_elem(J->v, J->dtype, kvhead + j * d + c)",
                         "o_out[c] += p * load_elem(J->v, J->dtype, kvhead + i * d + c)"),
-    "transposed_query": ("dot += load_elem(J->q, J->dtype, qhead + i * d + c)",
-                         "dot += load_elem(J->q, J->dtype, qhead + c * Nq + i)"),
+    "transposed_query": ("(c = 0; c < d; ++c) qi[c] = load_elem(J->q, J->dtype, qhead + i * d + c)",
+                         "(c = 0; c < d; ++c) qi[c] = load_elem(J->q, J->dtype, qhead + c * Nq + i)"),
     "dropped_normalisation": ("double p = exp(s[j] - m) / l;", "double p = exp(s[j] - m);"),
     "lse_sign": ("*lse_out = m + log(l);", "*lse_out = m - log(l);"),
     "lse_dropped_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
@@ -46,9 +46,9 @@ MUTANTS = {
                                   "(out[c] + a_new * ot[c]) / l_new"),
     "combine_lse_sign": ("lse[r] = l > 0.0 ? m + log(l)", "lse[r] = l > 0.0 ? m - log(l)"),
     "bwd_dropped_row_dot": ("ds[j] = p[j] * (dp - D);", "ds[j] = p[j] * dp;"),
-    "bwd_dk_from_keys": ("dk[j * d + c] += J->scale * ds[j] * load_elem(J->q,",
-                         "dk[j * d + c] += J->scale * ds[j] * load_elem(J->k,"),
-    "bwd_dv_from_ds": ("dv[j * d + c] += p[j] * g;", "dv[j * d + c] += ds[j] * g;"),
+    "bwd_dk_from_keys": ("dk[j * d + c] += J->scale * ds[j] * qi[c];",
+                         "dk[j * d + c] += J->scale * ds[j] * load_elem(J->k, J->dtype, kvhead + j * d + c);"),
+    "bwd_dv_from_ds": ("dv[j * d + c] += p[j] * gi[c];", "dv[j * d + c] += ds[j] * gi[c];"),
     "bwd_dq_dropped_scale": ("dq[i * d + c] += J->scale * ds[j] *", "dq[i * d + c] += ds[j] *"),
     "bwd_causal_bound": ("const int64_t nvis = causal ? i + 1 + (Nk - Nq) : Nk;",
                          "const int64_t nvis = causal ? i + (Nk - Nq) : Nk;"),
@@ -56,7 +56,7 @@ MUTANTS = {
                                "const int64_t nvis = causal ? i + 1 - (Nk - Nq) : Nk;"),
     "bwd_rows_dropped_row_dot": ("const double ds = p[j] * (dp - D);",
                                  "const double ds = p[j] * dp;"),
-    "bwd_row_dot_from_v": ("D += load_elem(J->dout, J->dtype, qhead + i * d + c) * o[c];",
+    "bwd_row_dot_from_v": ("D += gi[c] * o[c];",
                            "D += load_elem(J->v, J->dtype, qhead + i * d + c) * o[c];"),
     "bwd_group_member": ("const int64_t h = g * grp + hh;", "const int64_t h = hh * J->Hkv + g;"),
     "bwd_group_sum_dropped": (
@@ -66,6 +66,9 @@ MUTANTS = {
         "      for (int64_t e = 0; e < Nk * d; ++e) dk[e] = dv[e] = 0.0;"),
     "bwd_rows_kv_map": ("kvhead = (b * Hkv + h / (H / Hkv)) * Nk * d;",
                         "kvhead = (b * Hkv + h % Hkv) * Nk * d;"),
+    "bwd_row_parts_overwrite": ("hk[e] += jobs[t].pdk[e];", "hk[e] = jobs[t].pdk[e];"),
+    "f16_table_index": ("f16_table[((const uint16_t*)base)[idx]]",
+                        "f16_table[((const uint16_t*)base)[idx] ^ 1u]"),
 }
 
 
