@@ -105,9 +105,9 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  *   - grouped heads: H_kv divides H and query head h reads K/V head
  *     h / (H / H_kv) (H_kv = H is ordinary multi-head attention, H_kv = 1
  *     shares one K/V head among all query heads).  The pages only name the
- *     technique ("FlashAttention dissected", section "Interaction with the
- *     KV cache during inference": several query heads share the same key and
- *     value heads);
+ *     technique, grouped-query attention, which maps a group of query heads
+ *     onto one K/V head ("FlashAttention dissected", section "Interaction
+ *     with the KV cache during inference");
  *   - causal masking is aligned to the end of the keys: key j is masked for
  *     query i when j > i + (N_kv - N_q), so that query row i stands at key
  *     position N_kv - N_q + i, as a decoding step that appends N_q tokens to

@@ -8,9 +8,8 @@ Tolerances (fixed by the task for the forward output):
   * fp32 inputs: max |O - O_ref| <= 1e-4 and max |LSE - LSE_ref| <= 1e-4;
   * bf16/fp16 inputs: max |O - O_ref| <= 2e-2 and
     ||O - O_ref||_2 / ||O_ref||_2 <= 5e-3, max |LSE - LSE_ref| <= 2e-2.
-At full workload sizes the oracle recomputes a sample of rows (corners of the
-first and last head, the ragged tail and uniformly drawn rows); the rel-L2 is
-then taken over those rows.
+Every workload is compared with the oracle at its full size, row by row
+(the longest single-head case, 131072 keys, on a row sample).
 """
 import math
 import sys
@@ -123,21 +122,47 @@ def test_workload_full_oracle(name):
 
 
 @pytest.mark.parametrize("name", ["C3", "C4", "C5"])
-def test_workload_sampled_rows(name):
+def test_workload_every_row(name):
+    # Full size, every row against the oracle (about 10 s for C3 and 20 s
+    # each for C4 and C5 of fp64 work on 16 host threads).  O and LSE start
+    # as NaN, so a query tile the grid skipped or a row no wave stored fails
+    # even if its neighbours are right; C3 (128 causal units of 32 query
+    # tiles, 16 units per die) runs the grouped heavy-first tile order at its
+    # full size.
     w = WORKLOADS[name]
     q, k, v = make_inputs(w)
-    _note(f"workload {name} sampled")
-    o, lse = run_gpu(q, k, v, w.scale, w.causal)
-    rows = sample_rows(w, 768)
-    o_ref, lse_ref = oracle.fwd(q, k, v, w.scale, w.causal, rows=rows)
-    o_s = o.reshape(-1, w.d)[torch.from_numpy(rows)]
-    l_s = lse.reshape(-1)[torch.from_numpy(rows)]
-    assert_close(o_s, l_s, o_ref, lse_ref, w.dtype, name)
-    # properties at every row: finite outputs, |O| bounded by max|V| (O is a
-    # convex combination of value rows), LSE >= the row's own-score bound
-    vmax = float(v.abs().max())
-    assert torch.isfinite(lse).all()
-    assert float(o.float().abs().max()) <= vmax * (1 + 1e-2)
+    _note(f"workload {name} every row")
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=DEV)
+    binding.fwd(qd, kd, vd, w.scale, w.causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    del qd, kd, vd
+    # the oracle a few heads at a time (heads are independent problems)
+    o_ref = np.empty((w.B, w.H, w.N, w.d))
+    lse_ref = np.empty((w.B, w.H, w.N))
+    step = 4
+    for b in range(w.B):
+        for h0 in range(0, w.H, step):
+            sl = (slice(b, b + 1), slice(h0, h0 + step))
+            o_ref[sl], lse_ref[sl] = oracle.fwd(q[sl], k[sl], v[sl], w.scale, w.causal)
+            _note(f"  oracle {name} b={b} heads {h0}..{min(w.H, h0 + step) - 1}")
+    assert_close(o, lse, o_ref, lse_ref, w.dtype, name)
+    # and per (batch, head, 128-row query block): a block whose rows were
+    # computed against the wrong head or range stands out even when the
+    # tensor-wide rel-L2 is small
+    blk = 128
+    nb = -(-w.N // blk)
+    og = o.to(torch.float64).numpy()
+    for b in range(w.B):
+        for h in range(w.H):
+            for t in range(nb):
+                sl = slice(t * blk, min(w.N, (t + 1) * blk))
+                ref = o_ref[b, h, sl]
+                err = np.linalg.norm(og[b, h, sl] - ref) / max(np.linalg.norm(ref), 1e-300)
+                bound = 1e-4 * 10 if w.dtype == "f32" else 2e-2
+                assert err <= bound, f"{name}: block (b={b}, h={h}, rows {sl}) rel-L2 {err:.3e}"
 
 
 # --------------------------------------------------------------------------
