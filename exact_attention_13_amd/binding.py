@@ -19,13 +19,15 @@ FA_F32, FA_BF16, FA_F16 = 0, 1, 2
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM",
                 4: "FA_ERR_DTYPE", 5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ALIAS",
-                8: "FA_ERR_LAUNCH", 9: "FA_ERR_WORKSPACE"}
+                8: "FA_ERR_LAUNCH", 9: "FA_ERR_WORKSPACE", 10: "FA_ERR_SCRATCH"}
+# Bytes of fa_fwd_ex_noalloc's static device scratch (FA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 _DTYPE_CODES = {torch.float32: FA_F32, torch.bfloat16: FA_BF16, torch.float16: FA_F16}
 
 # Every symbol include/fa.h declares.
 EXPORTED = ("fa_bwd", "fa_bwd_ex", "fa_bwd_ex_default_splits", "fa_bwd_ex_workspace_bytes",
-            "fa_fwd", "fa_fwd_ex", "fa_fwd_ex_default_splits", "fa_fwd_ex_workspace_bytes",
-            "fa_lse_combine", "fa_strerror", "fa_version")
+            "fa_fwd", "fa_fwd_ex", "fa_fwd_ex_default_splits", "fa_fwd_ex_noalloc",
+            "fa_fwd_ex_workspace_bytes", "fa_lse_combine", "fa_strerror", "fa_version")
 
 _lib = None
 
@@ -55,6 +57,9 @@ def load() -> ctypes.CDLL:
         lib.fa_fwd_ex.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_void_p]
+        lib.fa_fwd_ex_noalloc.restype = ctypes.c_int
+        lib.fa_fwd_ex_noalloc.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 6 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
         lib.fa_fwd_ex_workspace_bytes.restype = ctypes.c_int64
         lib.fa_fwd_ex_workspace_bytes.argtypes = [ctypes.c_int64] * 6
         lib.fa_fwd_ex_default_splits.restype = ctypes.c_int64
@@ -146,6 +151,14 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, dtype, n
     return int(load().fa_fwd_ex(q, k, v, o, lse, int(B), int(H), int(H_kv), int(N_q), int(N_kv),
                                 int(d), float(scale), int(bool(causal)), int(dtype),
                                 int(num_splits), workspace, int(workspace_bytes), stream))
+
+
+def fa_fwd_ex_noalloc(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, dtype,
+                      num_splits, stream) -> int:
+    """Raw C call with integer pointers; returns the fa_status code."""
+    return int(load().fa_fwd_ex_noalloc(q, k, v, o, lse, int(B), int(H), int(H_kv), int(N_q),
+                                        int(N_kv), int(d), float(scale), int(bool(causal)),
+                                        int(dtype), int(num_splits), stream))
 
 
 def workspace_bytes(B, H, N_q, N_kv, d, num_splits) -> int:

@@ -1,6 +1,8 @@
 // fa_api.hip -- the C ABI of libfa (declared in include/fa.h): argument
 // validation on the host, choice of kernel instance, launch on the caller's
-// stream.  No allocation, no synchronisation, no global mutable state.
+// stream.  No allocation and no synchronisation; the only global state is the
+// cached device address of the static scratch of fa_fwd_ex_noalloc (set once
+// per device under a mutex).
 //
 // The error surface follows the GitHub README "CUDA Flash Attention...",
 // "Correctness Audit": a fixed head size is checked instead of assumed
@@ -10,12 +12,15 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "fa.h"
 #include "fa_api_util.hpp"
 #include "fa_device.hpp"
 
 #define LIBFA_VERSION_MAJOR 0
-#define LIBFA_VERSION_MINOR 4
+#define LIBFA_VERSION_MINOR 5
 #define LIBFA_VERSION_PATCH 0
 
 using namespace fa_api;
@@ -108,13 +113,17 @@ fa_status check_sizes(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N
   return FA_OK;
 }
 
-}  // namespace
+void* device_scratch_for(void* stream);
 
-extern "C" fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv,
-                               int64_t d, float scale, int causal, fa_dtype dtype,
-                               int64_t num_splits, void* workspace, int64_t workspace_bytes,
-                               void* stream) {
+// The whole extended forward call.  `workspace` is the caller's buffer
+// (fa_fwd_ex); with static_ws (fa_fwd_ex_noalloc) the partials go to the
+// static scratch of the stream's device instead, whose address is looked up
+// only after every argument has been validated, and partials larger than
+// workspace_bytes (the scratch size) report FA_ERR_SCRATCH.
+fa_status fwd_ex_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t d,
+                      float scale, int causal, fa_dtype dtype, int64_t num_splits,
+                      void* workspace, int64_t workspace_bytes, void* stream, bool static_ws) {
   fa_status st = check_ex(q, k, v, o, B, H, H_kv, N_q, N_kv, d, scale, dtype);
   if (st != FA_OK) return st;
   if (num_splits < 1) return FA_ERR_WORKSPACE;
@@ -142,6 +151,11 @@ extern "C" fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void
     return FA_ERR_ALIAS;
 
   const int64_t wbytes = splits > 1 ? splits * p.rows * (d + 1) * 4 : 0;
+  if (splits > 1 && static_ws) {
+    if (wbytes > workspace_bytes) return FA_ERR_SCRATCH;
+    workspace = device_scratch_for(stream);
+    if (!workspace) return FA_ERR_LAUNCH;
+  }
   if (splits > 1) {
     if (!workspace || workspace_bytes < wbytes || !aligned(workspace, 16))
       return FA_ERR_WORKSPACE;
@@ -179,6 +193,73 @@ extern "C" fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void
   if (st != FA_OK || !split) return st;
   return launch_status(fa_impl::launch_lse_combine(ws_o, ws_lse, (int)splits, p.rows, (int)d, o,
                                                    lse, (int)dtype, s));
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate (fa_fwd_ex_noalloc).
+//
+// `scratch` is a device array in the library's code object: every GPU the
+// library runs on holds its own copy, at its own address, from the first
+// use until the process ends.  In host code the name is only a stand-in for
+// the symbol; the device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and cached here, and only
+// that address is ever passed to a kernel.  The split kernels write every
+// partial row of their ranges before the combine reads it, so nothing has to
+// be cleared between calls.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on `dev` (nullptr when the lookup fails).
+void* device_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (ptr) return ptr;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* addr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess || !addr) return nullptr;
+  g_scratch_ptr[dev].store(addr, std::memory_order_release);
+  return addr;
+}
+
+// The scratch of the device that runs `stream` (the current device for the
+// null stream).
+void* device_scratch_for(void* stream) {
+  int dev = -1;
+  if (stream ? hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess
+             : hipGetDevice(&dev) != hipSuccess)
+    return nullptr;
+  return device_scratch(dev);
+}
+
+}  // namespace
+
+extern "C" fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv,
+                               int64_t d, float scale, int causal, fa_dtype dtype,
+                               int64_t num_splits, void* workspace, int64_t workspace_bytes,
+                               void* stream) {
+  return fwd_ex_impl(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, dtype, num_splits,
+                     workspace, workspace_bytes, stream, false);
+}
+
+extern "C" fa_status fa_fwd_ex_noalloc(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, int64_t B, int64_t H, int64_t H_kv,
+                                       int64_t N_q, int64_t N_kv, int64_t d, float scale,
+                                       int causal, fa_dtype dtype, int64_t num_splits,
+                                       void* stream) {
+  return fwd_ex_impl(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, dtype, num_splits,
+                     nullptr, FA_NOALLOC_SCRATCH_BYTES, stream, true);
 }
 
 extern "C" fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -263,6 +344,9 @@ extern "C" const char* fa_strerror(fa_status s) {
     case FA_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
     case FA_ERR_WORKSPACE:
       return "num_splits is below 1, or the workspace is null, too small or misaligned";
+    case FA_ERR_SCRATCH:
+      return "the split partials exceed the static scratch of fa_fwd_ex_noalloc "
+             "(FA_NOALLOC_SCRATCH_BYTES); use fewer splits or fa_fwd_ex with a workspace";
   }
   return "unknown fa_status value";
 }

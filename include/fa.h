@@ -55,8 +55,12 @@ typedef enum {
   FA_ERR_ALIGN = 6,    /* a tensor not 16-byte aligned, lse not 4-byte          */
   FA_ERR_ALIAS = 7,    /* an output or the workspace overlaps another buffer    */
   FA_ERR_LAUNCH = 8,   /* the HIP runtime refused the kernel launch             */
-  FA_ERR_WORKSPACE = 9 /* num_splits < 1, or workspace null, small or misaligned */
+  FA_ERR_WORKSPACE = 9, /* num_splits < 1, or workspace null, small or misaligned */
+  FA_ERR_SCRATCH = 10   /* fa_fwd_ex_noalloc: partials exceed its static scratch */
 } fa_status;
+
+/* Bytes of the static device scratch of fa_fwd_ex_noalloc (per GPU). */
+#define FA_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
 
 /*
  * fa_fwd -- O = softmax(Q K^T * scale) V and the per-row logsumexp.
@@ -141,6 +145,36 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
                     int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv, int64_t d,
                     float scale, int causal, fa_dtype dtype, int64_t num_splits,
                     void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_ex_noalloc -- fa_fwd_ex for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same operation, arguments, validation and results as
+ * fa_fwd_ex with the same num_splits (bitwise: the same kernels run), minus
+ * the workspace arguments: the split partials go to a static device array
+ * of FA_NOALLOC_SCRATCH_BYTES (32 MiB) that every GPU the library runs on
+ * holds from the first call until the process ends.  The call allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library routine).
+ *
+ * The partials of a call need fa_fwd_ex_workspace_bytes(B, H, N_q, N_kv, d,
+ * num_splits) bytes; more than FA_NOALLOC_SCRATCH_BYTES returns
+ * FA_ERR_SCRATCH and launches nothing (use fewer splits, or fa_fwd_ex).  An
+ * unsplit call (num_splits = 1, or keys too few to split) does not touch the
+ * scratch.  The first split call on a device looks up that device's scratch
+ * address once (hipGetSymbolAddress, with the device of `stream` current for
+ * the lookup); FA_ERR_LAUNCH reports a failed lookup.
+ *
+ * Every call on one GPU shares that GPU's scratch: two split calls whose
+ * kernels may overlap in time (different streams without ordering, or
+ * different host threads) race on it and can corrupt each other's results.
+ * Order such calls on one stream, or synchronise them.  Nothing needs to be
+ * cleared between calls (each split writes all of its partials before the
+ * merge reads them).
+ */
+fa_status fa_fwd_ex_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv,
+                            int64_t d, float scale, int causal, fa_dtype dtype,
+                            int64_t num_splits, void* stream);
 
 /* Workspace bytes fa_fwd_ex needs for `num_splits` (0 when the call runs
  * unsplit; -1 when the size overflows int64).  Invalid sizes give 0. */

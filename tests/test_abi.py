@@ -42,8 +42,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert libfa.version() == 400
-    for code in range(10):
+    assert libfa.version() == 500
+    for code in range(11):
         msg = libfa.strerror(code)
         assert msg and "unknown" not in msg
     assert "unknown" in libfa.strerror(99)
@@ -161,6 +161,41 @@ def test_fwd_ex_no_keys_allows_null_kv():
     assert call_ex(k=None, v=None, N_kv=0, N_q=0, num_splits=1, workspace=None) == 0
     # fa_fwd keeps requiring every pointer
     assert call(k=None, N=0) == 1
+
+
+def call_noalloc(**kw):
+    a = dict(EX_ARGS)
+    a.update(kw)
+    return libfa.fa_fwd_ex_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                   a["H_kv"], a["N_q"], a["N_kv"], a["d"], a["scale"],
+                                   a["causal"], a["dtype"], a["num_splits"], a["stream"])
+
+
+# fa_fwd_ex_noalloc validates like fa_fwd_ex, before it looks up (or uses)
+# the GPU's static scratch; partials beyond that scratch are FA_ERR_SCRATCH.
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(k=None), 1), (dict(H_kv=3), 2),
+    (dict(N_q=-1), 2), (dict(N_kv=1 << 31), 2), (dict(d=96), 3), (dict(dtype=5), 4),
+    (dict(scale=0.0), 5), (dict(q=Q + 4), 6), (dict(o=V + 64), 7), (dict(lse=O), 7),
+    (dict(num_splits=0), 9),
+    # 64 ranges of 262144 rows of d = 128: 8.6 GB of partials
+    (dict(B=1, H=64, H_kv=64, N_q=4096, N_kv=65536, num_splits=64), 10),
+])
+def test_fwd_ex_noalloc_rejects(kw, status):
+    assert call_noalloc(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0, H_kv=0), dict(N_q=0),
+                                dict(B=0, num_splits=8)])
+def test_fwd_ex_noalloc_empty_is_a_noop(kw):
+    assert call_noalloc(**kw) == 0
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = HEADER.read_text()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \((\d+) \* 1024 \* 1024\)", text)
+    assert m and int(m.group(1)) * 1024 * 1024 == libfa.NOALLOC_SCRATCH_BYTES
+    assert libfa.strerror(10).startswith("the split partials exceed the static scratch")
 
 
 def test_workspace_bytes():
