@@ -23,14 +23,18 @@ visible pair).  Prints ONE JSON line with:
                         launch, against the MI355X dense MFMA peak of the
                         input dtype, or against HBM bandwidth (8 TB/s)
                         when the workload's FLOP per algorithmic byte is
-                        below the ridge point; ``traffic`` is the HBM bytes per launch
+                        below the ridge point; ``hbm_gbs`` is the algorithmic
+                        bytes (Q, K, V read once, O and LSE written once) over
+                        that duration; ``traffic`` is the HBM bytes per launch
                         from the committed rocprofv3 counter summary when it
                         was taken on the current kernel source, else null;
                         ``kernel_ms_cold_median`` times further calls made
                         right after reading a 512 MiB buffer (L2 and MALL
                         flushed), so K/V start from HBM;
   cpu_baseline          the fp64 oracle timed on the host cores on a bounded
-                        row sample of the same workload (reported baseline).
+                        row sample of the same workload (reported baseline),
+                        with the CPU model, the host's core counts, the
+                        threads used, and the whole C1 workload on one thread.
 """
 from __future__ import annotations
 
@@ -128,9 +132,52 @@ def cpu_baseline(w, q, k, v, target_s: float):
     oracle.fwd_gqa(q, k, v, w.scale, w.causal, rows=rows, threads=threads)
     dt = time.perf_counter() - t0
     fl = rows_flops(rows)
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{want} of {total} query rows (uniform, seed 99) of the same workload, "
-                      f"{fl:.3e} FLOPs in {dt:.1f} s, fp64 three-pass, {threads} threads"}
+    out = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{want} of {total} query rows (uniform, seed 99) of the same workload, "
+                     f"{fl:.3e} FLOPs in {dt:.1f} s, fp64 three-pass, {threads} threads"}
+    out.update(host_cpu(threads))
+    out["one_thread_C1"] = one_thread_c1()
+    return out
+
+
+def host_cpu(threads: int) -> dict:
+    """The host the oracle ran on: CPU model, cores the process may use, and
+    the thread count taken (all of them up to 16, the host share of one GPU
+    on the measurement boxes)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    return {"cpu_model": model, "host_logical_cpus": os.cpu_count(),
+            "affinity_cpus": affinity, "threads_used": threads,
+            "thread_cap": "min(affinity, 16)"}
+
+
+def one_thread_c1() -> dict:
+    """The whole C1 workload (fp32, one 512-row head, d = 64) on one thread:
+    the kind of single-threaded CPU figure the pages report."""
+    from exact_attention_13_amd.inputs import WORKLOADS, make_inputs
+    import oracle
+    w = WORKLOADS["C1"]
+    q, k, v = make_inputs(w)
+    oracle.fwd(q, k, v, w.scale, w.causal, threads=1)  # warm (library load)
+    best = None
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.fwd(q, k, v, w.scale, w.causal, threads=1)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    return {"ms": round(best * 1e3, 3), "GFLOP/s": round(w.flops / best / 1e9, 3),
+            "workload": "C1: fp32 B=1 H=1 N=512 d=64, fp64 oracle, 1 thread, best of 3"}
 
 
 def cpu_baseline_bwd(w, q, k, v, dout, target_s: float):
@@ -373,6 +420,7 @@ def main():
                                if args.which == "bwd"
                                else "fa_fwd_ex call: split kernel + combine kernel" if splits > 1
                                else "one forward kernel"),
+                     "hbm_gbs": round(w.io_bytes / (avg_kernel_ms * 1e-3) / 1e9, 1),
                      "kernel_ms_avg": round(avg_kernel_ms, 5),
                      "kernel_ms_min": round(kernel_ms[0], 5),
                      "kernel_ms_median": round(kernel_ms[len(kernel_ms) // 2], 5),

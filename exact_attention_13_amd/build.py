@@ -69,5 +69,31 @@ def build(verbose: bool = False) -> Path:
     return LIB
 
 
+def resource_table() -> str:
+    """The last build's per-kernel resource report as a markdown table:
+    registers (VGPR, AGPR, SGPR), spills and scratch, LDS and occupancy."""
+    text = (BUILD_DIR / "kernel_resources.txt").read_text()
+    rows = []
+    for block in text.split("Function Name: ")[1:]:
+        name = block.split("\n", 1)[0].strip()
+        f = dict(re.findall(r"^([A-Za-z][A-Za-z /]*(?:\[[^\]]*\])?):\s*(\S+)", block, re.M))
+        demangled = subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip()
+        demangled = demangled.replace("fa_impl::(anonymous namespace)::", "").replace(
+            "fa_impl::", "")
+        demangled = re.sub(r"\(.*\)$", "", demangled)
+        rows.append((demangled or name, f.get("VGPRs"), f.get("AGPRs"), f.get("TotalSGPRs"),
+                     f.get("VGPRs Spill"), f.get("ScratchSize [bytes/lane]"),
+                     f.get("LDS Size [bytes/block]"), f.get("Occupancy [waves/SIMD]")))
+    out = ["| kernel | VGPR | AGPR | SGPR | VGPR spill | scratch B/lane | LDS B/block | waves/SIMD |",
+           "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append("| `" + r[0] + "` | " + " | ".join(str(x) for x in r[1:]) + " |")
+    return "\n".join(out) + "\n"
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose="--quiet" not in sys.argv))
+    if "--report" in sys.argv:
+        dest = Path(sys.argv[sys.argv.index("--report") + 1])
+        dest.write_text(resource_table())
+        print(dest)

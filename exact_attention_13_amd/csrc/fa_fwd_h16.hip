@@ -32,10 +32,11 @@
 //     is still -inf (no visible key yet) uses a shift of 0, so
 //     -inf - (-inf) never forms a NaN (GitHub README, "NaN guard").
 //   * P is rounded to bf16/fp16 (nearest-even) and is, unchanged, the
-//     B operand of O^T = V^T P^T; the row sum l adds the same rounded pairs
-//     with v_dot2c, which runs in the matrix pipe: on gfx950 plain VALU work
-//     and MFMAs compete for the same issue resources, while the matrix pipe
-//     has room to spare.
+//     B operand of O^T = V^T P^T.  The row sum l adds the same rounded pairs
+//     with one v_dot2c per pair at d = 64, whose register budget leaves no
+//     room for the unrounded weights, and the unrounded fp32 weights at
+//     d = 128 (v_dot2c keeps the SIMD about four times as long as an fp32
+//     add; measured 1-3 % faster at d = 128, slower at d = 64).
 //   * Causal and ragged masking (-inf) is applied only on tiles that cross
 //     the diagonal or the end of the sequence; tiles wholly above the
 //     diagonal are never loaded.
@@ -96,6 +97,9 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
   // keys per compute step: a staged tile of BN keys is consumed in BN / SB
   // steps, so a larger tile costs LDS but no registers
   constexpr int SB = BN > 64 ? 64 : BN;
+  // row sums of unrounded weights (fp32 adds) rather than of the rounded
+  // pairs (v_dot2c): see exp_row
+  constexpr bool kSumUnrounded = D == 128;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLdsElems];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -268,8 +272,12 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
         }
       };
 
-      // P = exp2(S c - m c), rounded; the row sum adds the rounded pairs, so
-      // the weights that multiply V sum exactly to l.
+      // P = exp2(S c - m c), rounded for the P.V product.  The row sum adds
+      // either the rounded pairs with v_dot2c (the d = 64 tiles: one
+      // instruction per pair, and their register budget has no room for the
+      // unrounded weights) or the unrounded fp32 weights (d = 128: cheaper to
+      // issue than v_dot2c, which occupies the SIMD about four times as long
+      // as an fp32 add, and l is then the sum of the exact weights).
       uint32_t pk[QB][SB / 32][8];
       auto exp_row = [&](int qb, const f32x16 (&sv)[SB / 32], float shift) {
         float ls[2];  // two independent sum chains, each started by its first pair
@@ -280,7 +288,8 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
             const float p0 = fast_exp2(fmaf(sv[kb][2 * j], c, shift));
             const float p1 = fast_exp2(fmaf(sv[kb][2 * j + 1], c, shift));
             pk[qb][kb][j] = HH::pack(p0, p1);
-            ls[j & 1] = HH::dot2(pk[qb][kb][j], kb == 0 && j < 2 ? 0.f : ls[j & 1]);
+            const float prev = kb == 0 && j < 2 ? 0.f : ls[j & 1];
+            ls[j & 1] = kSumUnrounded ? prev + (p0 + p1) : HH::dot2(pk[qb][kb][j], prev);
           }
         return ls[0] + ls[1];
       };
@@ -354,10 +363,14 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
     __syncthreads();
   }
 
-  // Epilogue: l over both half-waves, O / l, LSE.
+  // Epilogue: l over both half-waves, O / l, LSE.  The lane's row and column
+  // half are recomputed from the lane id (mbcnt) instead of being kept live
+  // across the key loop, which would cost registers the loop needs.
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int col_e = lane_e & 31, grp_e = lane_e >> 5;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int q = qw0 + 32 * qb + col;
+    const int q = qw0 + 32 * qb + col_e;
     const float l_tot = half_swap_sum(l_run[qb]);
     const float inv = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
     const float lse = l_tot > 0.f ? (m_run[qb] * c + fast_log2(l_tot)) * kLn2 : kNegInf;
@@ -372,9 +385,9 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
           for (int j = 0; j < 4; ++j) {
             const f32x4 w = {oacc[qb][db][4 * j] * inv, oacc[qb][db][4 * j + 1] * inv,
                              oacc[qb][db][4 * j + 2] * inv, oacc[qb][db][4 * j + 3] * inv};
-            *(f32x4*)(og + db * 32 + 8 * j + 4 * grp) = w;
+            *(f32x4*)(og + db * 32 + 8 * j + 4 * grp_e) = w;
           }
-        if (grp == 0) a.lse[row] = lse;
+        if (grp_e == 0) a.lse[row] = lse;
       }
       continue;
     }
@@ -384,12 +397,12 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int d0 = db * 32 + 8 * j + 4 * grp;
+          const int d0 = db * 32 + 8 * j + 4 * grp_e;
           const u32x2 w = {HH::pack(oacc[qb][db][4 * j] * inv, oacc[qb][db][4 * j + 1] * inv),
                            HH::pack(oacc[qb][db][4 * j + 2] * inv, oacc[qb][db][4 * j + 3] * inv)};
           *(u32x2*)(og + d0) = w;
         }
-      if (grp == 0 && a.lse) a.lse[(int64_t)prob * NQ + q] = lse;
+      if (grp_e == 0 && a.lse) a.lse[(int64_t)prob * NQ + q] = lse;
     }
   }
 }

@@ -20,7 +20,7 @@ struct Half<true> {
     return __builtin_bit_cast(uint32_t, t);
   }
   // acc + lo(p) + hi(p): sums a pair of rounded weights in one instruction
-  // (v_dot2c runs in the matrix pipe, leaving the VALU to the softmax)
+  // (v_dot2c; it occupies the SIMD about as long as four fp32 adds)
   static __device__ __forceinline__ float dot2(uint32_t p, float acc) {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
