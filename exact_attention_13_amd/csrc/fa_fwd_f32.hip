@@ -259,51 +259,69 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
                          dim3(kThreads), params, 0, s);
 }
 
-// ---------------------------------------------------------------------------
-// Short grids (fewer workgroups than kShortGrid): each workgroup owns only 32
-// query rows and its four waves split the keys instead of the rows.  A step
-// stages KS = 4 KW keys in LDS (cooperatively, single-buffered); wave w runs
-// the online softmax over keys [k0 + w KW, k0 + (w+1) KW) of every step, and
-// at the end the four partial results (m_w, l_w, O_w) are merged through LDS
-// with the rescaling of the online softmax ("FlashAttention dissected",
-// "Tiling and Online Softmax"): O = sum_w e^(m_w - m) O_w / sum_w e^(m_w - m) l_w.
-// The serial chain of a row is then a quarter as long, which is what bounds a
-// latency-bound problem such as one 512-row head.
-// ---------------------------------------------------------------------------
+// Grids of fewer than kShortGrid workgroups of 128 rows take the small-problem
+// kernel below.
 constexpr int kShortGrid = 128;
 
-template <int D>
-struct Short {
-  static constexpr int KW = D == 64 ? 64 : 32;  // keys per wave per step
-  static constexpr int KS = 4 * KW;             // keys per step
-  static constexpr int kKStride = D + 4;
-  static constexpr int kVStride = KS + 4;
-  static constexpr int kKFloats = KS * kKStride;
-  static constexpr int kVFloats = D * kVStride;
-  static constexpr int kLdsFloats = kKFloats + kVFloats;
-  static constexpr int kKChunks = KS * D / 4 / kThreads;         // float4 K chunks per thread
-  static constexpr int kVUnits = (KS / 4) * (D / 4) / kThreads;  // (4 keys, 4 columns) per thread
-  static_assert(kKChunks * kThreads * 4 == KS * D, "K tile split");
-  static_assert(kVUnits * kThreads * 16 == KS * D, "V tile split");
-  static_assert(4 * 32 * D + 2 * 4 * 32 <= kLdsFloats, "merge area");
-};
+// ---------------------------------------------------------------------------
+// Small fp32 problems (fewer than kShortGrid workgroups of 128 rows, e.g. one
+// 512-row head).  There the time is set by the serial MFMA chain of each
+// compute unit, not by the chip's throughput, so the work is cut finer:
+//   * 16 query rows per workgroup on v_mfma_f32_16x16x4_f32 (half the rows
+//     of a 32x32 tile, so twice as many compute units share a head);
+//   * the eight waves of a workgroup take every eighth 16-key tile of the
+//     keys, each with its own online-softmax state, and are merged through
+//     LDS at the end with the same rescale rule ("FlashAttention dissected",
+//     "The mathematical breakthrough": partial results over disjoint key
+//     sets combine through their maxima and sums);
+//   * no waves share K/V tiles, so each lane loads its MFMA operands from
+//     global memory (L2) directly, 16 contiguous bytes at a time, one tile
+//     ahead of the compute.
+// Operand layouts (measured on gfx950 with an in-bounds probe): for
+// 16x16x4, lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16], and
+// holds D[4 (l / 16) + r][l % 16] in register r.
+//   * S^T = K Q^T per 16-key tile: the contraction over d is split into D/4
+//     instructions; instruction m takes, in lane group g = l / 16, column
+//     g D/4 + m, so each lane reads D/4 consecutive floats of its key row
+//     (A) and of its query row (B).  Lane (j, g) ends up with keys 4g + r of
+//     query j (r = 0..3).
+//   * O^T += V^T P^T: instruction r of a tile contracts keys {4g + r}, which
+//     lane (j, g) holds as its score register r, so P^T needs no data
+//     movement; output tile t holds columns d = TD i + t (TD = D / 16) in
+//     row i, so each lane reads TD consecutive floats of a value row (A) and
+//     ends up with D/4 consecutive output columns g D/4 .. of query j.
+// ---------------------------------------------------------------------------
+constexpr int kTinyThreads = 512;  // eight waves
+constexpr int kTinyRows = 16;
+
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// max / sum over the four lane groups (lanes j, j + 16, j + 32, j + 48)
+__device__ __forceinline__ float quad_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  return half_swap_max(x);
+}
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fwd_f32_short_kernel(FwdArgs a, int n_qt, int total) {
-  using T = Short<D>;
-  constexpr int KW = T::KW, KS = T::KS;
-  __shared__ __attribute__((aligned(16))) float lds[T::kLdsFloats];
+__global__ __launch_bounds__(kTinyThreads) void fwd_f32_tiny_kernel(FwdArgs a, int n_qt, int total) {
+  constexpr int DQ = D / 4;    // floats per lane of a K or Q row, and output columns per lane
+  constexpr int TD = D / 16;   // output tiles of 16 columns
+  constexpr int NWV = kTinyThreads / 64;
+  __shared__ __attribute__((aligned(16))) float lds[NWV * kTinyRows * D + 2 * NWV * kTinyRows];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31, grp = lane >> 5;
+  const int j = lane & 15, g = lane >> 4;
   const int NQ = a.nq, NK = a.nk;
 
   const int L = xcd_remap(blockIdx.x, total);
   int prob, qt;
   tile_of<CAUSAL>(L, total, n_qt, prob, qt);
-  const int q0 = qt * 32;
-  const int my_q = q0 + col;
+  const int q0 = qt * kTinyRows;
   const int off = a.causal_off;
 
   const int64_t qhead = (int64_t)prob * NQ * D;
@@ -312,162 +330,143 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_short_kernel(FwdArgs a, int 
   const __amdgpu_buffer_rsrc_t kr = make_rsrc((const float*)a.k + kvhead, NK * D * 4);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc((const float*)a.v + kvhead, NK * D * 4);
 
-  f32x4 qf[D / 8];
+  // query row q0 + j, columns g DQ .. g DQ + DQ - 1 (rows past the end read 0)
+  float qv[DQ];
 #pragma unroll
-  for (int j = 0; j < D / 8; ++j)
-    qf[j] = __builtin_bit_cast(f32x4, buf_load16(qr, (my_q * D + j * 8 + grp * 4) * 4));
+  for (int i = 0; i < DQ / 4; ++i) {
+    const f32x4 x = __builtin_bit_cast(f32x4, buf_load16(qr, ((q0 + j) * D + g * DQ + 4 * i) * 4));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qv[4 * i + e] = x[e];
+  }
 
-  // keys the workgroup's last row may see, and the keys of this wave's rows
   int kstop = NK;
-  if (CAUSAL) kstop = max(0, min(kstop, q0 + 32 + off));
-  const int n_kv = (kstop + KS - 1) / KS;
+  if (CAUSAL) kstop = max(0, min(kstop, q0 + kTinyRows + off));
+  const int n_tiles = (kstop + 15) / 16;
+
+  // this wave's tiles: wave, wave + NWV, ...; operands of tile t:
+  // K row t*16 + j, columns g DQ ..; V rows t*16 + 4g + r, columns TD j ..
+  // They rotate through two register buffers: the wave's next tile loads
+  // while the current one is computed (a deeper ring measured no faster).
+  constexpr int NB = 2;
+  float kf[NB][DQ], vf[NB][4][TD];
+  auto load = [&](int buf, int t) {
+    const int k0 = t * 16;
+#pragma unroll
+    for (int i = 0; i < DQ / 4; ++i) {
+      const f32x4 x =
+          __builtin_bit_cast(f32x4, buf_load16(kr, ((k0 + j) * D + g * DQ + 4 * i) * 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kf[buf][4 * i + e] = x[e];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < TD / 4; ++i) {
+        const f32x4 x = __builtin_bit_cast(
+            f32x4, buf_load16(vr, ((k0 + 4 * g + r) * D + TD * j + 4 * i) * 4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vf[buf][r][4 * i + e] = x[e];
+      }
+  };
 
   const float c = a.scale_log2;
   float m_run = kNegInf, l_run = 0.f;
-  f32x16 oacc[D / 32];
+  f32x4 oacc[TD];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = (f32x16){};
+  for (int t = 0; t < TD; ++t) oacc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  float* ks = lds;
-  float* vs = lds + T::kKFloats;
-  for (int t = 0; t < n_kv; ++t) {
-    const int k0 = t * KS;
-    {
-      f32x4 kst[T::kKChunks];
-      f32x4 vst[T::kVUnits][4];
+  const int my_q = q0 + j;
+  // one tile of this wave from buffer buf (a constant at each call site, so
+  // the buffers stay in registers); the buffer is then refilled with the
+  // tile NB steps ahead
+  auto step = [&](int buf, int t) {
+    const int k0 = t * 16;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < T::kKChunks; ++i) {
-        const int u = tid + i * kThreads;
-        const int row = u / (D / 4), cc = u % (D / 4);
-        kst[i] = __builtin_bit_cast(f32x4, buf_load16(kr, ((k0 + row) * D + cc * 4) * 4));
+    for (int m = 0; m < DQ; ++m) s = mfma16(kf[buf][m], qv[m], s);
+    // lane (j, g) register r: key k0 + 4g + r of query my_q
+    if (k0 + 16 > NK || (CAUSAL && k0 + 15 > q0 + off)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + 4 * g + r;
+        const bool masked = key >= NK || (CAUSAL && key > my_q + off);
+        s[r] = masked ? kNegInf : s[r];
       }
-#pragma unroll
-      for (int i = 0; i < T::kVUnits; ++i) {
-        const int u = tid + i * kThreads;
-        const int kq = u % (KS / 4), cc = u / (KS / 4);
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          vst[i][h] =
-              __builtin_bit_cast(f32x4, buf_load16(vr, ((k0 + 4 * kq + h) * D + cc * 4) * 4));
-      }
-      if (t > 0) __syncthreads();  // the previous step's LDS reads are done
-#pragma unroll
-      for (int i = 0; i < T::kKChunks; ++i) {
-        const int u = tid + i * kThreads;
-        const int row = u / (D / 4), cc = u % (D / 4);
-        *(f32x4*)(ks + row * T::kKStride + cc * 4) = kst[i];
-      }
-#pragma unroll
-      for (int i = 0; i < T::kVUnits; ++i) {
-        const int u = tid + i * kThreads;
-        const int kq = u % (KS / 4), cc = u / (KS / 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const f32x4 w = {vst[i][0][e], vst[i][1][e], vst[i][2][e], vst[i][3][e]};
-          *(f32x4*)(vs + (cc * 4 + e) * T::kVStride + kq * 4) = w;
-        }
-      }
-      __syncthreads();
     }
-
-    const int kw = k0 + wave * KW;  // this wave's first key of the step
-    if (kw < kstop && (!CAUSAL || kw <= q0 + 31 + off)) {
-      f32x16 s[KW / 32];
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = quad_max(mx);
+    // lazy rescale: the reference maximum moves only when a score exceeds it
+    // by more than kRescaleLog2 in exp2 units
+    const bool grow = (mx - m_run) * c > kRescaleLog2;
+    if (__any(grow)) {
+      const float alpha = grow ? fast_exp2((m_run - mx) * c) : 1.f;
+      l_run *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < KW / 32; ++kb) s[kb] = (f32x16){};
-#pragma unroll
-      for (int j = 0; j < D / 8; ++j)
-#pragma unroll
-        for (int kb = 0; kb < KW / 32; ++kb) {
-          const f32x4 ka =
-              *(const f32x4*)(ks + (wave * KW + kb * 32 + col) * T::kKStride + j * 8 + grp * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[kb] = mfma_f32(ka[e], qf[j][e], s[kb]);
-        }
-
-      if (kw + KW > NK || (CAUSAL && kw + KW - 1 > q0 + off)) {
-#pragma unroll
-        for (int kb = 0; kb < KW / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kw + kb * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
-            const bool masked = key >= NK || (CAUSAL && key > my_q + off);
-            s[kb][r] = masked ? kNegInf : s[kb][r];
-          }
-      }
-
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < KW / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = half_swap_max(mx);
-      const bool grow = (mx - m_run) * c > kRescaleLog2;
-      if (__any(grow)) {
-        const float alpha = grow ? fast_exp2((m_run - mx) * c) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-        m_run = grow ? mx : m_run;
-      }
-      const float nmc = m_run == kNegInf ? 0.f : -m_run * c;
-#pragma unroll
-      for (int kb = 0; kb < KW / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[kb][r], c, nmc));
-          s[kb][r] = p;
-          l_run += p;
-        }
-#pragma unroll
-      for (int kb = 0; kb < KW / 32; ++kb)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const f32x4 va = *(const f32x4*)(vs + (db * 32 + col) * T::kVStride + wave * KW +
-                                             kb * 32 + g4 * 8 + grp * 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) oacc[db] = mfma_f32(va[e], s[kb][g4 * 4 + e], oacc[db]);
-          }
+      for (int u = 0; u < TD; ++u) oacc[u] *= alpha;
+      m_run = grow ? mx : m_run;
     }
+    const float nmc = m_run == kNegInf ? 0.f : -m_run * c;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = fast_exp2(fmaf(s[r], c, nmc));
+      l_run += p[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int u = 0; u < TD; ++u) oacc[u] = mfma16(vf[buf][r][u], p[r], oacc[u]);
+    if (t + NB * NWV < n_tiles) load(buf, t + NB * NWV);
+  };
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    if (wave + b * NWV < n_tiles) load(b, wave + b * NWV);
+  for (int t = wave; t < n_tiles; t += NB * NWV) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (t + b * NWV < n_tiles) step(b, t + b * NWV);
   }
 
-  // Merge the four waves' partial results: O_w (unnormalised), l_w, m_w.
-  const float l_w = half_swap_sum(l_run);
-  __syncthreads();  // every wave is done with the K/V tiles
-  float* om = lds;                   // [wave][row][D]
-  float* st = lds + 4 * 32 * D;      // [wave][row]: m, then l
+  // Merge the waves: O_w (unnormalised, this lane's columns g DQ .. of row
+  // j), l_w (the lane sum over the four lane groups) and m_w.
+  float l_w = l_run;
+  {
+    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(l_w), __float_as_uint(l_w),
+                                                    false, false);
+    l_w = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  }
+  l_w = half_swap_sum(l_w);
+  float* om = lds;                                // [wave][row][D]
+  float* st = lds + NWV * kTinyRows * D;          // [wave][row]: m, then l
+  // output column of oacc[u][r]: g DQ + TD r + u
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int jr = 0; jr < 4; ++jr)
-      *(f32x4*)(om + (wave * 32 + col) * D + db * 32 + 8 * jr + 4 * grp) =
-          (f32x4){oacc[db][4 * jr], oacc[db][4 * jr + 1], oacc[db][4 * jr + 2],
-                  oacc[db][4 * jr + 3]};
-  if (grp == 0) {
-    st[wave * 32 + col] = m_run;
-    st[4 * 32 + wave * 32 + col] = l_w;
+    for (int u0 = 0; u0 < TD; u0 += 4) {
+      const f32x4 w = {oacc[u0][r], oacc[u0 + 1][r], oacc[u0 + 2][r], oacc[u0 + 3][r]};
+      *(f32x4*)(om + (wave * kTinyRows + j) * D + g * DQ + TD * r + u0) = w;
+    }
+  if (g == 0) {
+    st[wave * kTinyRows + j] = m_run;
+    st[NWV * kTinyRows + wave * kTinyRows + j] = l_w;
   }
   __syncthreads();
 
-  // thread -> (row, 4-column group): D/4 groups per row, 32 rows
+  // thread -> (row, 4-column group)
   constexpr int kGroups = D / 4;
-#pragma unroll
-  for (int it = 0; it < 32 * kGroups / kThreads; ++it) {
-    const int u = tid + it * kThreads;
+  for (int u = tid; u < kTinyRows * kGroups; u += kTinyThreads) {
     const int row = u / kGroups, cg = u % kGroups;
     float m = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) m = fmaxf(m, st[w * 32 + row]);
+    for (int w = 0; w < NWV; ++w) m = fmaxf(m, st[w * kTinyRows + row]);
     float ltot = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = st[w * 32 + row];
+    for (int w = 0; w < NWV; ++w) {
+      const float mw = st[w * kTinyRows + row];
       const float wt = mw == kNegInf ? 0.f : fast_exp2((mw - m) * c);
-      ltot += wt * st[4 * 32 + w * 32 + row];
-      o += wt * *(const f32x4*)(om + (w * 32 + row) * D + cg * 4);
+      ltot += wt * st[NWV * kTinyRows + w * kTinyRows + row];
+      o += wt * *(const f32x4*)(om + (w * kTinyRows + row) * D + cg * 4);
     }
     const int q = q0 + row;
     if (q < NQ) {
@@ -480,19 +479,19 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_short_kernel(FwdArgs a, int 
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_short(const FwdArgs& a, hipStream_t s) {
-  int n_qt = (a.nq + 31) / 32;
+hipError_t launch_tiny(const FwdArgs& a, hipStream_t s) {
+  int n_qt = (a.nq + kTinyRows - 1) / kTinyRows;
   int total = (int)((int64_t)n_qt * a.problems);
   FwdArgs args = a;
   void* params[] = {&args, &n_qt, &total};
-  return hipLaunchKernel((const void*)&fwd_f32_short_kernel<D, CAUSAL>, dim3(total),
-                         dim3(kThreads), params, 0, s);
+  return hipLaunchKernel((const void*)&fwd_f32_tiny_kernel<D, CAUSAL>, dim3(total),
+                         dim3(kTinyThreads), params, 0, s);
 }
 
 template <int D>
 hipError_t launch_d(bool causal, bool split, const FwdArgs& a, hipStream_t s) {
   if (!split && (int64_t)((a.nq + kBM - 1) / kBM) * a.problems < kShortGrid)
-    return causal ? launch_short<D, true>(a, s) : launch_short<D, false>(a, s);
+    return causal ? launch_tiny<D, true>(a, s) : launch_tiny<D, false>(a, s);
   if (causal) return split ? launch<D, true, true>(a, s) : launch<D, true, false>(a, s);
   return split ? launch<D, false, true>(a, s) : launch<D, false, false>(a, s);
 }

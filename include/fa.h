@@ -77,8 +77,8 @@ typedef enum {
  *          zero is a valid empty problem and returns FA_OK with no launch.
  *          Limits (else FA_ERR_SHAPE): B*H <= 2^31-1, one head's N x d
  *          array (plus 1024 rows) below 2^31 bytes, and the launch grid
- *          (B*H*ceil(N/R) workgroups, where a workgroup takes R = 32 to 512
- *          query rows by dtype, d and mask) below 2^31.
+ *          (B*H*ceil(N/R) workgroups, where a workgroup takes R = 16 to 512
+ *          query rows by dtype, d, mask and problem size) below 2^31.
  * d        head dimension: 64 or 128.
  * scale    multiplier of the dot products (usually 1/sqrt(d)); finite, > 0.
  * causal   nonzero: key j is masked for query i when j > i.

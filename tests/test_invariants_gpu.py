@@ -49,8 +49,9 @@ LN2 = math.log(2.0)
 
 # (B, H, N): several key tiles and a ragged tail for every instance (d = 64
 # bf16/fp16 tiles are 512 query rows x 128 keys, d = 128 ones 128 x 32, fp32
-# ones 128 x 64); the fp32 short-grid kernel takes grids of fewer than 128
-# workgroups of 128 rows, so (1, 2, 1000) runs it and (2, 8, 1000) does not.
+# ones 128 x 64); the fp32 small-problem kernel (16 rows per workgroup) takes
+# grids of fewer than 128 workgroups of 128 rows, so (1, 2, 1000) runs it and
+# (2, 8, 1000) does not.
 SHAPES = [(1, 2, 1000), (2, 8, 1000)]
 
 

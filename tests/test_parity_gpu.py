@@ -86,9 +86,11 @@ def test_small_shapes(dtype, d, causal):
 @pytest.mark.parametrize("causal", [False, True])
 def test_f32_grid_sizes(d, causal):
     # fp32 problems of fewer than 128 workgroups of 128 rows take the
-    # short-grid kernel (four waves splitting the keys of 32 rows); larger
-    # ones the 128-row kernel.  Both sides of the switch, ragged tails.
-    for B, H, N, seed in ((1, 1, 700, 1600), (2, 16, 1000, 1601), (1, 31, 513, 1602)):
+    # small-problem kernel (16 rows per workgroup, eight waves splitting the
+    # keys in 16-key tiles); larger ones the 128-row kernel.  Both sides of
+    # the switch, ragged tails, key counts that leave waves without tiles.
+    for B, H, N, seed in ((1, 1, 700, 1600), (2, 16, 1000, 1601), (1, 31, 513, 1602),
+                          (1, 3, 100, 1603), (1, 2, 17, 1604)):
         w, (q, k, v) = small_case("f32", B, H, N, d, causal, seed=seed)
         _note(f"f32 grid d={d} causal={causal} B={B} H={H} N={N}")
         o, lse = run_gpu(q, k, v, w.scale, causal)
