@@ -9,14 +9,20 @@
 //     B operand of S^T = K Q^T (course lesson "FlashAttention Inner Loop
 //     Implementation", section "Implementing the Inner Loop": Q is loaded
 //     once and reused for every key/value step).
-//   * K/V tiles of 64 keys are staged HBM -> registers -> LDS, double
-//     buffered: tile t+1 is fetched by every thread (all four waves, 16-byte
-//     loads) while tile t is computed, then written to the other LDS buffer
-//     (GitHub README "CUDA Flash Attention...", "Performance Analysis": the
-//     K/V load must use all warps; "Design decisions": padded shared rows).
-//     K rows are padded by 16 bytes; V is stored transposed ([d][key]) with
-//     the key order permuted inside each 16-key chunk, so each lane's
-//     operand for the P.V product is one 16-byte LDS read.
+//   * K/V tiles are loaded by every thread of the workgroup (16-byte loads;
+//     GitHub README "CUDA Flash Attention...", "Performance Analysis": the
+//     K/V load must use all warps) while the previous tile is computed.
+//     d = 64: staged HBM -> registers -> LDS, double buffered; K rows
+//     padded by 16 bytes ("Design decisions": padded shared rows), V stored
+//     transposed ([d][key]) with the key order permuted inside each 16-key
+//     chunk, so each lane's operand for the P.V product is one 16-byte LDS
+//     read.  d = 128: loaded HBM -> LDS directly (buffer loads with the LDS
+//     bit: no staging registers, no LDS stores, no transposing permutes),
+//     three stages deep with tile t+2 in flight while tile t is computed;
+//     K and V both row-major, unpadded, 16-byte chunks XOR-swizzled per
+//     row so that the K reads and the transposed V reads (ds_read_b64_tr_b16)
+//     are free of bank conflicts.  The loads of a single-buffered tile sat
+//     exposed on the critical path: +5-7 % on the d = 128 causal shapes.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16}: each lane ends up with
 //     32 scores of ONE query (16 per 32-key block), the other 32 scores of
 //     that query sit in the lane 32 positions away.  Row statistics are thus
@@ -81,14 +87,71 @@ struct Cfg {
   // A one-wave workgroup has nobody to overlap with inside the workgroup:
   // it keeps one LDS stage (the next tile waits in registers) so that twice
   // as many workgroups fit in a CU's LDS.
-  static constexpr int kStages = NW == 1 ? 1 : 2;
-  static constexpr int kLdsElems = kStages * (kKStage + kVStage);
+  static constexpr int kStagesReg = NW == 1 ? 1 : 2;
+  // d = 128 multi-wave tiles go HBM -> LDS directly (16-byte buffer loads
+  // with the LDS bit), three stages deep, unpadded rows with swizzled chunks
+  static constexpr bool kDma = D == 128 && NW % 4 == 0;
+  static constexpr int kTileElems = BN * D;            // one K or V tile, unpadded
+  static constexpr int kStages = kDma ? 3 : kStagesReg;
+  static constexpr int kLdsElems = kDma ? kStages * 2 * kTileElems : kStages * (kKStage + kVStage);
+  static constexpr int kDmaPer = kTileElems * 2 / (kThreads * 16);  // loads per thread per tile
+  static_assert(!kDma || kDmaPer * kThreads * 16 == kTileElems * 2, "DMA tile split");
   static constexpr int kKUnits = BN * D / 8;        // 16-byte K chunks per tile
   static constexpr int kVUnits = (BN / 2) * (D / 8);  // (key pair, 8 columns) per tile
   static constexpr int kKPer = (kKUnits + kThreads - 1) / kThreads;
   static constexpr int kVPer = (kVUnits + kThreads - 1) / kThreads;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
 };
+
+// Slot of a 16-byte chunk inside a 256-byte LDS row of a d = 128 tile:
+// chunk c of tile row r sits at slot c ^ chunk_swz(r % 16).  The map is a
+// bijection of the 16 rows of a 16-row group, so the K reads (16 rows, one
+// chunk each) and the transposed V reads (4 rows x 64 bytes per half-wave)
+// each touch every bank once.
+__device__ __forceinline__ int chunk_swz(int r) {
+  return (((r >> 1) & 1) << 3) | ((r & 1) << 2) | ((((r >> 1) ^ (r >> 3)) & 1) << 1) |
+         ((r >> 2) & 1);
+}
+
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// 16-byte buffer load whose data goes straight to LDS: lane l of the wave
+// writes bytes [16 l, 16 l + 16) from `dst` (wave-uniform).  Offsets past
+// the resource's range read as zeros.  (A device function, not a lambda:
+// lambdas inside kernels are host + device, and the host pass rejects the
+// builtin there.)
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, uint16_t* dst,
+                                               int byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           byte_off, 0, 0, 0);
+}
+
+// LDS transpose read (ds_read_b64_tr_b16) at byte address addr + OFF, as
+// inline assembly, and a wait for every LDS read in flight that passes four
+// such results through, so that no use of them can be scheduled before it.
+// (The host pass of the compiler sees these bodies too; the asm exists only
+// in the device pass.)
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr16_b64(uint32_t addr) {
+  u32x2 r;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+#else
+  r = (u32x2){addr, 0u};
+#endif
+  return r;
+}
+__device__ __forceinline__ void lds_wait_all(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+#endif
+}
+
+// s_waitcnt operand that waits until at most N vector-memory operations are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14, the other
+// counters at their no-wait maxima)
+template <int N>
+constexpr int kVmcntWait = (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
 
 template <bool BF16, bool CAUSAL, bool SPLIT, class C>
 __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_qt, int total) {
@@ -100,7 +163,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
   // row sums of unrounded weights (fp32 adds) rather than of the rounded
   // pairs (v_dot2c): see exp_row
   constexpr bool kSumUnrounded = D == 128;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::kLdsElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::kLdsElems];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform across a wave: keep it (and every branch on
@@ -126,15 +189,6 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
   const int qw0 = q0 + wave * C::kQPerWave;  // first query of this wave
   const int off = a.causal_off;
 
-  // Q fragments: block qb, lane (col, grp) holds Q[qw0 + 32qb + col][16kc + 8grp .. +8);
-  // rows past the end read as zero.
-  u32x4 qf[QB][D / 16];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc)
-      qf[qb][kc] = buf_load16(qr, ((qw0 + 32 * qb + col) * D + kc * 16 + grp * 8) * 2);
-
   // Keys of this workgroup: its split's range, cut at the last key that the
   // tile's last row may see.  A wave stops at its own last visible key, and
   // a wave whose rows all lie past the end does no arithmetic at all.
@@ -145,6 +199,37 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
   const int n_kv = kstop > kbeg ? (kstop - kbeg + BN - 1) / BN : 0;
   int wave_kv_end = CAUSAL ? min(qw0 + C::kQPerWave + off, NK) : NK;
   if (qw0 >= NQ) wave_kv_end = kbeg;
+
+  // Direct HBM -> LDS staging (kDma): wave w's load i fills tile rows
+  // 4 (i NW + w) .. +3, lane l writing the 16 bytes at l * 16 of that block,
+  // i.e. slot l % 16 of row 4 (i NW + w) + l / 16; it fetches the chunk
+  // that the swizzle puts there.  The row within its 16-row group is the
+  // same for every i (NW is a multiple of 4), so the offset is one value.
+  const int dma_row = 4 * wave + (lane >> 4);
+  const int dma_off = dma_row * D * 2 + 16 * ((lane & 15) ^ chunk_swz(dma_row));
+  auto dma_tile = [&](int k0, int stage) {
+    uint16_t* kt = lds + stage * 2 * C::kTileElems;
+    uint16_t* vt = kt + C::kTileElems;
+    const int g = k0 * D * 2 + dma_off;
+#pragma unroll
+    for (int i = 0; i < C::kDmaPer; ++i) {
+      const int rows = 4 * (i * C::NW + wave);
+      buf_load16_lds(kr, kt + rows * D, g + i * C::NW * 4 * D * 2);
+      buf_load16_lds(vr, vt + rows * D, g + i * C::NW * 4 * D * 2);
+    }
+  };
+  if constexpr (C::kDma) {
+    if (n_kv > 0) dma_tile(kbeg, 0);
+  }
+
+  // Q fragments: block qb, lane (col, grp) holds Q[qw0 + 32qb + col][16kc + 8grp .. +8);
+  // rows past the end read as zero.
+  u32x4 qf[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc)
+      qf[qb][kc] = buf_load16(qr, ((qw0 + 32 * qb + col) * D + kc * 16 + grp * 8) * 2);
 
   u32x4 kst[C::kKPer];
   u32x4 vst[C::kVPer][2];
@@ -207,6 +292,18 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
     }
   };
 
+  // LDS byte offsets of this lane's operands inside a stage (DMA layout).
+  // K: row col, chunk 2 kc + grp -> slot (2 kc) ^ (grp ^ swz(col)); the
+  // 2 kc part is applied per read as an XOR of 32 kc.  V (transposed read,
+  // rows 4 grp + (lane % 16) / 4 and that + 8 of each 16-key chunk, bytes
+  // 64 db + 32 ((lane / 16) % 2) + 8 (lane % 4)): the 64 db part is applied
+  // per read as an XOR.
+  const int vrow = 4 * grp + ((lane & 15) >> 2);
+  const int vx = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const uint32_t k_off = col * D * 2 + 16 * (grp ^ chunk_swz(col));
+  const uint32_t v_off0 = vrow * D * 2 + 16 * (vx ^ chunk_swz(vrow)) + 8 * (lane & 1);
+  const uint32_t v_off1 = (vrow + 8) * D * 2 + 16 * (vx ^ chunk_swz(vrow + 8)) + 8 * (lane & 1);
+
   const float c = a.scale_log2;
   float m_run[QB];  // running reference max of raw scores q.k, per query row
   float l_run[QB];  // this lane's share of the running sum of exp2 terms
@@ -223,25 +320,60 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = (f32x16){};
   }
 
-  load_tile(kbeg);
-  store_tile(0);
-  // Everything loaded so far (Q included) has landed: the loop below then
-  // never waits on a prefetch before its own LDS store.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  if constexpr (C::kDma) {
+    // Tile 0 went out before Q (kernel start), tile 1 goes out now; all of
+    // them are waited for here, once.  The compiler's own wait counting
+    // leaves out loads into LDS, so a partial wait would leave Q "pending"
+    // to it and it would wait inside the loop, for the prefetched tiles as
+    // well; the two tiles were issued back to back, so waiting for tile 1
+    // costs little.
+    if (n_kv > 1) dma_tile(kbeg + BN, 1);
+    __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
+  } else {
+    load_tile(kbeg);
+    store_tile(0);
+    // Everything loaded so far (Q included) has landed: the loop below then
+    // never waits on a prefetch before its own LDS store.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
 
   for (int t = 0; t < n_kv; ++t) {
     const int k0 = kbeg + t * BN;
     const bool more = t + 1 < n_kv;
-    if (more) load_tile(k0 + BN);
-
-    const int buf = C::kStages == 2 ? (t & 1) : 0;
+    int buf;
+    if constexpr (C::kDma) {
+      // This thread's loads of tile t have landed once at most those of
+      // tile t + 1 are in flight; the barrier then makes every thread's
+      // share visible and tells that everyone is done with tile t - 1,
+      // whose stage the loads of tile t + 2 overwrite.  No fence: it would
+      // wait for the prefetch as well.
+      if (more)
+        __builtin_amdgcn_s_waitcnt(kVmcntWait<2 * C::kDmaPer>);
+      else
+        __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 2 < n_kv) dma_tile(k0 + 2 * BN, (t + 2) % 3);
+      buf = t % 3;
+    } else {
+      if (more) load_tile(k0 + BN);
+      buf = C::kStages == 2 ? (t & 1) : 0;
+    }
 #pragma unroll
     for (int hsub = 0; hsub < BN / SB; ++hsub)
     if (k0 + hsub * SB < wave_kv_end && k0 + hsub * SB < kend) {
       const int kh = k0 + hsub * SB;
       const uint16_t* ks = lds + buf * C::kKStage + hsub * SB * C::kKStride;
       const uint16_t* vs = lds + C::kStages * C::kKStage + buf * C::kVStage + hsub * SB;
+      // DMA layout: byte addresses of this lane's operands in the stage
+      const uint32_t stage_b =
+          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(lds + buf * 2 * C::kTileElems) +
+          hsub * SB * D * 2;
+      const uint32_t ka_b = stage_b + k_off;
+      const uint32_t va0_b = stage_b + C::kTileElems * 2 + v_off0;
+      const uint32_t va1_b = stage_b + C::kTileElems * 2 + v_off1;
       const bool ragged = kh + SB > kend;
       const bool diag = CAUSAL && (kh + SB - 1 > qw0 + off);
 
@@ -253,8 +385,11 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
           sv[kb] = (f32x16){};
 #pragma unroll
           for (int kc = 0; kc < D / 16; ++kc) {
-            const u32x4 ka =
-                *(const u32x4*)(ks + (kb * 32 + col) * C::kKStride + kc * 16 + grp * 8);
+            u32x4 ka;
+            if constexpr (C::kDma)
+              ka = *(const lds_u32x4*)(uintptr_t)((ka_b ^ (32u * kc)) + kb * 32 * D * 2);
+            else
+              ka = *(const u32x4*)(ks + (kb * 32 + col) * C::kKStride + kc * 16 + grp * 8);
             sv[kb] = HH::mfma(ka, qf[qb][kc], sv[kb]);
           }
         }
@@ -330,7 +465,60 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
           }
       };
 
-      if constexpr (QB == 2) {
+      // DMA layout: the V^T operands come from the row-major V tile through
+      // the LDS transpose read, issued as inline assembly: the compiler
+      // would otherwise make every such read wait for all loads into LDS
+      // in flight, the prefetched tiles included.  The values are then
+      // passed through the s_waitcnt that completes them, so nothing reads
+      // them before they have landed.
+      typedef u32x2 vpair[SB / 16][2];
+      auto vread = [&](int db, vpair& r) {
+        const uint32_t a0 = va0_b ^ (64u * db), a1 = va1_b ^ (64u * db);
+#pragma unroll
+        for (int pc = 0; pc < SB / 16; ++pc) {
+          r[pc][0] = pc == 0 ? lds_read_tr16_b64<0>(a0) : lds_read_tr16_b64<16 * D * 2>(a0);
+          r[pc][1] = pc == 0 ? lds_read_tr16_b64<0>(a1) : lds_read_tr16_b64<16 * D * 2>(a1);
+        }
+      };
+      auto vwait = [&](vpair& r) {
+        if constexpr (C::kDma) {
+          static_assert(SB / 16 == 2, "four transposed reads per d block");
+          lds_wait_all(r[0][0], r[0][1], r[1][0], r[1][1]);
+        }
+      };
+      auto vmma = [&](int qb, int db, const vpair& r) {
+#pragma unroll
+        for (int pc = 0; pc < SB / 16; ++pc) {
+          const u32x4 va = {r[pc][0][0], r[pc][0][1], r[pc][1][0], r[pc][1][1]};
+          const int kb = pc >> 1, h = (pc & 1) * 4;
+          const u32x4 pb = {pk[qb][kb][h], pk[qb][kb][h + 1], pk[qb][kb][h + 2], pk[qb][kb][h + 3]};
+          oacc[qb][db] = HH::mfma(va, pb, oacc[qb][db]);
+        }
+      };
+
+      if constexpr (C::kDma) {
+        static_assert(QB == 1 && D == 128, "DMA tiles: one 32-row block per wave, d = 128");
+        // d block 0's operands are read while the softmax runs; each later
+        // block's read is in flight during the previous block's MFMAs.
+        f32x16 s0[SB / 32];
+        qk(0, s0);
+        mask(0, s0);
+        vpair r0, r1;
+        vread(0, r0);
+        const float lt0 = fast(0, s0);
+        settle(0, s0, lt0);
+        vwait(r0);
+        vread(1, r1);
+        vmma(0, 0, r0);
+        vwait(r1);
+        vread(2, r0);
+        vmma(0, 1, r1);
+        vwait(r0);
+        vread(3, r1);
+        vmma(0, 2, r0);
+        vwait(r1);
+        vmma(0, 3, r1);
+      } else if constexpr (QB == 2) {
         // The two 32-row blocks are independent: issued in this order, the
         // QK MFMAs of block 1 run under the softmax of block 0 and the PV
         // MFMAs of block 0 under the softmax of block 1, so each wave keeps
@@ -358,9 +546,11 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
       }
     }
 
-    if (C::kStages == 1) __syncthreads();  // tile t's LDS reads are done
-    if (more) store_tile(C::kStages == 2 ? ((t + 1) & 1) : 0);
-    __syncthreads();
+    if constexpr (!C::kDma) {
+      if (C::kStages == 1) __syncthreads();  // tile t's LDS reads are done
+      if (more) store_tile(C::kStages == 2 ? ((t + 1) & 1) : 0);
+      __syncthreads();
+    }
   }
 
   // Epilogue: l over both half-waves, O / l, LSE.  The lane's row and column
