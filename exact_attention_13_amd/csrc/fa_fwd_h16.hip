@@ -380,16 +380,34 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
       // S^T = K Q^T for row block qb: lane holds keys
       // k0 + 32*kb + 8*(r/4) + 4*grp + r%4 of query qw0 + 32*qb + col.
       auto qk = [&](int qb, f32x16 (&sv)[SB / 32]) {
+        if constexpr (C::kDma) {
+          // K fragments read two ahead of the MFMA that takes them; the
+          // scheduling barriers keep the compiler from pulling each read
+          // down to its MFMA (+2 % on the d = 128 causal shapes)
+          static_assert(SB == 32, "one 32-key block per compute step");
+          constexpr int KP = 2;
+          u32x4 kf[KP];
+#pragma unroll
+          for (int j = 0; j < KP; ++j) kf[j] = *(const lds_u32x4*)(uintptr_t)(ka_b ^ (32u * j));
+          __builtin_amdgcn_sched_barrier(0);
+          sv[0] = (f32x16){};
+#pragma unroll
+          for (int kc = 0; kc < D / 16; ++kc) {
+            const u32x4 ka = kf[kc % KP];
+            if (kc + KP < D / 16)
+              kf[kc % KP] = *(const lds_u32x4*)(uintptr_t)(ka_b ^ (32u * (kc + KP)));
+            sv[0] = HH::mfma(ka, qf[qb][kc], sv[0]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          return;
+        }
 #pragma unroll
         for (int kb = 0; kb < SB / 32; ++kb) {
           sv[kb] = (f32x16){};
 #pragma unroll
           for (int kc = 0; kc < D / 16; ++kc) {
-            u32x4 ka;
-            if constexpr (C::kDma)
-              ka = *(const lds_u32x4*)(uintptr_t)((ka_b ^ (32u * kc)) + kb * 32 * D * 2);
-            else
-              ka = *(const u32x4*)(ks + (kb * 32 + col) * C::kKStride + kc * 16 + grp * 8);
+            const u32x4 ka =
+                *(const u32x4*)(ks + (kb * 32 + col) * C::kKStride + kc * 16 + grp * 8);
             sv[kb] = HH::mfma(ka, qf[qb][kc], sv[kb]);
           }
         }
