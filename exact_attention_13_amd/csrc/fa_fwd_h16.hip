@@ -414,14 +414,21 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
       };
       auto mask = [&](int qb, f32x16 (&sv)[SB / 32]) {
         if (ragged || diag) {
+          // register r holds key base + 8 (r / 4) + r % 4; the key is
+          // masked past the end (>= kend) or, causal, past the row's
+          // diagonal: both are "offset > lim" for one per-lane limit, so
+          // each score costs one compare against a constant (the key
+          // indices themselves, once hoisted by the compiler, cost an add
+          // per score on every tile)
 #pragma unroll
-          for (int kb = 0; kb < SB / 32; ++kb)
+          for (int kb = 0; kb < SB / 32; ++kb) {
+            const int base = kh + kb * 32 + 4 * grp;
+            int lim = kend - 1 - base;
+            if (CAUSAL) lim = min(lim, qw0 + 32 * qb + col + off - base);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kh + kb * 32 + 8 * (r >> 2) + 4 * grp + (r & 3);
-              const bool masked = key >= kend || (CAUSAL && key > qw0 + 32 * qb + col + off);
-              sv[kb][r] = masked ? kNegInf : sv[kb][r];
-            }
+            for (int r = 0; r < 16; ++r)
+              sv[kb][r] = 8 * (r >> 2) + (r & 3) > lim ? kNegInf : sv[kb][r];
+          }
         }
       };
 
