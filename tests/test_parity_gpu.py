@@ -214,6 +214,31 @@ def test_canaries_untouched_and_not_read(dtype):
     assert_close(o.cpu(), lse.cpu(), o_ref, lse_ref, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_tail_reads_zeros_over_stale_lds(dtype, d, causal):
+    # Keys past the end must reach the P.V product as zero rows (their
+    # weights are 0, and 0 * NaN would be NaN).  A first launch of the same
+    # kernel on all-NaN K/V (every CU busy) leaves NaN in the LDS stages;
+    # the second problem's last key tile is ragged and lands in a stage
+    # that its workgroup has not written before (65 keys: 32-key tiles 0, 1
+    # full, tile 2 one key; 100 keys: 64-key steps), so its rows past the
+    # end must be written as zeros by the loads themselves, not left over.
+    tdt = TORCH[dtype]
+    Bp, Hp, Np = 4, 64, 1024
+    nan = torch.full((Bp, Hp, Np, d), float("nan"), dtype=tdt, device=DEV)
+    qp = torch.randn(Bp, Hp, Np, d, device=DEV).to(tdt)
+    op = torch.empty_like(qp)
+    for n in (65, 100):
+        _note(f"stale-LDS ragged {dtype} d={d} causal={causal} N={n}")
+        binding.fwd(qp, nan, nan, 0.1, causal, out=op)
+        w, (q, k, v) = small_case(dtype, 8, 64, n, d, causal, seed=2100 + n)
+        o, lse = run_gpu(q, k, v, w.scale, causal)
+        o_ref, lse_ref = oracle.fwd(q, k, v, w.scale, causal)
+        assert_close(o, lse, o_ref, lse_ref, dtype, f"N={n}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_deterministic_bitwise(dtype):
     w, (q, k, v) = small_case(dtype, 1, 4, 1000, 64, False, seed=11)
