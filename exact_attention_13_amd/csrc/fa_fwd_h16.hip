@@ -425,6 +425,9 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
             const int base = kh + kb * 32 + 4 * grp;
             int lim = kend - 1 - base;
             if (CAUSAL) lim = min(lim, qw0 + 32 * qb + col + off - base);
+            // keep the compares below inside this branch: hoisted into the
+            // QK MFMAs' shadow they ran on every tile
+            asm volatile("" : "+v"(lim));
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               sv[kb][r] = 8 * (r >> 2) + (r & 3) > lim ? kNegInf : sv[kb][r];
