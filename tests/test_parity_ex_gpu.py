@@ -216,12 +216,30 @@ def test_workload_D1_full_oracle():
 
 
 @pytest.mark.parametrize("name", ["G1", "G2"])
-def test_workload_grouped_sampled_rows(name):
+def test_workload_grouped_every_row(name):
+    # Full size, every row against the oracle (G1: 16 query heads on 4 K/V
+    # heads at 16384 rows; G2: 8 x 16 causal heads on 2 K/V heads at 4096),
+    # with O and LSE pre-filled with NaN so that a tile the grid skipped
+    # fails.  The oracle runs a few query heads at a time (rows are flat
+    # indices (b H + h) N + i), printing its progress.
     w = WORKLOADS[name]
     q, k, v = make_inputs(w)
-    _note(f"workload {name} sampled")
-    o, lse = run_ex(q, k, v, w.scale, w.causal, num_splits=1)
-    rows = sample_rows(w, 768)
-    o_ref, lse_ref = oracle.fwd_gqa(q, k, v, w.scale, w.causal, rows=rows)
-    idx = torch.from_numpy(rows)
-    assert_close(o.reshape(-1, w.d)[idx], lse.reshape(-1)[idx], o_ref, lse_ref, w.dtype, name)
+    _note(f"workload {name} every row")
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=DEV)
+    binding.fwd_ex(qd, kd, vd, w.scale, w.causal, num_splits=1, out=o, lse=lse)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    del qd, kd, vd
+    o_ref = np.empty((w.B * w.H * w.N, w.d))
+    lse_ref = np.empty((w.B * w.H * w.N,))
+    step = 4
+    for b in range(w.B):
+        for h0 in range(0, w.H, step):
+            lo = (b * w.H + h0) * w.N
+            hi = (b * w.H + min(w.H, h0 + step)) * w.N
+            rows = np.arange(lo, hi, dtype=np.int64)
+            o_ref[lo:hi], lse_ref[lo:hi] = oracle.fwd_gqa(q, k, v, w.scale, w.causal, rows=rows)
+            _note(f"  oracle {name} b={b} heads {h0}..{min(w.H, h0 + step) - 1}")
+    assert_close(o.reshape(-1, w.d), lse.reshape(-1), o_ref, lse_ref, w.dtype, name)
