@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from exact_attention_13_amd import binding
-from exact_attention_13_amd.inputs import WORKLOADS, Workload, make_inputs, sample_rows
+from exact_attention_13_amd.inputs import WORKLOADS, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
 
