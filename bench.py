@@ -58,14 +58,14 @@ COLD_FLUSH_BYTES = 512 << 20
 # Sources of the forward kernels of each input-type family (a committed
 # traffic summary counts only while these hash to the value it records).
 FWD_SOURCES = {
-    "h16": ["fa_device.hpp", "fa_h16.hpp", "fa_fwd_h16.hip", "fa_api.hip", "fa_api_util.hpp",
-            "fa_combine.hip"],
+    "h16": ["fa_device.hpp", "fa_h16.hpp", "fa_lds_dma.hpp", "fa_fwd_h16.hip", "fa_api.hip",
+            "fa_api_util.hpp", "fa_combine.hip"],
     "f32": ["fa_device.hpp", "fa_fwd_f32.hip", "fa_api.hip", "fa_api_util.hpp", "fa_combine.hip"],
 }
 
 
-BWD_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_bwd.hpp", "fa_bwd_h16.hip", "fa_bwd_f32.hip",
-               "fa_api_bwd.hip", "fa_api_util.hpp"]
+BWD_SOURCES = ["fa_device.hpp", "fa_h16.hpp", "fa_lds_dma.hpp", "fa_bwd.hpp", "fa_bwd_h16.hip",
+               "fa_bwd_f32.hip", "fa_api_bwd.hip", "fa_api_util.hpp"]
 
 
 def fwd_sources(dtype: str):

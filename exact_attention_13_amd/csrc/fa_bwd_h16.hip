@@ -24,11 +24,16 @@
 //     (Q and dO fragments in registers, one query per lane in S^T = K Q^T and
 //     dP^T = V dO^T) and streams 32-key tiles of K and V (row-major); dS^T is
 //     the B operand of dQ^T += K^T dS^T, whose K^T operand comes from the K
-//     rows through the transpose load.
+//     rows through the transpose load.  At d = 128 the tiles go HBM -> LDS
+//     directly, three stages deep, in the forward's swizzled layout
+//     (fa_lds_dma.hpp): the single-buffered register staging sat on the
+//     critical path (C3 backward 2.06 -> 1.99 ms, C5 3.76 -> 3.70, G2
+//     1.96 -> 1.92).
 // Causal masking, ragged tails and the -inf guard follow the forward kernels.
 #include <type_traits>
 
 #include "fa_bwd.hpp"
+#include "fa_lds_dma.hpp"
 #include "fa_h16.hpp"
 
 namespace fa_impl {
@@ -411,7 +416,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
   constexpr int QB = kDqBlocks<D>;
   constexpr int kRows = kDqRows<D>;
   constexpr int kStage = 2 * T::kRowElems;  // K rows, V rows
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+  // d = 128: K and V tiles loaded HBM -> LDS directly, unpadded swizzled
+  // rows, three stages (the forward's layout, fa_lds_dma.hpp); d = 64:
+  // register staging into two stages of padded rows
+  constexpr bool kDma = D == 128;
+  constexpr int kTileElems = kBT * D;
+  constexpr int kDmaPer = kTileElems * 2 / (kBwdThreads * 16);  // loads per thread per tile
+  static_assert(!kDma || (kDmaPer * kBwdThreads * 16 == kTileElems * 2 && kBwdWaves % 4 == 0),
+                "DMA tile split");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kDma ? 3 * 2 * kTileElems : 2 * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -433,6 +446,32 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
   const __amdgpu_buffer_rsrc_t gr = make_rsrc((const uint16_t*)a.dout + qhead, nq * D * 2);
   const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.lse + (int64_t)bh * nq, nq * 4);
   const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.delta + (int64_t)bh * nq, nq * 4);
+
+  // causal: row i sees keys j <= i + off
+  const int kv_end = CAUSAL ? max(0, min(q0 + kRows + off, nk)) : nk;
+  const int n_kv = (kv_end + kBT - 1) / kBT;
+  const int wave_kv_end = CAUSAL ? max(0, min(qw0 + 32 * QB + off, nk)) : nk;
+
+  // Direct HBM -> LDS loads (kDma): wave w's load i fills tile rows
+  // 4 (4 i + w) .. +3, lane l the 16 bytes at l * 16 of that block (slot
+  // l % 16 of row 4 (4 i + w) + l / 16), fetching the chunk the swizzle puts
+  // there.
+  const int dma_row = 4 * wave + (lane >> 4);
+  const int dma_off = dma_row * D * 2 + 16 * ((lane & 15) ^ chunk_swz(dma_row));
+  auto dma_tile = [&](int k0, int stage) {
+    uint16_t* kt = lds + stage * 2 * kTileElems;
+    uint16_t* vt = kt + kTileElems;
+    const int g = k0 * D * 2 + dma_off;
+#pragma unroll
+    for (int i = 0; i < kDmaPer; ++i) {
+      const int rows = 4 * (i * kBwdWaves + wave);
+      buf_load16_lds(kr, kt + rows * D, g + i * kBwdWaves * 1024);
+      buf_load16_lds(vr, vt + rows * D, g + i * kBwdWaves * 1024);
+    }
+  };
+  if constexpr (kDma) {
+    if (n_kv > 0) dma_tile(0, 0);
+  }
 
   // Q and dO rows of this lane's queries as B operands.
   u32x4 qf[QB][D / 16], gf[QB][D / 16];
@@ -457,11 +496,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
 #pragma unroll
     for (int r = 0; r < 16; ++r) ndrow[r] = -drow[0];
   }
-
-  // causal: row i sees keys j <= i + off
-  const int kv_end = CAUSAL ? max(0, min(q0 + kRows + off, nk)) : nk;
-  const int n_kv = (kv_end + kBT - 1) / kBT;
-  const int wave_kv_end = CAUSAL ? max(0, min(qw0 + 32 * QB + off, nk)) : nk;
 
   // Staging of one key tile: (row pair, 8 columns) units of K then V.
   constexpr int kUnits = 2 * T::kPairUnits;
@@ -502,19 +536,58 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dqT[qb][db] = (f32x16){};
 
-  load_tile(0);
-  store_tile(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // LDS byte offsets of this lane's operands inside a DMA stage: K and V
+  // rows (row col, chunk 2 kc + grp; the 2 kc part applied per read as an
+  // XOR of 32 kc) and the transposed K^T reads (rows 4 grp + (lane % 16) / 4
+  // and that + 8 of each 16-key chunk, bytes 64 db + 32 ((lane / 16) % 2) +
+  // 8 (lane % 4); the 64 db part applied per read as an XOR)
+  const int trow = 4 * grp + ((lane & 15) >> 2);
+  const int tx = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const uint32_t r_off = col * D * 2 + 16 * (grp ^ chunk_swz(col));
+  const uint32_t t_off0 = trow * D * 2 + 16 * (tx ^ chunk_swz(trow)) + 8 * (lane & 1);
+  const uint32_t t_off1 = (trow + 8) * D * 2 + 16 * (tx ^ chunk_swz(trow + 8)) + 8 * (lane & 1);
+
+  if constexpr (kDma) {
+    // tile 0 went out before Q; tile 1 now; everything (Q, dO, lse, D
+    // included) waited for here, once, as in the forward
+    if (n_kv > 1) dma_tile(kBT, 1);
+    __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
+  } else {
+    load_tile(0);
+    store_tile(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
 
   for (int t = 0; t < n_kv; ++t) {
-    const int k0 = t * kBT, buf = t & 1;
+    const int k0 = t * kBT;
     const bool more = t + 1 < n_kv;
-    if (more) load_tile(k0 + kBT);
+    int buf;
+    if constexpr (kDma) {
+      // this thread's loads of tile t landed once at most tile t + 1's are
+      // in flight; the barrier makes every thread's share visible and says
+      // that tile t - 1 (whose stage tile t + 2 overwrites) is done
+      if (more)
+        __builtin_amdgcn_s_waitcnt(kVmcntWait<2 * kDmaPer>);
+      else
+        __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 2 < n_kv) dma_tile(k0 + 2 * kBT, (t + 2) % 3);
+      buf = t % 3;
+    } else {
+      buf = t & 1;
+      if (more) load_tile(k0 + kBT);
+    }
 
     if (k0 < wave_kv_end) {
       const uint16_t* krm = lds + buf * kStage;
       const uint16_t* vrm = krm + T::kRowElems;
+      const uint32_t stage_b =
+          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(lds + buf * 2 * kTileElems);
+      const uint32_t kr_b = stage_b + r_off, vr_b = stage_b + kTileElems * 2 + r_off;
+      const uint32_t kt0_b = stage_b + t_off0, kt1_b = stage_b + t_off1;
 
       // S^T = K Q^T and dP^T (- D) = V dO^T (- D) for every block: lane
       // holds query qw0 + 32 qb + col, keys k0 + 8 (r/4) + 4 grp + r%4.  Each
@@ -527,13 +600,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
       }
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
-        const u32x4 ka = *(const u32x4*)(krm + col * T::kRowStride + kc * 16 + grp * 8);
+        const u32x4 ka = kDma ? *(const lds_u32x4*)(uintptr_t)(kr_b ^ (32u * kc))
+                              : *(const u32x4*)(krm + col * T::kRowStride + kc * 16 + grp * 8);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb] = HH::mfma(ka, qf[qb][kc], s[qb]);
       }
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
-        const u32x4 va = *(const u32x4*)(vrm + col * T::kRowStride + kc * 16 + grp * 8);
+        const u32x4 va = kDma ? *(const lds_u32x4*)(uintptr_t)(vr_b ^ (32u * kc))
+                              : *(const u32x4*)(vrm + col * T::kRowStride + kc * 16 + grp * 8);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) dp[qb] = HH::mfma(va, gf[qb][kc], dp[qb]);
       }
@@ -568,22 +643,61 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
 
       // dQ^T += K^T dS^T over the two 16-key chunks; each K^T operand feeds
       // every block.
+      if constexpr (kDma) {
+        // K^T operands by transpose reads (inline assembly: the compiler
+        // would make its own transpose-load intrinsic wait for every load
+        // into LDS in flight), each d block's read in flight while the
+        // previous block's MFMAs run
+        static_assert(QB == 1, "one 32-row block per wave at d = 128");
+        auto tread = [&](int db, u32x2 (&r)[2][2]) {
+          const uint32_t a0 = kt0_b ^ (64u * db), a1 = kt1_b ^ (64u * db);
+          r[0][0] = lds_read_tr16_b64<0>(a0);
+          r[0][1] = lds_read_tr16_b64<0>(a1);
+          r[1][0] = lds_read_tr16_b64<16 * D * 2>(a0);
+          r[1][1] = lds_read_tr16_b64<16 * D * 2>(a1);
+        };
+        auto tmma = [&](int db, const u32x2 (&r)[2][2]) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-          const u32x4 ka = lds_tr_operand(krm, T::kRowStride, ch * 16, db * 32, lane);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const u32x4 bd = {pd[qb][4 * ch], pd[qb][4 * ch + 1], pd[qb][4 * ch + 2],
-                              pd[qb][4 * ch + 3]};
-            dqT[qb][db] = HH::mfma(ka, bd, dqT[qb][db]);
+          for (int ch = 0; ch < 2; ++ch) {
+            const u32x4 ka = {r[ch][0][0], r[ch][0][1], r[ch][1][0], r[ch][1][1]};
+            const u32x4 bd = {pd[0][4 * ch], pd[0][4 * ch + 1], pd[0][4 * ch + 2],
+                              pd[0][4 * ch + 3]};
+            dqT[0][db] = HH::mfma(ka, bd, dqT[0][db]);
           }
-        }
+        };
+        u32x2 r0[2][2], r1[2][2];
+        tread(0, r0);
+        lds_wait_all(r0[0][0], r0[0][1], r0[1][0], r0[1][1]);
+        tread(1, r1);
+        tmma(0, r0);
+        lds_wait_all(r1[0][0], r1[0][1], r1[1][0], r1[1][1]);
+        tread(2, r0);
+        tmma(1, r1);
+        lds_wait_all(r0[0][0], r0[0][1], r0[1][0], r0[1][1]);
+        tread(3, r1);
+        tmma(2, r0);
+        lds_wait_all(r1[0][0], r1[0][1], r1[1][0], r1[1][1]);
+        tmma(3, r1);
+      } else {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int ch = 0; ch < 2; ++ch) {
+            const u32x4 ka = lds_tr_operand(krm, T::kRowStride, ch * 16, db * 32, lane);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+              const u32x4 bd = {pd[qb][4 * ch], pd[qb][4 * ch + 1], pd[qb][4 * ch + 2],
+                                pd[qb][4 * ch + 3]};
+              dqT[qb][db] = HH::mfma(ka, bd, dqT[qb][db]);
+            }
+          }
+      }
     }
 
-    if (more) store_tile(buf ^ 1);
-    __syncthreads();
+    if constexpr (!kDma) {
+      if (more) store_tile(buf ^ 1);
+      __syncthreads();
+    }
   }
 
 #pragma unroll
