@@ -19,7 +19,11 @@
 //     them as A operands (their accumulators give every lane one key), and
 //     dV^T += dO^T P, dK^T += Q^T dS read the transposed operands straight
 //     from the same rows with the LDS transpose load, in the query order in
-//     which the P and dS accumulators are, unchanged, the B operands;
+//     which the P and dS accumulators are, unchanged, the B operands.  At
+//     d = 128 the Q and dO tiles go HBM -> LDS directly, two stages deep, in
+//     the swizzled layout of fa_lds_dma.hpp, and the V rows wait in LDS in the
+//     same layout (C3 backward 1.99 -> 1.91 ms, C5 3.69 -> 3.55, G2
+//     1.94 -> 1.89);
 //   * bwd_dq_kernel: the forward kernel's shape: a workgroup owns 128 queries
 //     (Q and dO fragments in registers, one query per lane in S^T = K Q^T and
 //     dP^T = V dO^T) and streams 32-key tiles of K and V (row-major); dS^T is
@@ -51,8 +55,7 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // more than half the register file; its V rows wait in LDS instead, so that
 // two waves share a SIMD without spills (two waves instead of one are worth
 // +37-51 %: one wave's exponentials and packing hide under the other's
-// MFMAs).  At d = 64 the dK/dV kernel runs three waves per SIMD (the causal
-// instance spills two registers).
+// MFMAs).  At d = 64 the dK/dV kernel runs three waves per SIMD.
 template <int D> constexpr int kDkdvWaves = D == 64 ? 3 : 2;
 template <int D> constexpr int kDqWaves = 2;
 // 32-query blocks per wave in the dQ kernel, and queries per workgroup.  At
@@ -137,8 +140,28 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
   using HH = Half<BF16>;
   using T = BwdTile<D>;
   constexpr int kStage = 2 * T::kRowElems;  // Q rows, dO rows
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
-  __shared__ __attribute__((aligned(16))) float stat[2][2][kBT];  // [stage][lse2, D][query]
+  // d = 128: Q and dO tiles loaded HBM -> LDS directly into two stages of
+  // unpadded swizzled rows (fa_lds_dma.hpp); d = 64: register staging
+  constexpr bool kDma = D == 128;
+  constexpr int kTileElems = kBT * D;
+  constexpr int kDmaPer = kTileElems * 2 / (kBwdThreads * 16);  // loads per thread per tile
+  static_assert(!kDma || (kDmaPer * kBwdThreads * 16 == kTileElems * 2 && kBwdWaves % 4 == 0),
+                "DMA tile split");
+  // At d = 128 the V rows of the workgroup's keys wait in LDS (see below).
+  constexpr bool kVLds = D == 128;
+  // One LDS array holds the Q / dO stages, the V rows and the per-query
+  // statistics [stage][lse2, D][query].  (With several arrays the compiler
+  // tags the direct loads with an alias scope, and then makes every LDS read
+  // after one wait for it.)  The statistics are aligned to their size, so
+  // that an offset inside them can be applied as an XOR.
+  constexpr int kQgBytes = (kDma ? 2 * 2 * kTileElems : 2 * kStage) * 2;
+  constexpr int kVBytes = kVLds ? kBwdRows * D * 2 : 0;
+  constexpr int kStatBytes = 2 * 2 * kBT * 4;
+  static_assert((kQgBytes + kVBytes) % kStatBytes == 0 && kQgBytes % 1024 == 0, "LDS regions");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kQgBytes + kVBytes + kStatBytes];
+  uint16_t* const lds = (uint16_t*)smem;
+  uint16_t* const vlds = (uint16_t*)(smem + kQgBytes);
+  float(*const stat)[2][kBT] = (float(*)[2][kBT])(smem + kQgBytes + kVBytes);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -169,17 +192,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
   // d = 128 the V rows wait in LDS instead (each wave reads back only its own
   // rows, so no barrier is needed): 32 registers fewer, which keeps the
   // kernel from spilling at two waves per SIMD.
-  constexpr bool kVLds = D == 128;
-  constexpr int kVStride = D + 8;  // 16 consecutive rows at one column: conflict-free
-  __shared__ __attribute__((aligned(16))) uint16_t vlds[kVLds ? kBwdRows * kVStride : 8];
-  uint16_t* vrow = vlds + (kVLds ? (wave * 32 + col) * kVStride + grp * 8 : 0);
+  // Unpadded 256-byte rows with the chunk swizzle (lane (col, grp) reads
+  // row wave * 32 + col, chunk (2 kc + grp) ^ chunk_swz(col), i.e. one base
+  // XOR 32 kc: conflict-free like the Q and dO row reads).
+  const int vrow_off = kVLds ? ((wave * 32 + col) * D * 2 + 16 * (grp ^ chunk_swz(col))) : 0;
   u32x4 kf[D / 16], vf[kVLds ? 1 : D / 16];
 #pragma unroll
   for (int kc = 0; kc < D / 16; ++kc) {
     kf[kc] = buf_load16(kr, ((kw0 + col) * D + kc * 16 + grp * 8) * 2);
     const u32x4 x = buf_load16(vr, ((kw0 + col) * D + kc * 16 + grp * 8) * 2);
     if constexpr (kVLds)
-      *(u32x4*)(vrow + kc * 16) = x;
+      *(u32x4*)((char*)vlds + (vrow_off ^ (32 * kc))) = x;
     else
       vf[kc] = x;
   }
@@ -249,19 +272,91 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
   };
   constexpr int kFirst = kHalves ? 1 : kPer;  // parts loaded at the top of an iteration
 
+  // Direct loads of the Q and dO tile of (query head hh, rows q0 ..) into
+  // stage `stage` (kDma): wave w's load i fills rows 4 (4 i + w) .. +3, lane
+  // l the 16 bytes at l * 16 of that block, fetching the chunk the swizzle
+  // puts there.  The tile's lse and D values still go through a register
+  // (load_stat / store_stat: they are transformed on the way).
+  const int dma_row = 4 * wave + (lane >> 4);
+  const int dma_off = dma_row * D * 2 + 16 * ((lane & 15) ^ chunk_swz(dma_row));
+  // The resources start at the tile's first row and end with the head, so
+  // that the per-lane offsets stay loop-invariant and rows past the end
+  // still read as zeros (the range check covers the per-lane offset only).
+  auto dma_tile = [&](int hh, int q0, int stage) {
+    const int64_t row0 = (bh0 + hh) * (int64_t)nq + q0;
+    const int bytes = (nq - q0) * D * 2;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint16_t*)a.q + row0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t gr = make_rsrc((const uint16_t*)a.dout + row0 * D, bytes);
+    uint16_t* qt_ = lds + stage * 2 * kTileElems;
+    uint16_t* gt_ = qt_ + kTileElems;
+#pragma unroll
+    for (int i = 0; i < kDmaPer; ++i) {
+      const int rows = 4 * (i * kBwdWaves + wave);
+      buf_load16_lds(qr, qt_ + rows * D, dma_off + i * kBwdWaves * 1024);
+      buf_load16_lds(gr, gt_ + rows * D, dma_off + i * kBwdWaves * 1024);
+    }
+  };
+  auto load_stat = [&](int hh, int q0) {
+    const int64_t bhq = bh0 + hh;
+    const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.lse + bhq * nq, nq * 4);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.delta + bhq * nq, nq * 4);
+    if (tid < kBT)
+      st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lr, (q0 + tid) * 4, 0, 0));
+    else if (tid < 2 * kBT)
+      st = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(dr, (q0 + tid - kBT) * 4, 0, 0));
+  };
+  auto store_stat = [&](int buf) {
+    if (tid < 2 * kBT) stat[buf][tid / kBT][tid % kBT] = tid < kBT ? lse_log2(st) : -st;
+  };
+  // LDS byte offsets of this lane's operands inside a DMA stage: Q and dO
+  // rows (row col, chunk 2 kc + grp; the 2 kc part applied per read as an
+  // XOR of 32 kc) and the transposed Q^T / dO^T reads (rows 4 grp +
+  // (lane % 16) / 4 and that + 8 of each 16-query chunk, bytes 64 db +
+  // 32 ((lane / 16) % 2) + 8 (lane % 4); the 64 db part applied as an XOR).
+  // The reads go through LDS byte addresses, with the swizzled part and
+  // the per-read offsets applied as XORs on aligned bases.  The bases pass
+  // through an empty asm, which keeps the compiler from folding them back
+  // into per-read address arithmetic (more instructions and registers).
+  uint32_t stat_b = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&stat[0][0][0];
+  uint32_t vrow_b = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)vlds + vrow_off;
+  uint32_t lds_b = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds;
+  asm("" : "+v"(stat_b), "+v"(vrow_b), "+v"(lds_b));
+  auto lds_f32x4 = [](uint32_t addr) {
+    return *(const __attribute__((address_space(3))) f32x4*)(uintptr_t)addr;
+  };
+  const int trow = 4 * grp + ((lane & 15) >> 2);
+  const int tx = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const uint32_t r_off = col * D * 2 + 16 * (grp ^ chunk_swz(col));
+  const uint32_t t_off0 = trow * D * 2 + 16 * (tx ^ chunk_swz(trow)) + 8 * (lane & 1);
+  const uint32_t t_off1 = (trow + 8) * D * 2 + 16 * (tx ^ chunk_swz(trow + 8)) + 8 * (lane & 1);
+
   const float c = a.scale_log2;
   f32x16 dkT[D / 32], dvT[D / 32];  // dK^T, dV^T: lane holds key kw0 + col
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dkT[db] = dvT[db] = (f32x16){};
 
-  load_part(0, qt_begin * kBT, 0, kFirst);
-  store_part(0, 0, kFirst);
-  if (kHalves) {
-    load_part(0, qt_begin * kBT, 1, 2);
-    store_part(0, 1, 2);
+  if constexpr (kDma) {
+    if (total_it > 0) {
+      dma_tile(0, qt_begin * kBT, 0);
+      load_stat(0, qt_begin * kBT);
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
+    if (total_it > 0) store_stat(0);
+  } else {
+    load_part(0, qt_begin * kBT, 0, kFirst);
+    store_part(0, 0, kFirst);
+    if (kHalves) {
+      load_part(0, qt_begin * kBT, 1, 2);
+      store_part(0, 1, 2);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // nothing is pending on any path into the loop (the compiler merges the
+  // two total_it tests above and would leave the K fragments "pending" on
+  // the path that skips them, then wait for them inside every iteration)
+  if constexpr (kDma) __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
 
   int hh = 0, qt = qt_begin;  // query head (within the group) and tile of step `it`
   for (int it = 0; it < total_it; ++it) {
@@ -271,12 +366,25 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     const bool wrap = qt + 1 == n_qt;
     const int hh_next = wrap ? hh + 1 : hh;
     const int q0_next = (wrap ? qt_begin : qt + 1) * kBT;
-    if (more) load_part(hh_next, q0_next, 0, kFirst);
+    if constexpr (kDma) {
+      // the next tile goes to the other stage, read last in the previous
+      // iteration (the barrier at its end has passed)
+      if (more) {
+        dma_tile(hh_next, q0_next, buf ^ 1);
+        load_stat(hh_next, q0_next);
+      }
+    } else {
+      if (more) load_part(hh_next, q0_next, 0, kFirst);
+    }
 
     // causal: a tile whose last query sees none of this wave's keys is empty
     const bool active = !(CAUSAL && q0 + kBT - 1 + off < kw0);
     const uint16_t* qrm = lds + buf * kStage;
     const uint16_t* grm = qrm + T::kRowElems;
+    const uint32_t stage_b = lds_b + buf * 2 * kTileElems * 2;
+    const uint32_t qr_b = stage_b + r_off, gr_b = stage_b + kTileElems * 2 + r_off;
+    const uint32_t qt0_b = stage_b + t_off0, qt1_b = stage_b + t_off1;
+    const uint32_t gt0_b = qt0_b + kTileElems * 2, gt1_b = qt1_b + kTileElems * 2;
 
     // S = Q K^T and dP - D = dO V^T - D: lane holds key kw0 + col of the
     // queries q0 + 8 (r/4) + 4 grp + r%4; the dP product starts from -D, so
@@ -285,21 +393,24 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     if (active) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 nd = *(const f32x4*)(&stat[buf][1][8 * j + 4 * grp]);
+        const f32x4 nd = kDma ? lds_f32x4(stat_b ^ (((buf * 2 + 1) * kBT + 8 * j + 4 * grp) * 4))
+                              : *(const f32x4*)(&stat[buf][1][8 * j + 4 * grp]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) dp[4 * j + e] = nd[e];
       }
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
-        const u32x4 qa = *(const u32x4*)(qrm + col * T::kRowStride + kc * 16 + grp * 8);
+        const u32x4 qa = kDma ? *(const lds_u32x4*)(uintptr_t)(qr_b ^ (32u * kc))
+                              : *(const u32x4*)(qrm + col * T::kRowStride + kc * 16 + grp * 8);
         s = HH::mfma(qa, kf[kc], s);
       }
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
-        const u32x4 ga = *(const u32x4*)(grm + col * T::kRowStride + kc * 16 + grp * 8);
+        const u32x4 ga = kDma ? *(const lds_u32x4*)(uintptr_t)(gr_b ^ (32u * kc))
+                              : *(const u32x4*)(grm + col * T::kRowStride + kc * 16 + grp * 8);
         u32x4 vb;
         if constexpr (kVLds)
-          vb = *(const u32x4*)(vrow + kc * 16);
+          vb = *(const lds_u32x4*)(uintptr_t)(vrow_b ^ (32u * kc));
         else
           vb = vf[kc];
         dp = HH::mfma(ga, vb, dp);
@@ -325,7 +436,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int j = 2 * ch + jj;
-        const f32x4 l4 = *(const f32x4*)(&stat[buf][0][8 * j + 4 * grp]);
+        const f32x4 l4 = kDma ? lds_f32x4(stat_b ^ (((buf * 2 + 0) * kBT + 8 * j + 4 * grp) * 4))
+                              : *(const f32x4*)(&stat[buf][0][8 * j + 4 * grp]);
         float pv[4], dsv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -341,7 +453,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
         pd[2 * jj + 1] = HH::pack(dsv[2], dsv[3]);
       }
     };
-    auto chunk = [&](int ch) {
+    auto chunk = [&](auto chc) {
+      const int ch = chc;
       uint32_t pp[4], pd[4];
       if (diag)
         weights(std::true_type{}, ch, pp, pd);
@@ -349,21 +462,66 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
         weights(std::false_type{}, ch, pp, pd);
       const u32x4 bp = {pp[0], pp[1], pp[2], pp[3]};
       const u32x4 bd = {pd[0], pd[1], pd[2], pd[3]};
+      if constexpr (kDma) {
+        // dO^T and Q^T by transpose reads in inline assembly (the
+        // compiler's own transpose-load intrinsic would wait for every load
+        // into LDS in flight), each d block's four reads in flight during
+        // the previous block's MFMAs
+        auto tread = [&](int db, u32x2 (&r)[4]) {
+          constexpr int o = decltype(chc)::value * 16 * D * 2;
+          r[0] = lds_read_tr16_b64<o>(gt0_b ^ (64u * db));
+          r[1] = lds_read_tr16_b64<o>(gt1_b ^ (64u * db));
+          r[2] = lds_read_tr16_b64<o>(qt0_b ^ (64u * db));
+          r[3] = lds_read_tr16_b64<o>(qt1_b ^ (64u * db));
+        };
+        auto tmma = [&](int db, const u32x2 (&r)[4]) {
+          const u32x4 ga = {r[0][0], r[0][1], r[1][0], r[1][1]};
+          const u32x4 qa = {r[2][0], r[2][1], r[3][0], r[3][1]};
+          dvT[db] = HH::mfma(ga, bp, dvT[db]);
+          dkT[db] = HH::mfma(qa, bd, dkT[db]);
+        };
+        static_assert(D / 32 == 4, "four d blocks");
+        u32x2 r0[4], r1[4];
+        tread(0, r0);
+        lds_wait_all(r0[0], r0[1], r0[2], r0[3]);
+        tread(1, r1);
+        tmma(0, r0);
+        lds_wait_all(r1[0], r1[1], r1[2], r1[3]);
+        tread(2, r0);
+        tmma(1, r1);
+        lds_wait_all(r0[0], r0[1], r0[2], r0[3]);
+        tread(3, r1);
+        tmma(2, r0);
+        lds_wait_all(r1[0], r1[1], r1[2], r1[3]);
+        tmma(3, r1);
+      } else {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const u32x4 ga = lds_tr_operand(grm, T::kRowStride, ch * 16, db * 32, lane);
-        const u32x4 qa = lds_tr_operand(qrm, T::kRowStride, ch * 16, db * 32, lane);
-        dvT[db] = HH::mfma(ga, bp, dvT[db]);
-        dkT[db] = HH::mfma(qa, bd, dkT[db]);
+        for (int db = 0; db < D / 32; ++db) {
+          const u32x4 ga = lds_tr_operand(grm, T::kRowStride, ch * 16, db * 32, lane);
+          const u32x4 qa = lds_tr_operand(qrm, T::kRowStride, ch * 16, db * 32, lane);
+          dvT[db] = HH::mfma(ga, bp, dvT[db]);
+          dkT[db] = HH::mfma(qa, bd, dkT[db]);
+        }
       }
     };
-    if (active) chunk(0);
-    if (kHalves && more) {
-      store_part(buf ^ 1, 0, 1);
-      load_part(hh_next, q0_next, 1, 2);
+    if constexpr (kDma) {
+      if (active) {
+        chunk(std::integral_constant<int, 0>{});
+        chunk(std::integral_constant<int, 1>{});
+      }
+      if (more) store_stat(buf ^ 1);
+      // the next tile's loads have landed (this thread's share) before the
+      // barrier that hands the stage over
+      __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
+    } else {
+      if (active) chunk(0);
+      if (kHalves && more) {
+        store_part(buf ^ 1, 0, 1);
+        load_part(hh_next, q0_next, 1, 2);
+      }
+      if (active) chunk(1);
+      if (more) store_part(buf ^ 1, kHalves ? 1 : 0, kPer);
     }
-    if (active) chunk(1);
-    if (more) store_part(buf ^ 1, kHalves ? 1 : 0, kPer);
     __syncthreads();
     hh = hh_next;
     qt = wrap ? qt_begin : qt + 1;
