@@ -398,22 +398,57 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 #pragma unroll
         for (int e = 0; e < 4; ++e) dp[4 * j + e] = nd[e];
       }
+      if constexpr (kDma) {
+        // the 2 D / 16 MFMAs of S and dP as one sequence, each operand read
+        // from LDS two MFMAs ahead of its use (the barriers keep the
+        // scheduler from sinking the reads to their uses)
+        constexpr int KC = D / 16;
+        auto rd_a = [&](int op) {
+          return *(const lds_u32x4*)(uintptr_t)((op < KC ? qr_b : gr_b) ^ (32u * (op % KC)));
+        };
+        auto rd_b = [&](int op) {
+          return *(const lds_u32x4*)(uintptr_t)(vrow_b ^ (32u * (op - KC)));
+        };
+        u32x4 ra[2], rb[2];
+        ra[0] = rd_a(0);
+        ra[1] = rd_a(1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        const u32x4 qa = kDma ? *(const lds_u32x4*)(uintptr_t)(qr_b ^ (32u * kc))
-                              : *(const u32x4*)(qrm + col * T::kRowStride + kc * 16 + grp * 8);
-        s = HH::mfma(qa, kf[kc], s);
-      }
+        for (int op = 0; op < 2 * KC; ++op) {
+          const u32x4 a_ = ra[op % 2];
+          const u32x4 b_ = op < KC ? kf[op % KC] : rb[op % 2];
+          if (op + 2 < 2 * KC) {
+            ra[op % 2] = rd_a(op + 2);
+            if (op + 2 >= KC) rb[op % 2] = rd_b(op + 2);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (op < KC)
+            s = HH::mfma(a_, b_, s);
+          else
+            dp = HH::mfma(a_, b_, dp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        constexpr int KC = D / 16;
+        auto rd_a = [&](int op) {
+          return *(const u32x4*)((op < KC ? qrm : grm) + col * T::kRowStride + (op % KC) * 16 +
+                                 grp * 8);
+        };
+        u32x4 ra[2];
+        ra[0] = rd_a(0);
+        ra[1] = rd_a(1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        const u32x4 ga = kDma ? *(const lds_u32x4*)(uintptr_t)(gr_b ^ (32u * kc))
-                              : *(const u32x4*)(grm + col * T::kRowStride + kc * 16 + grp * 8);
-        u32x4 vb;
-        if constexpr (kVLds)
-          vb = *(const lds_u32x4*)(uintptr_t)(vrow_b ^ (32u * kc));
-        else
-          vb = vf[kc];
-        dp = HH::mfma(ga, vb, dp);
+        for (int op = 0; op < 2 * KC; ++op) {
+          const u32x4 a_ = ra[op % 2];
+          if (op + 2 < 2 * KC) ra[op % 2] = rd_a(op + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          if (op < KC)
+            s = HH::mfma(a_, kf[op % KC], s);
+          else
+            dp = HH::mfma(a_, vf[op % KC], dp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
 
@@ -495,12 +530,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
         lds_wait_all(r1[0], r1[1], r1[2], r1[3]);
         tmma(3, r1);
       } else {
+        // every d block's transposed operands read before the first MFMA
+        u32x4 ga[D / 32], qa[D / 32];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const u32x4 ga = lds_tr_operand(grm, T::kRowStride, ch * 16, db * 32, lane);
-          const u32x4 qa = lds_tr_operand(qrm, T::kRowStride, ch * 16, db * 32, lane);
-          dvT[db] = HH::mfma(ga, bp, dvT[db]);
-          dkT[db] = HH::mfma(qa, bd, dkT[db]);
+          ga[db] = lds_tr_operand(grm, T::kRowStride, ch * 16, db * 32, lane);
+          qa[db] = lds_tr_operand(qrm, T::kRowStride, ch * 16, db * 32, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          dvT[db] = HH::mfma(ga[db], bp, dvT[db]);
+          dkT[db] = HH::mfma(qa[db], bd, dkT[db]);
         }
       }
     };
@@ -756,19 +797,43 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
         s[qb] = (f32x16){};
         dp[qb] = QB == 1 ? ndrow : (f32x16){};
       }
+      if constexpr (kDma) {
+        // the 2 D / 16 MFMAs of S and dP as one sequence, each K or V
+        // operand read from LDS two MFMAs ahead of its use (as in the dK/dV
+        // kernel)
+        static_assert(QB == 1, "one query block per wave with direct loads");
+        constexpr int KC = D / 16;
+        auto rd = [&](int op) {
+          return *(const lds_u32x4*)(uintptr_t)((op < KC ? kr_b : vr_b) ^ (32u * (op % KC)));
+        };
+        u32x4 ra[2];
+        ra[0] = rd(0);
+        ra[1] = rd(1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        const u32x4 ka = kDma ? *(const lds_u32x4*)(uintptr_t)(kr_b ^ (32u * kc))
-                              : *(const u32x4*)(krm + col * T::kRowStride + kc * 16 + grp * 8);
+        for (int op = 0; op < 2 * KC; ++op) {
+          const u32x4 a_ = ra[op % 2];
+          if (op + 2 < 2 * KC) ra[op % 2] = rd(op + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          if (op < KC)
+            s[0] = HH::mfma(a_, qf[0][op % KC], s[0]);
+          else
+            dp[0] = HH::mfma(a_, gf[0][op % KC], dp[0]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb] = HH::mfma(ka, qf[qb][kc], s[qb]);
-      }
+        for (int kc = 0; kc < D / 16; ++kc) {
+          const u32x4 ka = *(const u32x4*)(krm + col * T::kRowStride + kc * 16 + grp * 8);
 #pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        const u32x4 va = kDma ? *(const lds_u32x4*)(uintptr_t)(vr_b ^ (32u * kc))
-                              : *(const u32x4*)(vrm + col * T::kRowStride + kc * 16 + grp * 8);
+          for (int qb = 0; qb < QB; ++qb) s[qb] = HH::mfma(ka, qf[qb][kc], s[qb]);
+        }
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) dp[qb] = HH::mfma(va, gf[qb][kc], dp[qb]);
+        for (int kc = 0; kc < D / 16; ++kc) {
+          const u32x4 va = *(const u32x4*)(vrm + col * T::kRowStride + kc * 16 + grp * 8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) dp[qb] = HH::mfma(va, gf[qb][kc], dp[qb]);
+        }
       }
 
       // dS^T = P^T (dP^T - D).  The masked form runs only on diagonal and
