@@ -500,8 +500,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
       if constexpr (kDma) {
         // dO^T and Q^T by transpose reads in inline assembly (the
         // compiler's own transpose-load intrinsic would wait for every load
-        // into LDS in flight), each d block's four reads in flight during
-        // the previous block's MFMAs
+        // into LDS in flight), each d block's four reads issued two blocks
+        // ahead of its MFMAs; the scheduling barriers keep the MFMAs from
+        // sinking below later waits
         auto tread = [&](int db, u32x2 (&r)[4]) {
           constexpr int o = decltype(chc)::value * 16 * D * 2;
           r[0] = lds_read_tr16_b64<o>(gt0_b ^ (64u * db));
@@ -516,19 +517,23 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
           dkT[db] = HH::mfma(qa, bd, dkT[db]);
         };
         static_assert(D / 32 == 4, "four d blocks");
-        u32x2 r0[4], r1[4];
+        u32x2 r0[4], r1[4], r2[4];
         tread(0, r0);
-        lds_wait_all(r0[0], r0[1], r0[2], r0[3]);
         tread(1, r1);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait_keep4(r0[0], r0[1], r0[2], r0[3]);
+        tread(2, r2);
         tmma(0, r0);
-        lds_wait_all(r1[0], r1[1], r1[2], r1[3]);
-        tread(2, r0);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait_keep4(r1[0], r1[1], r1[2], r1[3]);
+        tread(3, r0);
         tmma(1, r1);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait_keep4(r2[0], r2[1], r2[2], r2[3]);
+        tmma(2, r2);
+        __builtin_amdgcn_sched_barrier(0);
         lds_wait_all(r0[0], r0[1], r0[2], r0[3]);
-        tread(3, r1);
-        tmma(2, r0);
-        lds_wait_all(r1[0], r1[1], r1[2], r1[3]);
-        tmma(3, r1);
+        tmma(3, r0);
       } else {
         // every d block's transposed operands read before the first MFMA
         u32x4 ga[D / 32], qa[D / 32];
@@ -841,6 +846,23 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
       // k0 + 8 (r/4) + 4 grp + r%4, so the key is masked (past the end, or
       // after the row's last visible key) when 8 (r/4) + r%4 exceeds one
       // per-lane limit.
+      // d = 128: the K^T operands of d blocks 0 and 1 (transpose reads in
+      // inline assembly: the compiler would make its own transpose-load
+      // intrinsic wait for every load into LDS in flight) are read while the
+      // weights are formed, each later block's two blocks ahead of its MFMAs
+      auto tread = [&](int db, u32x2 (&r)[2][2]) {
+        const uint32_t a0 = kt0_b ^ (64u * db), a1 = kt1_b ^ (64u * db);
+        r[0][0] = lds_read_tr16_b64<0>(a0);
+        r[0][1] = lds_read_tr16_b64<0>(a1);
+        r[1][0] = lds_read_tr16_b64<16 * D * 2>(a0);
+        r[1][1] = lds_read_tr16_b64<16 * D * 2>(a1);
+      };
+      u32x2 r0[2][2], r1[2][2], r2[2][2];
+      if constexpr (kDma) {
+        tread(0, r0);
+        tread(1, r1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       uint32_t pd[QB][8];
       auto weights = [&](auto masked, int qb) {
         const int my_q = qw0 + 32 * qb + col;
@@ -867,18 +889,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
       // dQ^T += K^T dS^T over the two 16-key chunks; each K^T operand feeds
       // every block.
       if constexpr (kDma) {
-        // K^T operands by transpose reads (inline assembly: the compiler
-        // would make its own transpose-load intrinsic wait for every load
-        // into LDS in flight), each d block's read in flight while the
-        // previous block's MFMAs run
         static_assert(QB == 1, "one 32-row block per wave at d = 128");
-        auto tread = [&](int db, u32x2 (&r)[2][2]) {
-          const uint32_t a0 = kt0_b ^ (64u * db), a1 = kt1_b ^ (64u * db);
-          r[0][0] = lds_read_tr16_b64<0>(a0);
-          r[0][1] = lds_read_tr16_b64<0>(a1);
-          r[1][0] = lds_read_tr16_b64<16 * D * 2>(a0);
-          r[1][1] = lds_read_tr16_b64<16 * D * 2>(a1);
-        };
         auto tmma = [&](int db, const u32x2 (&r)[2][2]) {
 #pragma unroll
           for (int ch = 0; ch < 2; ++ch) {
@@ -888,19 +899,23 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
             dqT[0][db] = HH::mfma(ka, bd, dqT[0][db]);
           }
         };
-        u32x2 r0[2][2], r1[2][2];
-        tread(0, r0);
-        lds_wait_all(r0[0][0], r0[0][1], r0[1][0], r0[1][1]);
-        tread(1, r1);
+        // (the scheduling barriers keep the MFMAs from sinking below later
+        // waits)
+        static_assert(D / 32 == 4, "four d blocks");
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait_keep4(r0[0][0], r0[0][1], r0[1][0], r0[1][1]);
+        tread(2, r2);
         tmma(0, r0);
-        lds_wait_all(r1[0][0], r1[0][1], r1[1][0], r1[1][1]);
-        tread(2, r0);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait_keep4(r1[0][0], r1[0][1], r1[1][0], r1[1][1]);
+        tread(3, r0);
         tmma(1, r1);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_wait_keep4(r2[0][0], r2[0][1], r2[1][0], r2[1][1]);
+        tmma(2, r2);
+        __builtin_amdgcn_sched_barrier(0);
         lds_wait_all(r0[0][0], r0[0][1], r0[1][0], r0[1][1]);
-        tread(3, r1);
-        tmma(2, r0);
-        lds_wait_all(r1[0][0], r1[0][1], r1[1][0], r1[1][1]);
-        tmma(3, r1);
+        tmma(3, r0);
       } else {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)

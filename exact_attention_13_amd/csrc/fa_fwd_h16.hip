@@ -23,6 +23,8 @@
 //     row so that the K reads and the transposed V reads (ds_read_b64_tr_b16)
 //     are free of bank conflicts.  The loads of a single-buffered tile sat
 //     exposed on the critical path: +5-7 % on the d = 128 causal shapes.
+//     The K and V^T operands are read from LDS two MFMAs ahead of their use
+//     (+3-4 % together on the same shapes).
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16}: each lane ends up with
 //     32 scores of ONE query (16 per 32-key block), the other 32 scores of
 //     that query sit in the lane 32 positions away.  Row statistics are thus
@@ -333,8 +335,10 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
       auto qk = [&](int qb, f32x16 (&sv)[SB / 32]) {
         if constexpr (C::kDma) {
           // K fragments read two ahead of the MFMA that takes them; the
-          // scheduling barriers keep the compiler from pulling each read
-          // down to its MFMA (+2 % on the d = 128 causal shapes)
+          // scheduling barriers on both sides of each MFMA keep the compiler
+          // from pulling each read down to its MFMA or behind the one before
+          // (+2 %, and 1-2 % more once the second barrier made it a true
+          // two-ahead, on the d = 128 causal shapes)
           static_assert(SB == 32, "one 32-key block per compute step");
           constexpr int KP = 2;
           u32x4 kf[KP];
@@ -347,6 +351,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
             const u32x4 ka = kf[kc % KP];
             if (kc + KP < D / 16)
               kf[kc % KP] = *(const lds_u32x4*)(uintptr_t)(ka_b ^ (32u * (kc + KP)));
+            __builtin_amdgcn_sched_barrier(0);
             sv[0] = HH::mfma(ka, qf[qb][kc], sv[0]);
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -465,6 +470,11 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
           lds_wait_all(r[0][0], r[0][1], r[1][0], r[1][1]);
         }
       };
+      // r's reads done, the four issued after them (the next block's) may
+      // still be in flight
+      auto vwait_next = [&](vpair& r) {
+        if constexpr (C::kDma) lds_wait_keep4(r[0][0], r[0][1], r[1][0], r[1][1]);
+      };
       auto vmma = [&](int qb, int db, const vpair& r) {
 #pragma unroll
         for (int pc = 0; pc < SB / 16; ++pc) {
@@ -477,26 +487,33 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
 
       if constexpr (C::kDma) {
         static_assert(QB == 1 && D == 128, "DMA tiles: one 32-row block per wave, d = 128");
-        // d block 0's operands are read while the softmax runs; each later
-        // block's read is in flight during the previous block's MFMAs.
+        // d blocks 0 and 1's operands are read while the softmax runs; each
+        // later block's read is issued two blocks ahead of its MFMAs.
+        static_assert(D / 32 == 4, "four d blocks");
         f32x16 s0[SB / 32];
         qk(0, s0);
         mask(0, s0);
-        vpair r0, r1;
+        // (The scheduling barriers keep the compiler from sinking the reads
+        // below the softmax and the MFMAs below later waits.)
+        vpair r0, r1, r2;
         vread(0, r0);
+        vread(1, r1);
+        __builtin_amdgcn_sched_barrier(0);
         const float lt0 = fast(0, s0);
         settle(0, s0, lt0);
-        vwait(r0);
-        vread(1, r1);
+        vwait_next(r0);
+        vread(2, r2);
         vmma(0, 0, r0);
-        vwait(r1);
-        vread(2, r0);
+        __builtin_amdgcn_sched_barrier(0);
+        vwait_next(r1);
+        vread(3, r0);
         vmma(0, 1, r1);
+        __builtin_amdgcn_sched_barrier(0);
+        vwait_next(r2);
+        vmma(0, 2, r2);
+        __builtin_amdgcn_sched_barrier(0);
         vwait(r0);
-        vread(3, r1);
-        vmma(0, 2, r0);
-        vwait(r1);
-        vmma(0, 3, r1);
+        vmma(0, 3, r0);
       } else if constexpr (QB == 2) {
         // The two 32-row blocks are independent: issued in this order, the
         // QK MFMAs of block 1 run under the softmax of block 0 and the PV

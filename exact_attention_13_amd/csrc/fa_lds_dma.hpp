@@ -4,9 +4,13 @@
 // A tile of 32 rows x 128 bf16/fp16 columns sits in LDS unpadded, 256 bytes
 // per row, with its 16-byte chunks XOR-swizzled per row; the 16-byte buffer
 // loads that carry the LDS bit write it without passing through registers.
-// The compiler counts neither those loads in its own vmcnt waits nor the
-// LDS they write, so the kernels wait for them by hand (kVmcntWait) and
-// read transposed operands through inline assembly (see below).
+// The compiler leaves those loads out of the waits it places for ordinary
+// loads, so the kernels wait for them by hand (kVmcntWait).  It does make
+// its transpose-load intrinsic wait for every one in flight, and, in a
+// kernel that declares more than one LDS array, every LDS read as well
+// (the arrays' alias scopes mark the loads): so the kernels that use them
+// declare one LDS array and read transposed operands through inline
+// assembly (see below).
 #pragma once
 
 #include "fa_h16.hpp"
@@ -55,6 +59,14 @@ __device__ __forceinline__ u32x2 lds_read_tr16_b64(uint32_t addr) {
 __device__ __forceinline__ void lds_wait_all(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+#endif
+}
+// The same, leaving the four most recent LDS operations in flight: enough
+// for four reads that were followed by at least four more (LDS operations
+// complete in order), such as the next operand block's reads.
+__device__ __forceinline__ void lds_wait_keep4(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 #endif
 }
 
