@@ -19,11 +19,12 @@
 //     them as A operands (their accumulators give every lane one key), and
 //     dV^T += dO^T P, dK^T += Q^T dS read the transposed operands straight
 //     from the same rows with the LDS transpose load, in the query order in
-//     which the P and dS accumulators are, unchanged, the B operands.  At
-//     d = 128 the Q and dO tiles go HBM -> LDS directly, two stages deep, in
-//     the swizzled layout of fa_lds_dma.hpp, and the V rows wait in LDS in the
-//     same layout (C3 backward 1.99 -> 1.91 ms, C5 3.69 -> 3.55, G2
-//     1.94 -> 1.89);
+//     which the P and dS accumulators are, unchanged, the B operands.  The
+//     Q and dO tiles go HBM -> LDS directly, two stages deep, in unpadded
+//     swizzled rows (row_swz), and at d = 128 the V rows wait in LDS in the
+//     same layout (against register staging into padded rows: C3 backward
+//     1.99 -> 1.91 ms, C5 3.69 -> 3.55, G2 1.94 -> 1.89; at d = 64 within
+//     1 %);
 //   * bwd_dq_kernel: the forward kernel's shape: a workgroup owns 128 queries
 //     (Q and dO fragments in registers, one query per lane in S^T = K Q^T and
 //     dP^T = V dO^T) and streams 32-key tiles of K and V (row-major); dS^T is
@@ -47,6 +48,18 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdRows = 32 * kBwdWaves;  // keys (dK/dV) or queries (dQ) per workgroup
 constexpr int kBT = 32;                   // rows of a streamed tile
+
+// Slot swizzle of a tile row of D bf16/fp16 columns: 256-byte rows
+// (d = 128) take chunk_swz; 128-byte rows (d = 64, 8 chunks) take
+// (r1, r0 ^ r2, r0 ^ r3), which keeps both the 16-row reads and the
+// transpose reads free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int row_swz(int r) {
+  if constexpr (D == 128)
+    return chunk_swz(r);
+  else
+    return (((r >> 1) & 1) << 2) | (((r ^ (r >> 2)) & 1) << 1) | ((r ^ (r >> 3)) & 1);
+}
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // Waves per SIMD that the register allocation must leave room for.  Both
@@ -65,19 +78,18 @@ template <int D> constexpr int kDqWaves = 2;
 template <int D> constexpr int kDqBlocks = D == 64 ? 2 : 1;
 template <int D> constexpr int kDqRows = 32 * kBwdWaves * kDqBlocks<D>;
 
-// Row padding of the LDS tiles, for 64 banks of 4 bytes.  Two access
-// patterns read the same rows: 16-byte row reads (16 lanes at the same
-// column of 16 consecutive rows: conflict-free when the row stride is an odd
-// multiple of 4 banks) and transpose loads (32 lanes over 4 consecutive rows
-// x 64 bytes: conflict-free only for a stride of an odd multiple of 16 banks).
-// No stride serves both; 12 or 20 banks (mod 64) keep the row reads
-// conflict-free and the transpose loads 2-way: d = 128 pads by 24 elements
-// (76 banks), d = 64 by 8 (36 banks).  Measured against a pad of 8 at
-// d = 128: 3-4 % faster backward (C3, C5, G2); a pad of 40 (84 banks) is no
-// faster.
+// Row padding of the register-staged LDS tiles (the dQ kernel at d = 64;
+// the other tiles are unpadded and swizzled, row_swz), for 64 banks of 4
+// bytes.  Two access patterns read the same rows: 16-byte row reads (16
+// lanes at the same column of 16 consecutive rows: conflict-free when the
+// row stride is an odd multiple of 4 banks) and transpose loads (32 lanes
+// over 4 consecutive rows x 64 bytes: conflict-free only for a stride of an
+// odd multiple of 16 banks).  No stride serves both; 12 or 20 banks (mod 64)
+// keep the row reads conflict-free and the transpose loads 2-way: d = 64
+// pads by 8 elements (36 banks).
 template <int D>
 struct BwdTile {
-  static constexpr int kRowStride = D + (D == 128 ? 24 : 8);  // elements per padded row
+  static constexpr int kRowStride = D + 8;  // elements per padded row
   static constexpr int kRowElems = kBT * kRowStride;
   static constexpr int kPairUnits = (kBT / 2) * (D / 8);  // (row pair, 8 columns)
 };
@@ -138,14 +150,11 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 template <bool BF16, bool CAUSAL, int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDkdvWaves<D>))) void bwd_dkdv_kernel(BwdArgs a) {
   using HH = Half<BF16>;
-  using T = BwdTile<D>;
-  constexpr int kStage = 2 * T::kRowElems;  // Q rows, dO rows
-  // d = 128: Q and dO tiles loaded HBM -> LDS directly into two stages of
-  // unpadded swizzled rows (fa_lds_dma.hpp); d = 64: register staging
-  constexpr bool kDma = D == 128;
+  // Q and dO tiles go HBM -> LDS directly into two stages of unpadded
+  // swizzled rows (row_swz, fa_lds_dma.hpp)
   constexpr int kTileElems = kBT * D;
   constexpr int kDmaPer = kTileElems * 2 / (kBwdThreads * 16);  // loads per thread per tile
-  static_assert(!kDma || (kDmaPer * kBwdThreads * 16 == kTileElems * 2 && kBwdWaves % 4 == 0),
+  static_assert(kDmaPer * kBwdThreads * 16 == kTileElems * 2 && kBwdWaves % 4 == 0,
                 "DMA tile split");
   // At d = 128 the V rows of the workgroup's keys wait in LDS (see below).
   constexpr bool kVLds = D == 128;
@@ -154,7 +163,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
   // tags the direct loads with an alias scope, and then makes every LDS read
   // after one wait for it.)  The statistics are aligned to their size, so
   // that an offset inside them can be applied as an XOR.
-  constexpr int kQgBytes = (kDma ? 2 * 2 * kTileElems : 2 * kStage) * 2;
+  constexpr int kQgBytes = 2 * 2 * kTileElems * 2;
   constexpr int kVBytes = kVLds ? kBwdRows * D * 2 : 0;
   constexpr int kStatBytes = 2 * 2 * kBT * 4;
   static_assert((kQgBytes + kVBytes) % kStatBytes == 0 && kQgBytes % 1024 == 0, "LDS regions");
@@ -215,70 +224,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
   const int n_iter = max(0, n_qt - qt_begin);
   const int total_it = n_iter * (h_hi - h_lo);
 
-  // Staging of one query tile: (row pair, 8 columns) units of Q then dO,
-  // plus the tile's 32 lse and 32 D values.  Part i of the units goes through
-  // register slot i; at d = 128 there are two parts (Q, then dO) and they
-  // share one slot: the Q half of the next tile is stored halfway through the
-  // current tile, before the dO half is loaded, so only one half is in flight
-  // (16 fewer live registers, which lets two waves share a SIMD).
-  constexpr int kUnits = 2 * T::kPairUnits;
-  constexpr int kPer = (kUnits + kBwdThreads - 1) / kBwdThreads;
-  constexpr bool kHalves = kPer == 2;
-  constexpr int kSlots = kHalves ? 1 : kPer;
-  u32x4 sx[kSlots], sy[kSlots];
-  float st = 0.f;
-  // Units are dealt by whole waves (kPairUnits is a multiple of 64), so the
-  // Q-or-dO choice is wave-uniform and the buffer resource stays scalar.
-  static_assert(T::kPairUnits % 64 == 0 && kUnits % kBwdThreads == 0, "unit split");
-  auto load_part = [&](int hh, int q0, int i0, int i1) {
-    const int64_t bhq = bh0 + hh;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc((const uint16_t*)a.q + bhq * nq * D, nq * D * 2);
-    const __amdgpu_buffer_rsrc_t gr =
-        make_rsrc((const uint16_t*)a.dout + bhq * nq * D, nq * D * 2);
-#pragma unroll
-    for (int i = i0; i < i1; ++i) {
-      const int u = tid + i * kBwdThreads;
-      const int w = u % T::kPairUnits;
-      const int p = w % (kBT / 2), cc = w / (kBT / 2);
-      const int sl = kHalves ? 0 : i;
-      if (wave * 64 + i * kBwdThreads < T::kPairUnits)
-        load_pair<D>(qr, q0, p, cc, sx[sl], sy[sl]);
-      else
-        load_pair<D>(gr, q0, p, cc, sx[sl], sy[sl]);
-    }
-    if (i0 == 0) {
-      const __amdgpu_buffer_rsrc_t lr = make_rsrc(a.lse + bhq * nq, nq * 4);
-      const __amdgpu_buffer_rsrc_t dr = make_rsrc(a.delta + bhq * nq, nq * 4);
-      if (tid < kBT)
-        st = __builtin_bit_cast(float,
-                                __builtin_amdgcn_raw_buffer_load_b32(lr, (q0 + tid) * 4, 0, 0));
-      else if (tid < 2 * kBT)
-        st = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(dr, (q0 + tid - kBT) * 4, 0, 0));
-    }
-  };
-  auto store_part = [&](int buf, int i0, int i1) {
-    uint16_t* base = lds + buf * kStage;
-#pragma unroll
-    for (int i = i0; i < i1; ++i) {
-      const int u = tid + i * kBwdThreads;
-      const int w = u % T::kPairUnits;
-      const int p = w % (kBT / 2), cc = w / (kBT / 2);
-      const int sl = kHalves ? 0 : i;
-      const bool first = wave * 64 + i * kBwdThreads < T::kPairUnits;
-      store_rows<D>(base + (first ? 0 : T::kRowElems), p, cc, sx[sl], sy[sl]);
-    }
-    if (i0 == 0 && tid < 2 * kBT) stat[buf][tid / kBT][tid % kBT] = tid < kBT ? lse_log2(st) : -st;
-  };
-  constexpr int kFirst = kHalves ? 1 : kPer;  // parts loaded at the top of an iteration
+  float st = 0.f;  // this thread's lse or D value of the next tile
 
   // Direct loads of the Q and dO tile of (query head hh, rows q0 ..) into
-  // stage `stage` (kDma): wave w's load i fills rows 4 (4 i + w) .. +3, lane
-  // l the 16 bytes at l * 16 of that block, fetching the chunk the swizzle
-  // puts there.  The tile's lse and D values still go through a register
+  // stage `stage`: wave w's load i fills the kLoadRows rows from
+  // kLoadRows (4 i + w) on, lane l the 16 bytes at l * 16 of that block,
+  // fetching the chunk the swizzle puts there.  The tile's lse and D values still go through a register
   // (load_stat / store_stat: they are transformed on the way).
-  const int dma_row = 4 * wave + (lane >> 4);
-  const int dma_off = dma_row * D * 2 + 16 * ((lane & 15) ^ chunk_swz(dma_row));
+  constexpr int kChunks = D / 8;           // 16-byte chunks per tile row
+  constexpr int kLoadRows = 64 / kChunks;  // tile rows one wave's load fills
+  const int dma_row = kLoadRows * wave + lane / kChunks;
+  const int dma_off = dma_row * D * 2 + 16 * ((lane % kChunks) ^ row_swz<D>(dma_row));
   // The resources start at the tile's first row and end with the head, so
   // that the per-lane offsets stay loop-invariant and rows past the end
   // still read as zeros (the range check covers the per-lane offset only).
@@ -291,7 +247,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     uint16_t* gt_ = qt_ + kTileElems;
 #pragma unroll
     for (int i = 0; i < kDmaPer; ++i) {
-      const int rows = 4 * (i * kBwdWaves + wave);
+      const int rows = kLoadRows * (i * kBwdWaves + wave);
       buf_load16_lds(qr, qt_ + rows * D, dma_off + i * kBwdWaves * 1024);
       buf_load16_lds(gr, gt_ + rows * D, dma_off + i * kBwdWaves * 1024);
     }
@@ -327,36 +283,26 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
   };
   const int trow = 4 * grp + ((lane & 15) >> 2);
   const int tx = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const uint32_t r_off = col * D * 2 + 16 * (grp ^ chunk_swz(col));
-  const uint32_t t_off0 = trow * D * 2 + 16 * (tx ^ chunk_swz(trow)) + 8 * (lane & 1);
-  const uint32_t t_off1 = (trow + 8) * D * 2 + 16 * (tx ^ chunk_swz(trow + 8)) + 8 * (lane & 1);
+  const uint32_t r_off = col * D * 2 + 16 * (grp ^ row_swz<D>(col));
+  const uint32_t t_off0 = trow * D * 2 + 16 * (tx ^ row_swz<D>(trow)) + 8 * (lane & 1);
+  const uint32_t t_off1 = (trow + 8) * D * 2 + 16 * (tx ^ row_swz<D>(trow + 8)) + 8 * (lane & 1);
 
   const float c = a.scale_log2;
   f32x16 dkT[D / 32], dvT[D / 32];  // dK^T, dV^T: lane holds key kw0 + col
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dkT[db] = dvT[db] = (f32x16){};
 
-  if constexpr (kDma) {
-    if (total_it > 0) {
-      dma_tile(0, qt_begin * kBT, 0);
-      load_stat(0, qt_begin * kBT);
-    }
-    __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
-    if (total_it > 0) store_stat(0);
-  } else {
-    load_part(0, qt_begin * kBT, 0, kFirst);
-    store_part(0, 0, kFirst);
-    if (kHalves) {
-      load_part(0, qt_begin * kBT, 1, 2);
-      store_part(0, 1, 2);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
+  if (total_it > 0) {
+    dma_tile(0, qt_begin * kBT, 0);
+    load_stat(0, qt_begin * kBT);
   }
+  __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
+  if (total_it > 0) store_stat(0);
   __syncthreads();
   // nothing is pending on any path into the loop (the compiler merges the
   // two total_it tests above and would leave the K fragments "pending" on
   // the path that skips them, then wait for them inside every iteration)
-  if constexpr (kDma) __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
+  __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
 
   int hh = 0, qt = qt_begin;  // query head (within the group) and tile of step `it`
   for (int it = 0; it < total_it; ++it) {
@@ -366,21 +312,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     const bool wrap = qt + 1 == n_qt;
     const int hh_next = wrap ? hh + 1 : hh;
     const int q0_next = (wrap ? qt_begin : qt + 1) * kBT;
-    if constexpr (kDma) {
-      // the next tile goes to the other stage, read last in the previous
-      // iteration (the barrier at its end has passed)
-      if (more) {
-        dma_tile(hh_next, q0_next, buf ^ 1);
-        load_stat(hh_next, q0_next);
-      }
-    } else {
-      if (more) load_part(hh_next, q0_next, 0, kFirst);
+    // the next tile goes to the other stage, read last in the previous
+    // iteration (the barrier at its end has passed)
+    if (more) {
+      dma_tile(hh_next, q0_next, buf ^ 1);
+      load_stat(hh_next, q0_next);
     }
 
     // causal: a tile whose last query sees none of this wave's keys is empty
     const bool active = !(CAUSAL && q0 + kBT - 1 + off < kw0);
-    const uint16_t* qrm = lds + buf * kStage;
-    const uint16_t* grm = qrm + T::kRowElems;
     const uint32_t stage_b = lds_b + buf * 2 * kTileElems * 2;
     const uint32_t qr_b = stage_b + r_off, gr_b = stage_b + kTileElems * 2 + r_off;
     const uint32_t qt0_b = stage_b + t_off0, qt1_b = stage_b + t_off1;
@@ -393,63 +333,44 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
     if (active) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 nd = kDma ? lds_f32x4(stat_b ^ (((buf * 2 + 1) * kBT + 8 * j + 4 * grp) * 4))
-                              : *(const f32x4*)(&stat[buf][1][8 * j + 4 * grp]);
+        const f32x4 nd = lds_f32x4(stat_b ^ (((buf * 2 + 1) * kBT + 8 * j + 4 * grp) * 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) dp[4 * j + e] = nd[e];
       }
-      if constexpr (kDma) {
-        // the 2 D / 16 MFMAs of S and dP as one sequence, each operand read
-        // from LDS two MFMAs ahead of its use (the barriers keep the
-        // scheduler from sinking the reads to their uses)
-        constexpr int KC = D / 16;
-        auto rd_a = [&](int op) {
-          return *(const lds_u32x4*)(uintptr_t)((op < KC ? qr_b : gr_b) ^ (32u * (op % KC)));
-        };
-        auto rd_b = [&](int op) {
-          return *(const lds_u32x4*)(uintptr_t)(vrow_b ^ (32u * (op - KC)));
-        };
-        u32x4 ra[2], rb[2];
-        ra[0] = rd_a(0);
-        ra[1] = rd_a(1);
-        __builtin_amdgcn_sched_barrier(0);
+      // the 2 D / 16 MFMAs of S and dP as one sequence, each operand read
+      // from LDS two MFMAs ahead of its use (the barriers keep the
+      // scheduler from sinking the reads to their uses)
+      constexpr int KC = D / 16;
+      auto rd_a = [&](int op) {
+        return *(const lds_u32x4*)(uintptr_t)((op < KC ? qr_b : gr_b) ^ (32u * (op % KC)));
+      };
+      auto rd_b = [&](int op) {
+        return *(const lds_u32x4*)(uintptr_t)(vrow_b ^ (32u * (op - KC)));
+      };
+      u32x4 ra[2], rb[2];
+      ra[0] = rd_a(0);
+      ra[1] = rd_a(1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int op = 0; op < 2 * KC; ++op) {
-          const u32x4 a_ = ra[op % 2];
-          const u32x4 b_ = op < KC ? kf[op % KC] : rb[op % 2];
-          if (op + 2 < 2 * KC) {
-            ra[op % 2] = rd_a(op + 2);
-            if (op + 2 >= KC) rb[op % 2] = rd_b(op + 2);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          if (op < KC)
-            s = HH::mfma(a_, b_, s);
-          else
-            dp = HH::mfma(a_, b_, dp);
-          __builtin_amdgcn_sched_barrier(0);
+      for (int op = 0; op < 2 * KC; ++op) {
+        const u32x4 a_ = ra[op % 2];
+        u32x4 b_;
+        if constexpr (kVLds)
+          b_ = op < KC ? kf[op % KC] : rb[op % 2];
+        else
+          b_ = op < KC ? kf[op % KC] : vf[op % KC];
+        if (op + 2 < 2 * KC) {
+          ra[op % 2] = rd_a(op + 2);
+          if (kVLds && op + 2 >= KC) rb[op % 2] = rd_b(op + 2);
         }
-      } else {
-        constexpr int KC = D / 16;
-        auto rd_a = [&](int op) {
-          return *(const u32x4*)((op < KC ? qrm : grm) + col * T::kRowStride + (op % KC) * 16 +
-                                 grp * 8);
-        };
-        u32x4 ra[2];
-        ra[0] = rd_a(0);
-        ra[1] = rd_a(1);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int op = 0; op < 2 * KC; ++op) {
-          const u32x4 a_ = ra[op % 2];
-          if (op + 2 < 2 * KC) ra[op % 2] = rd_a(op + 2);
-          __builtin_amdgcn_sched_barrier(0);
-          if (op < KC)
-            s = HH::mfma(a_, kf[op % KC], s);
-          else
-            dp = HH::mfma(a_, vf[op % KC], dp);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        if (op < KC)
+          s = HH::mfma(a_, b_, s);
+        else
+          dp = HH::mfma(a_, b_, dp);
+        __builtin_amdgcn_sched_barrier(0);
       }
+
     }
 
     // Only the causal mask is applied.  A query row past the end has zero Q
@@ -471,8 +392,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int j = 2 * ch + jj;
-        const f32x4 l4 = kDma ? lds_f32x4(stat_b ^ (((buf * 2 + 0) * kBT + 8 * j + 4 * grp) * 4))
-                              : *(const f32x4*)(&stat[buf][0][8 * j + 4 * grp]);
+        const f32x4 l4 = lds_f32x4(stat_b ^ (((buf * 2 + 0) * kBT + 8 * j + 4 * grp) * 4));
         float pv[4], dsv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -497,77 +417,64 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
         weights(std::false_type{}, ch, pp, pd);
       const u32x4 bp = {pp[0], pp[1], pp[2], pp[3]};
       const u32x4 bd = {pd[0], pd[1], pd[2], pd[3]};
-      if constexpr (kDma) {
-        // dO^T and Q^T by transpose reads in inline assembly (the
-        // compiler's own transpose-load intrinsic would wait for every load
-        // into LDS in flight), each d block's four reads issued two blocks
-        // ahead of its MFMAs; the scheduling barriers keep the MFMAs from
-        // sinking below later waits
-        auto tread = [&](int db, u32x2 (&r)[4]) {
-          constexpr int o = decltype(chc)::value * 16 * D * 2;
-          r[0] = lds_read_tr16_b64<o>(gt0_b ^ (64u * db));
-          r[1] = lds_read_tr16_b64<o>(gt1_b ^ (64u * db));
-          r[2] = lds_read_tr16_b64<o>(qt0_b ^ (64u * db));
-          r[3] = lds_read_tr16_b64<o>(qt1_b ^ (64u * db));
-        };
-        auto tmma = [&](int db, const u32x2 (&r)[4]) {
-          const u32x4 ga = {r[0][0], r[0][1], r[1][0], r[1][1]};
-          const u32x4 qa = {r[2][0], r[2][1], r[3][0], r[3][1]};
-          dvT[db] = HH::mfma(ga, bp, dvT[db]);
-          dkT[db] = HH::mfma(qa, bd, dkT[db]);
-        };
-        static_assert(D / 32 == 4, "four d blocks");
-        u32x2 r0[4], r1[4], r2[4];
+      // dO^T and Q^T by transpose reads in inline assembly (the
+      // compiler's own transpose-load intrinsic would wait for every load
+      // into LDS in flight), each d block's four reads issued two blocks
+      // ahead of its MFMAs; the scheduling barriers keep the MFMAs from
+      // sinking below later waits
+      auto tread = [&](int db, u32x2 (&r)[4]) {
+        constexpr int o = decltype(chc)::value * 16 * D * 2;
+        r[0] = lds_read_tr16_b64<o>(gt0_b ^ (64u * db));
+        r[1] = lds_read_tr16_b64<o>(gt1_b ^ (64u * db));
+        r[2] = lds_read_tr16_b64<o>(qt0_b ^ (64u * db));
+        r[3] = lds_read_tr16_b64<o>(qt1_b ^ (64u * db));
+      };
+      auto tmma = [&](int db, const u32x2 (&r)[4]) {
+        const u32x4 ga = {r[0][0], r[0][1], r[1][0], r[1][1]};
+        const u32x4 qa = {r[2][0], r[2][1], r[3][0], r[3][1]};
+        dvT[db] = HH::mfma(ga, bp, dvT[db]);
+        dkT[db] = HH::mfma(qa, bd, dkT[db]);
+      };
+      if constexpr (D / 32 == 2) {
+        u32x2 r0[4], r1[4];
         tread(0, r0);
         tread(1, r1);
         __builtin_amdgcn_sched_barrier(0);
         lds_wait_keep4(r0[0], r0[1], r0[2], r0[3]);
-        tread(2, r2);
         tmma(0, r0);
         __builtin_amdgcn_sched_barrier(0);
-        lds_wait_keep4(r1[0], r1[1], r1[2], r1[3]);
-        tread(3, r0);
+        lds_wait_all(r1[0], r1[1], r1[2], r1[3]);
         tmma(1, r1);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_wait_keep4(r2[0], r2[1], r2[2], r2[3]);
-        tmma(2, r2);
-        __builtin_amdgcn_sched_barrier(0);
-        lds_wait_all(r0[0], r0[1], r0[2], r0[3]);
-        tmma(3, r0);
       } else {
-        // every d block's transposed operands read before the first MFMA
-        u32x4 ga[D / 32], qa[D / 32];
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          ga[db] = lds_tr_operand(grm, T::kRowStride, ch * 16, db * 32, lane);
-          qa[db] = lds_tr_operand(qrm, T::kRowStride, ch * 16, db * 32, lane);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          dvT[db] = HH::mfma(ga[db], bp, dvT[db]);
-          dkT[db] = HH::mfma(qa[db], bd, dkT[db]);
-        }
+      static_assert(D / 32 == 4, "two or four d blocks");
+      u32x2 r0[4], r1[4], r2[4];
+      tread(0, r0);
+      tread(1, r1);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_wait_keep4(r0[0], r0[1], r0[2], r0[3]);
+      tread(2, r2);
+      tmma(0, r0);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_wait_keep4(r1[0], r1[1], r1[2], r1[3]);
+      tread(3, r0);
+      tmma(1, r1);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_wait_keep4(r2[0], r2[1], r2[2], r2[3]);
+      tmma(2, r2);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_wait_all(r0[0], r0[1], r0[2], r0[3]);
+      tmma(3, r0);
       }
+
     };
-    if constexpr (kDma) {
-      if (active) {
-        chunk(std::integral_constant<int, 0>{});
-        chunk(std::integral_constant<int, 1>{});
-      }
-      if (more) store_stat(buf ^ 1);
-      // the next tile's loads have landed (this thread's share) before the
-      // barrier that hands the stage over
-      __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
-    } else {
-      if (active) chunk(0);
-      if (kHalves && more) {
-        store_part(buf ^ 1, 0, 1);
-        load_part(hh_next, q0_next, 1, 2);
-      }
-      if (active) chunk(1);
-      if (more) store_part(buf ^ 1, kHalves ? 1 : 0, kPer);
+    if (active) {
+      chunk(std::integral_constant<int, 0>{});
+      chunk(std::integral_constant<int, 1>{});
     }
+    if (more) store_stat(buf ^ 1);
+    // the next tile's loads have landed (this thread's share) before the
+    // barrier that hands the stage over
+    __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
     __syncthreads();
     hh = hh_next;
     qt = wrap ? qt_begin : qt + 1;
