@@ -284,6 +284,10 @@ def main():
     if args.splits is not None:
         w = w.with_(splits=args.splits)
     q, k, v = make_inputs(w)
+    # SHA-256 of each input's stored bits (host copy, first 16 hex digits):
+    # identifies the exact synthetic tensors a run used
+    input_sha = {n: hashlib.sha256(t.contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()[:16]
+                 for n, t in zip("qkv", (q, k, v))}
     dev = torch.device("cuda:0")
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     o = torch.empty_like(qd)
@@ -292,7 +296,10 @@ def main():
 
     splits, workspace = 1, None
     if args.which == "bwd":
-        dout = make_upstream(w, w.seed + 100).to(dev)
+        dout_h = make_upstream(w, w.seed + 100)
+        input_sha["dO"] = hashlib.sha256(
+            dout_h.contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()[:16]
+        dout = dout_h.to(dev)
         if w.extended:
             binding.fwd_ex(qd, kd, vd, w.scale, w.causal, out=o, lse=lse, stream=stream)
         else:
@@ -410,7 +417,8 @@ def main():
                                     f" H_kv={w.h_kv} N_kv={w.n_kv} splits={splits} (fa_fwd_ex)")
                                    if w.extended else ""),
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "flops_per_step": flops, "parallelism": "single GPU"},
+                   "flops_per_step": flops, "parallelism": "single GPU",
+                   "inputs_sha256": input_sha},
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "algorithmic_bytes": w.io_bytes,
