@@ -25,15 +25,16 @@
 //     same layout (against register staging into padded rows: C3 backward
 //     1.99 -> 1.91 ms, C5 3.69 -> 3.55, G2 1.94 -> 1.89; at d = 64 within
 //     1 %);
-//   * bwd_dq_kernel: the forward kernel's shape: a workgroup owns 128 queries
-//     (Q and dO fragments in registers, one query per lane in S^T = K Q^T and
+//   * bwd_dq_kernel: the forward kernel's shape: a workgroup owns 128 (d = 128)
+//     or 256 (d = 64, two 32-query blocks per wave) queries (Q and dO
+//     fragments in registers, one query per lane in S^T = K Q^T and
 //     dP^T = V dO^T) and streams 32-key tiles of K and V (row-major); dS^T is
 //     the B operand of dQ^T += K^T dS^T, whose K^T operand comes from the K
-//     rows through the transpose load.  At d = 128 the tiles go HBM -> LDS
-//     directly, three stages deep, in the forward's swizzled layout
-//     (fa_lds_dma.hpp): the single-buffered register staging sat on the
-//     critical path (C3 backward 2.06 -> 1.99 ms, C5 3.76 -> 3.70, G2
-//     1.96 -> 1.92).
+//     rows through the transpose load.  The tiles go HBM -> LDS directly,
+//     three stages deep, in unpadded swizzled rows (row_swz): the
+//     single-buffered register staging sat on the critical path (C3 backward
+//     2.06 -> 1.99 ms, C5 3.76 -> 3.70, G2 1.96 -> 1.92; at d = 64 against
+//     double-buffered staging into padded rows, C4 3.63 -> 3.58).
 // Causal masking, ragged tails and the -inf guard follow the forward kernels.
 #include <type_traits>
 
@@ -77,37 +78,6 @@ template <int D> constexpr int kDqWaves = 2;
 // instead of three: 1-1.5 % faster backward (C4, G1).
 template <int D> constexpr int kDqBlocks = D == 64 ? 2 : 1;
 template <int D> constexpr int kDqRows = 32 * kBwdWaves * kDqBlocks<D>;
-
-// Row padding of the register-staged LDS tiles (the dQ kernel at d = 64;
-// the other tiles are unpadded and swizzled, row_swz), for 64 banks of 4
-// bytes.  Two access patterns read the same rows: 16-byte row reads (16
-// lanes at the same column of 16 consecutive rows: conflict-free when the
-// row stride is an odd multiple of 4 banks) and transpose loads (32 lanes
-// over 4 consecutive rows x 64 bytes: conflict-free only for a stride of an
-// odd multiple of 16 banks).  No stride serves both; 12 or 20 banks (mod 64)
-// keep the row reads conflict-free and the transpose loads 2-way: d = 64
-// pads by 8 elements (36 banks).
-template <int D>
-struct BwdTile {
-  static constexpr int kRowStride = D + 8;  // elements per padded row
-  static constexpr int kRowElems = kBT * kRowStride;
-  static constexpr int kPairUnits = (kBT / 2) * (D / 8);  // (row pair, 8 columns)
-};
-
-// Rows 2p and 2p+1, columns 8cc .. 8cc+7, of a [rows, D] array.
-template <int D>
-__device__ __forceinline__ void load_pair(__amdgpu_buffer_rsrc_t r, int row0, int p, int cc,
-                                          u32x4& x, u32x4& y) {
-  x = buf_load16(r, ((row0 + 2 * p) * D + cc * 8) * 2);
-  y = buf_load16(r, ((row0 + 2 * p + 1) * D + cc * 8) * 2);
-}
-
-template <int D>
-__device__ __forceinline__ void store_rows(uint16_t* rm, int p, int cc, u32x4 x, u32x4 y) {
-  using T = BwdTile<D>;
-  *(u32x4*)(rm + (2 * p) * T::kRowStride + cc * 8) = x;
-  *(u32x4*)(rm + (2 * p + 1) * T::kRowStride + cc * 8) = y;
-}
 
 // logsumexp in exp2 units; a row without a visible key (LSE = -inf) gets +inf
 // so that every weight exp2(s c - lse2) is 0 instead of inf.
@@ -523,19 +493,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 template <bool BF16, bool CAUSAL, int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDqWaves<D>))) void bwd_dq_kernel(BwdArgs a, int n_qt, int total) {
   using HH = Half<BF16>;
-  using T = BwdTile<D>;
   constexpr int QB = kDqBlocks<D>;
   constexpr int kRows = kDqRows<D>;
-  constexpr int kStage = 2 * T::kRowElems;  // K rows, V rows
-  // d = 128: K and V tiles loaded HBM -> LDS directly, unpadded swizzled
-  // rows, three stages (the forward's layout, fa_lds_dma.hpp); d = 64:
-  // register staging into two stages of padded rows
-  constexpr bool kDma = D == 128;
+  // K and V tiles loaded HBM -> LDS directly into three stages of unpadded
+  // swizzled rows (row_swz)
   constexpr int kTileElems = kBT * D;
   constexpr int kDmaPer = kTileElems * 2 / (kBwdThreads * 16);  // loads per thread per tile
-  static_assert(!kDma || (kDmaPer * kBwdThreads * 16 == kTileElems * 2 && kBwdWaves % 4 == 0),
+  static_assert(kDmaPer * kBwdThreads * 16 == kTileElems * 2 && kBwdWaves % 4 == 0,
                 "DMA tile split");
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[kDma ? 3 * 2 * kTileElems : 2 * kStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[3 * 2 * kTileElems];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -563,26 +529,25 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
   const int n_kv = (kv_end + kBT - 1) / kBT;
   const int wave_kv_end = CAUSAL ? max(0, min(qw0 + 32 * QB + off, nk)) : nk;
 
-  // Direct HBM -> LDS loads (kDma): wave w's load i fills tile rows
-  // 4 (4 i + w) .. +3, lane l the 16 bytes at l * 16 of that block (slot
-  // l % 16 of row 4 (4 i + w) + l / 16), fetching the chunk the swizzle puts
-  // there.
-  const int dma_row = 4 * wave + (lane >> 4);
-  const int dma_off = dma_row * D * 2 + 16 * ((lane & 15) ^ chunk_swz(dma_row));
+  // Direct HBM -> LDS loads: wave w's load i fills the kLoadRows tile rows
+  // from kLoadRows (4 i + w) on, lane l the 16 bytes at l * 16 of that
+  // block, fetching the chunk the swizzle puts there.
+  constexpr int kChunks = D / 8;           // 16-byte chunks per tile row
+  constexpr int kLoadRows = 64 / kChunks;  // tile rows one wave's load fills
+  const int dma_row = kLoadRows * wave + lane / kChunks;
+  const int dma_off = dma_row * D * 2 + 16 * ((lane % kChunks) ^ row_swz<D>(dma_row));
   auto dma_tile = [&](int k0, int stage) {
     uint16_t* kt = lds + stage * 2 * kTileElems;
     uint16_t* vt = kt + kTileElems;
     const int g = k0 * D * 2 + dma_off;
 #pragma unroll
     for (int i = 0; i < kDmaPer; ++i) {
-      const int rows = 4 * (i * kBwdWaves + wave);
+      const int rows = kLoadRows * (i * kBwdWaves + wave);
       buf_load16_lds(kr, kt + rows * D, g + i * kBwdWaves * 1024);
       buf_load16_lds(vr, vt + rows * D, g + i * kBwdWaves * 1024);
     }
   };
-  if constexpr (kDma) {
-    if (n_kv > 0) dma_tile(0, 0);
-  }
+  if (n_kv > 0) dma_tile(0, 0);
 
   // Q and dO rows of this lane's queries as B operands.
   u32x4 qf[QB][D / 16], gf[QB][D / 16];
@@ -608,38 +573,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
     for (int r = 0; r < 16; ++r) ndrow[r] = -drow[0];
   }
 
-  // Staging of one key tile: (row pair, 8 columns) units of K then V.
-  constexpr int kUnits = 2 * T::kPairUnits;
-  constexpr int kPer = (kUnits + kBwdThreads - 1) / kBwdThreads;
-  u32x4 sx[kPer], sy[kPer];
-  static_assert(T::kPairUnits % 64 == 0 && kUnits % kBwdThreads == 0, "unit split");
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int u = tid + i * kBwdThreads;
-      const int w = u % T::kPairUnits;
-      const int p = w % (kBT / 2), cc = w / (kBT / 2);
-      if (wave * 64 + i * kBwdThreads < T::kPairUnits)
-        load_pair<D>(kr, k0, p, cc, sx[i], sy[i]);
-      else
-        load_pair<D>(vr, k0, p, cc, sx[i], sy[i]);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* base = lds + buf * kStage;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int u = tid + i * kBwdThreads;
-      const int w = u % T::kPairUnits;
-      const int p = w % (kBT / 2), cc = w / (kBT / 2);
-      if (wave * 64 + i * kBwdThreads < T::kPairUnits) {
-        store_rows<D>(base, p, cc, sx[i], sy[i]);
-      } else {
-        store_rows<D>(base + T::kRowElems, p, cc, sx[i], sy[i]);
-      }
-    }
-  };
-
   const float c = a.scale_log2;
   f32x16 dqT[QB][D / 32];  // dQ^T: lane holds query qw0 + 32 qb + col
 #pragma unroll
@@ -647,54 +580,39 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dqT[qb][db] = (f32x16){};
 
-  // LDS byte offsets of this lane's operands inside a DMA stage: K and V
+  // LDS byte offsets of this lane's operands inside a stage: K and V
   // rows (row col, chunk 2 kc + grp; the 2 kc part applied per read as an
   // XOR of 32 kc) and the transposed K^T reads (rows 4 grp + (lane % 16) / 4
   // and that + 8 of each 16-key chunk, bytes 64 db + 32 ((lane / 16) % 2) +
   // 8 (lane % 4); the 64 db part applied per read as an XOR)
   const int trow = 4 * grp + ((lane & 15) >> 2);
   const int tx = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const uint32_t r_off = col * D * 2 + 16 * (grp ^ chunk_swz(col));
-  const uint32_t t_off0 = trow * D * 2 + 16 * (tx ^ chunk_swz(trow)) + 8 * (lane & 1);
-  const uint32_t t_off1 = (trow + 8) * D * 2 + 16 * (tx ^ chunk_swz(trow + 8)) + 8 * (lane & 1);
+  const uint32_t r_off = col * D * 2 + 16 * (grp ^ row_swz<D>(col));
+  const uint32_t t_off0 = trow * D * 2 + 16 * (tx ^ row_swz<D>(trow)) + 8 * (lane & 1);
+  const uint32_t t_off1 = (trow + 8) * D * 2 + 16 * (tx ^ row_swz<D>(trow + 8)) + 8 * (lane & 1);
 
-  if constexpr (kDma) {
-    // tile 0 went out before Q; tile 1 now; everything (Q, dO, lse, D
-    // included) waited for here, once, as in the forward
-    if (n_kv > 1) dma_tile(kBT, 1);
-    __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
-  } else {
-    load_tile(0);
-    store_tile(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
+  // tile 0 went out before Q; tile 1 now; everything (Q, dO, lse, D
+  // included) waited for here, once, as in the forward
+  if (n_kv > 1) dma_tile(kBT, 1);
+  __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
 
   for (int t = 0; t < n_kv; ++t) {
     const int k0 = t * kBT;
     const bool more = t + 1 < n_kv;
-    int buf;
-    if constexpr (kDma) {
-      // this thread's loads of tile t landed once at most tile t + 1's are
-      // in flight; the barrier makes every thread's share visible and says
-      // that tile t - 1 (whose stage tile t + 2 overwrites) is done
-      if (more)
-        __builtin_amdgcn_s_waitcnt(kVmcntWait<2 * kDmaPer>);
-      else
-        __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (t + 2 < n_kv) dma_tile(k0 + 2 * kBT, (t + 2) % 3);
-      buf = t % 3;
-    } else {
-      buf = t & 1;
-      if (more) load_tile(k0 + kBT);
-    }
+    // this thread's loads of tile t landed once at most tile t + 1's are
+    // in flight; the barrier makes every thread's share visible and says
+    // that tile t - 1 (whose stage tile t + 2 overwrites) is done
+    if (more)
+      __builtin_amdgcn_s_waitcnt(kVmcntWait<2 * kDmaPer>);
+    else
+      __builtin_amdgcn_s_waitcnt(kVmcntWait<0>);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + 2 < n_kv) dma_tile(k0 + 2 * kBT, (t + 2) % 3);
+    const int buf = t % 3;
 
     if (k0 < wave_kv_end) {
-      const uint16_t* krm = lds + buf * kStage;
-      const uint16_t* vrm = krm + T::kRowElems;
       const uint32_t stage_b =
           (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(lds + buf * 2 * kTileElems);
       const uint32_t kr_b = stage_b + r_off, vr_b = stage_b + kTileElems * 2 + r_off;
@@ -709,11 +627,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
         s[qb] = (f32x16){};
         dp[qb] = QB == 1 ? ndrow : (f32x16){};
       }
-      if constexpr (kDma) {
-        // the 2 D / 16 MFMAs of S and dP as one sequence, each K or V
-        // operand read from LDS two MFMAs ahead of its use (as in the dK/dV
-        // kernel)
-        static_assert(QB == 1, "one query block per wave with direct loads");
+      {
+        // the 2 D / 16 MFMA steps of S and dP as one sequence, each K or V
+        // operand read from LDS two steps ahead of its use (as in the dK/dV
+        // kernel) and fed to the products of every block
         constexpr int KC = D / 16;
         auto rd = [&](int op) {
           return *(const lds_u32x4*)(uintptr_t)((op < KC ? kr_b : vr_b) ^ (32u * (op % KC)));
@@ -727,24 +644,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
           const u32x4 a_ = ra[op % 2];
           if (op + 2 < 2 * KC) ra[op % 2] = rd(op + 2);
           __builtin_amdgcn_sched_barrier(0);
-          if (op < KC)
-            s[0] = HH::mfma(a_, qf[0][op % KC], s[0]);
-          else
-            dp[0] = HH::mfma(a_, gf[0][op % KC], dp[0]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            if (op < KC)
+              s[qb] = HH::mfma(a_, qf[qb][op % KC], s[qb]);
+            else
+              dp[qb] = HH::mfma(a_, gf[qb][op % KC], dp[qb]);
+          }
           __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-#pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-          const u32x4 ka = *(const u32x4*)(krm + col * T::kRowStride + kc * 16 + grp * 8);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb] = HH::mfma(ka, qf[qb][kc], s[qb]);
-        }
-#pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-          const u32x4 va = *(const u32x4*)(vrm + col * T::kRowStride + kc * 16 + grp * 8);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) dp[qb] = HH::mfma(va, gf[qb][kc], dp[qb]);
         }
       }
 
@@ -753,10 +660,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
       // k0 + 8 (r/4) + 4 grp + r%4, so the key is masked (past the end, or
       // after the row's last visible key) when 8 (r/4) + r%4 exceeds one
       // per-lane limit.
-      // d = 128: the K^T operands of d blocks 0 and 1 (transpose reads in
-      // inline assembly: the compiler would make its own transpose-load
-      // intrinsic wait for every load into LDS in flight) are read while the
-      // weights are formed, each later block's two blocks ahead of its MFMAs
+      // The K^T operands of d blocks 0 and 1 (transpose reads in inline
+      // assembly: the compiler would make its own transpose-load intrinsic
+      // wait for every load into LDS in flight) are read while the weights
+      // are formed, each later block's two blocks ahead of its MFMAs.
       auto tread = [&](int db, u32x2 (&r)[2][2]) {
         const uint32_t a0 = kt0_b ^ (64u * db), a1 = kt1_b ^ (64u * db);
         r[0][0] = lds_read_tr16_b64<0>(a0);
@@ -765,11 +672,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
         r[1][1] = lds_read_tr16_b64<16 * D * 2>(a1);
       };
       u32x2 r0[2][2], r1[2][2], r2[2][2];
-      if constexpr (kDma) {
-        tread(0, r0);
-        tread(1, r1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      tread(0, r0);
+      tread(1, r1);
+      __builtin_amdgcn_sched_barrier(0);
       uint32_t pd[QB][8];
       auto weights = [&](auto masked, int qb) {
         const int my_q = qw0 + 32 * qb + col;
@@ -795,21 +700,29 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
 
       // dQ^T += K^T dS^T over the two 16-key chunks; each K^T operand feeds
       // every block.
-      if constexpr (kDma) {
-        static_assert(QB == 1, "one 32-row block per wave at d = 128");
-        auto tmma = [&](int db, const u32x2 (&r)[2][2]) {
+      auto tmma = [&](int db, const u32x2 (&r)[2][2]) {
 #pragma unroll
-          for (int ch = 0; ch < 2; ++ch) {
-            const u32x4 ka = {r[ch][0][0], r[ch][0][1], r[ch][1][0], r[ch][1][1]};
-            const u32x4 bd = {pd[0][4 * ch], pd[0][4 * ch + 1], pd[0][4 * ch + 2],
-                              pd[0][4 * ch + 3]};
-            dqT[0][db] = HH::mfma(ka, bd, dqT[0][db]);
+        for (int ch = 0; ch < 2; ++ch) {
+          const u32x4 ka = {r[ch][0][0], r[ch][0][1], r[ch][1][0], r[ch][1][1]};
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const u32x4 bd = {pd[qb][4 * ch], pd[qb][4 * ch + 1], pd[qb][4 * ch + 2],
+                              pd[qb][4 * ch + 3]};
+            dqT[qb][db] = HH::mfma(ka, bd, dqT[qb][db]);
           }
-        };
-        // (the scheduling barriers keep the MFMAs from sinking below later
-        // waits)
-        static_assert(D / 32 == 4, "four d blocks");
+        }
+      };
+      // (the scheduling barriers keep the MFMAs from sinking below later
+      // waits)
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (D / 32 == 2) {
+        lds_wait_keep4(r0[0][0], r0[0][1], r0[1][0], r0[1][1]);
+        tmma(0, r0);
         __builtin_amdgcn_sched_barrier(0);
+        lds_wait_all(r1[0][0], r1[0][1], r1[1][0], r1[1][1]);
+        tmma(1, r1);
+      } else {
+        static_assert(D / 32 == 4, "two or four d blocks");
         lds_wait_keep4(r0[0][0], r0[0][1], r0[1][0], r0[1][1]);
         tread(2, r2);
         tmma(0, r0);
@@ -823,25 +736,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDq
         __builtin_amdgcn_sched_barrier(0);
         lds_wait_all(r0[0][0], r0[0][1], r0[1][0], r0[1][1]);
         tmma(3, r0);
-      } else {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int ch = 0; ch < 2; ++ch) {
-            const u32x4 ka = lds_tr_operand(krm, T::kRowStride, ch * 16, db * 32, lane);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-              const u32x4 bd = {pd[qb][4 * ch], pd[qb][4 * ch + 1], pd[qb][4 * ch + 2],
-                                pd[qb][4 * ch + 3]};
-              dqT[qb][db] = HH::mfma(ka, bd, dqT[qb][db]);
-            }
-          }
       }
-    }
-
-    if constexpr (!kDma) {
-      if (more) store_tile(buf ^ 1);
-      __syncthreads();
     }
   }
 
