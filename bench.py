@@ -30,7 +30,11 @@ visible pair).  Prints ONE JSON line with:
                         was taken on the current kernel source, else null;
                         ``kernel_ms_cold_median`` times further calls made
                         right after reading a 512 MiB buffer (L2 and MALL
-                        flushed), so K/V start from HBM;
+                        flushed), so K/V start from HBM; ``mfma_loop_tflops``
+                        is the rate of a plain MFMA loop of the same input
+                        type on every SIMD (libfa_probe.so), measured after
+                        the timed steps at the clock the chip then holds, and
+                        ``frac_of_mfma_loop`` the kernel's rate against it;
   cpu_baseline          the fp64 oracle timed on the host cores on a bounded
                         row sample of the same workload (reported baseline),
                         with the CPU model, the host's core counts, the
@@ -238,6 +242,9 @@ def main():
                     help="calls after the timed steps, each preceded by a 512 MiB read that "
                          "flushes the caches; "
                          "their median duration is roofline.kernel_ms_cold_median (0: skip)")
+    ap.add_argument("--no-mfma-loop", action="store_true",
+                    help="skip the MFMA-loop rate (roofline.mfma_loop_tflops: independent "
+                         "32x32 MFMAs on every SIMD, measured after the timed steps)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, run a plain device copy of this many bytes "
                          "(calibrates the HBM traffic counters)")
@@ -383,6 +390,13 @@ def main():
         cold_ms = round(cold_sorted[len(cold_sorted) // 2], 5)
         del flush, sink
 
+    # The dense MFMA rate of a plain MFMA loop on this GPU, measured right
+    # after the attention calls (same warm chip), for the FLOP-bound lines.
+    mfma_loop = None
+    if not args.no_mfma_loop:
+        from exact_attention_13_amd import probe
+        mfma_loop = probe.mfma_tflops(w.dtype, stream=stream)
+
     flops = w.flops * (2.5 if args.which == "bwd" else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -434,6 +448,9 @@ def main():
                      "kernel_ms_median": round(kernel_ms[len(kernel_ms) // 2], 5),
                      "kernel_ms_cold_median": cold_ms},
     }
+    if mfma_loop is not None and not hbm_bound:
+        out["roofline"]["mfma_loop_tflops"] = round(mfma_loop, 1)
+        out["roofline"]["frac_of_mfma_loop"] = round(achieved / mfma_loop, 4)
     if not args.no_cpu_baseline:
         if args.which == "bwd":
             out["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, dout.cpu(), args.cpu_seconds)

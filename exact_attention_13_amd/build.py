@@ -1,4 +1,5 @@
-"""Build step for libfa: compiles the HIP sources for gfx950 into libfa.so.
+"""Build step for libfa: compiles the HIP sources for gfx950 into libfa.so
+(and the benchmark's MFMA-rate probe into libfa_probe.so).
 
 Run ``python -m exact_attention_13_amd.build``.  The library is built
 in-tree (``exact_attention_13_amd/libfa.so``) so that it travels with the
@@ -23,6 +24,9 @@ ARCH = "gfx950"
 
 SOURCES = ["fa_api.hip", "fa_api_bwd.hip", "fa_fwd_h16.hip", "fa_fwd_f32.hip", "fa_combine.hip",
            "fa_bwd_h16.hip", "fa_bwd_f32.hip"]
+# The benchmark's MFMA-rate probe: a library of its own, not part of libfa.
+PROBE_LIB = PKG / "libfa_probe.so"
+PROBE_SOURCES = ["mfma_probe.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 are generated.
 HIPCC_FLAGS = [
@@ -66,7 +70,21 @@ def build(verbose: bool = False) -> Path:
         sys.stderr.write("\n".join(l for l in r.stderr.splitlines()
                                    if not any(n in l for n in noise)))
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
+
+
+def build_probe() -> Path:
+    """Compile libfa_probe.so (the measured MFMA-loop rate the benchmark
+    reports beside the published peak)."""
+    tmp = PROBE_LIB.with_name(PROBE_LIB.name + ".tmp")
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", str(tmp), *[str(CSRC / s) for s in PROBE_SOURCES]]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr)
+        raise RuntimeError(f"hipcc failed ({r.returncode}) building libfa_probe")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 def resource_table() -> str:
