@@ -5,8 +5,8 @@ seeded upstream gradient dO, and compares dQ, dK, dV element by element with
 ``oracle.bwd`` (fp64 gradients of sum(dO * O) computed from the same stored
 bits).
 
-Tolerance (not stated by the task for gradients; derived from the
-arithmetic).  The kernels round P and dS to the input type for the MFMA
+Tolerance (no accuracy target is stated for gradients; this one is derived
+from the arithmetic).  The kernels round P and dS to the input type for the MFMA
 operands, and round dQ, dK, dV once from fp32 accumulators; each of these
 three roundings is relative, at most one unit roundoff of the type (bf16
 2^-8, fp16 2^-11).  With u = 2^-9 for bf16 (half its unit roundoff) and

@@ -4,7 +4,8 @@ Every case runs the library through its C ABI (``binding.fwd`` -> ``fa_fwd``)
 on seeded synthetic inputs and compares O and LSE element by element with the
 three-pass fp64 oracle on the same bits.
 
-Tolerances (fixed by the task for the forward output):
+Tolerances of the forward output (the stated accuracy targets; LSE's own bound
+follows that of O):
   * fp32 inputs: max |O - O_ref| <= 1e-4 and max |LSE - LSE_ref| <= 1e-4;
   * bf16/fp16 inputs: max |O - O_ref| <= 2e-2 and
     ||O - O_ref||_2 / ||O_ref||_2 <= 5e-3, max |LSE - LSE_ref| <= 2e-2.
