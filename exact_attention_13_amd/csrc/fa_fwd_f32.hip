@@ -298,6 +298,72 @@ __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// 16-byte buffer load written as inline assembly (offsets past the
+// resource's range read as zeros).  The compiler places no wait for it: the
+// kernel waits by hand with tiny_vm_wait before any use, and never lets the
+// result die before that wait (a load still in flight would otherwise land
+// in registers given to another value).
+__device__ __forceinline__ u32x4 tiny_buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  u32x4 v;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(byte_off), "s"(r));
+#else
+  v = (u32x4){(uint32_t)byte_off, 0u, 0u, 0u};
+#endif
+  return v;
+}
+// Wait until at most N vector-memory operations are in flight, passing one
+// register buffer's loads through the wait so that no use of them can be
+// scheduled before it.
+template <int N, int KL, int VL>
+__device__ __forceinline__ void tiny_vm_wait(u32x4 (&k)[KL], u32x4 (&v)[4][VL]);
+template <>
+__device__ __forceinline__ void tiny_vm_wait<8, 4, 1>(u32x4 (&k)[4], u32x4 (&v)[4][1]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(8)" : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3]),
+               "+v"(v[0][0]), "+v"(v[1][0]), "+v"(v[2][0]), "+v"(v[3][0]));
+#endif
+}
+template <>
+__device__ __forceinline__ void tiny_vm_wait<0, 4, 1>(u32x4 (&k)[4], u32x4 (&v)[4][1]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3]),
+               "+v"(v[0][0]), "+v"(v[1][0]), "+v"(v[2][0]), "+v"(v[3][0]));
+#endif
+}
+template <>
+__device__ __forceinline__ void tiny_vm_wait<16, 8, 2>(u32x4 (&k)[8], u32x4 (&v)[4][2]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(16)" : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3]), "+v"(k[4]),
+               "+v"(k[5]), "+v"(k[6]), "+v"(k[7]), "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[1][0]),
+               "+v"(v[1][1]), "+v"(v[2][0]), "+v"(v[2][1]), "+v"(v[3][0]), "+v"(v[3][1]));
+#endif
+}
+template <>
+__device__ __forceinline__ void tiny_vm_wait<0, 8, 2>(u32x4 (&k)[8], u32x4 (&v)[4][2]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3]), "+v"(k[4]),
+               "+v"(k[5]), "+v"(k[6]), "+v"(k[7]), "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[1][0]),
+               "+v"(v[1][1]), "+v"(v[2][0]), "+v"(v[2][1]), "+v"(v[3][0]), "+v"(v[3][1]));
+#endif
+}
+
+template <int N, int QL>
+__device__ __forceinline__ void tiny_vm_wait_q(u32x4 (&q)[QL]);
+template <>
+__device__ __forceinline__ void tiny_vm_wait_q<16, 4>(u32x4 (&q)[4]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(16)" : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]));
+#endif
+}
+template <>
+__device__ __forceinline__ void tiny_vm_wait_q<32, 8>(u32x4 (&q)[8]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(32)" : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(q[4]),
+               "+v"(q[5]), "+v"(q[6]), "+v"(q[7]));
+#endif
+}
+
 // max / sum over the four lane groups (lanes j, j + 16, j + 32, j + 48)
 __device__ __forceinline__ float quad_max(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
@@ -330,14 +396,13 @@ __global__ __launch_bounds__(kTinyThreads) void fwd_f32_tiny_kernel(FwdArgs a, i
   const __amdgpu_buffer_rsrc_t kr = make_rsrc((const float*)a.k + kvhead, NK * D * 4);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc((const float*)a.v + kvhead, NK * D * 4);
 
-  // query row q0 + j, columns g DQ .. g DQ + DQ - 1 (rows past the end read 0)
-  float qv[DQ];
+  // query row q0 + j, columns g DQ .. g DQ + DQ - 1 (rows past the end read
+  // 0); loaded like the K/V tiles below (inline assembly, waited for by
+  // hand), so that no load the compiler counts is in flight at the loop
+  u32x4 qq[DQ / 4];
 #pragma unroll
-  for (int i = 0; i < DQ / 4; ++i) {
-    const f32x4 x = __builtin_bit_cast(f32x4, buf_load16(qr, ((q0 + j) * D + g * DQ + 4 * i) * 4));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) qv[4 * i + e] = x[e];
-  }
+  for (int i = 0; i < DQ / 4; ++i) qq[i] = tiny_buf_load16(qr, ((q0 + j) * D + g * DQ + 4 * i) * 4);
+  float qv[DQ];  // filled from qq once it has landed
 
   int kstop = NK;
   if (CAUSAL) kstop = max(0, min(kstop, q0 + kTinyRows + off));
@@ -346,28 +411,34 @@ __global__ __launch_bounds__(kTinyThreads) void fwd_f32_tiny_kernel(FwdArgs a, i
   // this wave's tiles: wave, wave + NWV, ...; operands of tile t:
   // K row t*16 + j, columns g DQ ..; V rows t*16 + 4g + r, columns TD j ..
   // They rotate through two register buffers: the wave's next tile loads
-  // while the current one is computed (a deeper ring measured no faster).
+  // while the current one is computed.  The loads are inline assembly with
+  // the waits placed by hand (tiny_vm_wait): the compiler's own waits for
+  // loads still in flight across the loop's back edge fell back to waiting
+  // for all of them, the other buffer's prefetch included, so the loop ran
+  // at one load latency per tile.  Every buffer is refilled on every pass
+  // (tiles past the end read as zeros through the buffer range check and are
+  // never computed), and every load is waited for before its registers die.
   constexpr int NB = 2;
-  float kf[NB][DQ], vf[NB][4][TD];
+  constexpr int KL = DQ / 4, VL = TD / 4;  // 16-byte loads per K row, per V row
+  constexpr int kLoadsPerBuf = KL + 4 * VL;
+  static_assert(kLoadsPerBuf <= 16, "buffer loads per wait");
+  u32x4 kq[NB][KL], vq[NB][4][VL];
   auto load = [&](int buf, int t) {
     const int k0 = t * 16;
 #pragma unroll
-    for (int i = 0; i < DQ / 4; ++i) {
-      const f32x4 x =
-          __builtin_bit_cast(f32x4, buf_load16(kr, ((k0 + j) * D + g * DQ + 4 * i) * 4));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kf[buf][4 * i + e] = x[e];
-    }
+    for (int i = 0; i < KL; ++i)
+      kq[buf][i] = tiny_buf_load16(kr, ((k0 + j) * D + g * DQ + 4 * i) * 4);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int i = 0; i < TD / 4; ++i) {
-        const f32x4 x = __builtin_bit_cast(
-            f32x4, buf_load16(vr, ((k0 + 4 * g + r) * D + TD * j + 4 * i) * 4));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vf[buf][r][4 * i + e] = x[e];
-      }
+      for (int i = 0; i < VL; ++i)
+        vq[buf][r][i] = tiny_buf_load16(vr, ((k0 + 4 * g + r) * D + TD * j + 4 * i) * 4);
   };
+  // buffer buf has landed once at most the other buffer's loads, issued
+  // after it, are in flight
+  auto wait_buf = [&](int buf) { tiny_vm_wait<(NB - 1) * kLoadsPerBuf, KL, VL>(kq[buf], vq[buf]); };
+  auto kf = [&](int buf, int m) { return __uint_as_float(kq[buf][m >> 2][m & 3]); };
+  auto vf = [&](int buf, int r, int u) { return __uint_as_float(vq[buf][r][u >> 2][u & 3]); };
 
   const float c = a.scale_log2;
   float m_run = kNegInf, l_run = 0.f;
@@ -383,7 +454,7 @@ __global__ __launch_bounds__(kTinyThreads) void fwd_f32_tiny_kernel(FwdArgs a, i
     const int k0 = t * 16;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < DQ; ++m) s = mfma16(kf[buf][m], qv[m], s);
+    for (int m = 0; m < DQ; ++m) s = mfma16(kf(buf, m), qv[m], s);
     // lane (j, g) register r: key k0 + 4g + r of query my_q
     if (k0 + 16 > NK || (CAUSAL && k0 + 15 > q0 + off)) {
 #pragma unroll
@@ -415,17 +486,24 @@ __global__ __launch_bounds__(kTinyThreads) void fwd_f32_tiny_kernel(FwdArgs a, i
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int u = 0; u < TD; ++u) oacc[u] = mfma16(vf[buf][r][u], p[r], oacc[u]);
-    if (t + NB * NWV < n_tiles) load(buf, t + NB * NWV);
+      for (int u = 0; u < TD; ++u) oacc[u] = mfma16(vf(buf, r, u), p[r], oacc[u]);
   };
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-    if (wave + b * NWV < n_tiles) load(b, wave + b * NWV);
+  for (int b = 0; b < NB; ++b) load(b, wave + b * NWV);
+  tiny_vm_wait_q<NB * kLoadsPerBuf>(qq);  // Q has landed (issued before both buffers)
+#pragma unroll
+  for (int m = 0; m < DQ; ++m) qv[m] = __uint_as_float(qq[m >> 2][m & 3]);
   for (int t = wave; t < n_tiles; t += NB * NWV) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b) {
+      wait_buf(b);
       if (t + b * NWV < n_tiles) step(b, t + b * NWV);
+      load(b, t + b * NWV + NB * NWV);
+    }
   }
+  // the last refills (past the end) must land before their registers die
+#pragma unroll
+  for (int b = 0; b < NB; ++b) tiny_vm_wait<0, KL, VL>(kq[b], vq[b]);
 
   // Merge the waves: O_w (unnormalised, this lane's columns g DQ .. of row
   // j), l_w (the lane sum over the four lane groups) and m_w.
