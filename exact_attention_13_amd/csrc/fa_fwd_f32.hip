@@ -372,10 +372,19 @@ __device__ __forceinline__ float quad_max(float x) {
   return half_swap_max(x);
 }
 
-template <int D, bool CAUSAL>
+// TU: output tiles of 16 columns per workgroup.  With TU < TD the D / 16
+// tiles of a 16-row block are shared out among TD / TU workgroups, each of
+// which computes the block's scores and weights in full (the same bits in
+// every one of them) but only its own tiles of P.V, so that each compute
+// unit's MFMA chain is QK plus TU / TD of the P.V work when the blocks alone
+// would leave most units idle.  They write disjoint columns of O; the first
+// of them writes the LSE.
+template <int D, bool CAUSAL, int TU>
 __global__ __launch_bounds__(kTinyThreads) void fwd_f32_tiny_kernel(FwdArgs a, int n_qt, int total) {
   constexpr int DQ = D / 4;    // floats per lane of a K or Q row, and output columns per lane
   constexpr int TD = D / 16;   // output tiles of 16 columns
+  constexpr int CG = TD / TU;  // workgroups per 16-row block
+  static_assert(TU >= 1 && TD % TU == 0, "output tiles per workgroup");
   constexpr int NWV = kTinyThreads / 64;
   __shared__ __attribute__((aligned(16))) float lds[NWV * kTinyRows * D + 2 * NWV * kTinyRows];
 
@@ -384,9 +393,13 @@ __global__ __launch_bounds__(kTinyThreads) void fwd_f32_tiny_kernel(FwdArgs a, i
   const int j = lane & 15, g = lane >> 4;
   const int NQ = a.nq, NK = a.nk;
 
+  // logical index -> (16-row block, column group); the column groups of a
+  // block are consecutive, so they run on one die and share its L2
   const int L = xcd_remap(blockIdx.x, total);
+  const int cgi = CG == 1 ? 0 : L % CG;
+  const int u0 = cgi * TU;  // first output tile of this workgroup
   int prob, qt;
-  tile_of<CAUSAL>(L, total, n_qt, prob, qt);
+  tile_of<CAUSAL>(CG == 1 ? L : L / CG, total / CG, n_qt, prob, qt);
   const int q0 = qt * kTinyRows;
   const int off = a.causal_off;
 
@@ -438,13 +451,23 @@ __global__ __launch_bounds__(kTinyThreads) void fwd_f32_tiny_kernel(FwdArgs a, i
   // after it, are in flight
   auto wait_buf = [&](int buf) { tiny_vm_wait<(NB - 1) * kLoadsPerBuf, KL, VL>(kq[buf], vq[buf]); };
   auto kf = [&](int buf, int m) { return __uint_as_float(kq[buf][m >> 2][m & 3]); };
-  auto vf = [&](int buf, int r, int u) { return __uint_as_float(vq[buf][r][u >> 2][u & 3]); };
+  // value of this workgroup's output tile u0 + uu from the V row loaded for
+  // key 4g + r (the loads bring every tile's column; u0 is uniform)
+  auto vf = [&](int buf, int r, int uu) {
+    float x = __uint_as_float(vq[buf][r][uu >> 2][uu & 3]);
+#pragma unroll
+    for (int c = 1; c < CG; ++c) {
+      const int u = c * TU + uu;
+      x = cgi == c ? __uint_as_float(vq[buf][r][u >> 2][u & 3]) : x;
+    }
+    return x;
+  };
 
   const float c = a.scale_log2;
   float m_run = kNegInf, l_run = 0.f;
-  f32x4 oacc[TD];
+  f32x4 oacc[TU];
 #pragma unroll
-  for (int t = 0; t < TD; ++t) oacc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TU; ++t) oacc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   const int my_q = q0 + j;
   // one tile of this wave from buffer buf (a constant at each call site, so
@@ -473,7 +496,7 @@ __global__ __launch_bounds__(kTinyThreads) void fwd_f32_tiny_kernel(FwdArgs a, i
       const float alpha = grow ? fast_exp2((m_run - mx) * c) : 1.f;
       l_run *= alpha;
 #pragma unroll
-      for (int u = 0; u < TD; ++u) oacc[u] *= alpha;
+      for (int u = 0; u < TU; ++u) oacc[u] *= alpha;
       m_run = grow ? mx : m_run;
     }
     const float nmc = m_run == kNegInf ? 0.f : -m_run * c;
@@ -486,7 +509,7 @@ __global__ __launch_bounds__(kTinyThreads) void fwd_f32_tiny_kernel(FwdArgs a, i
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int u = 0; u < TD; ++u) oacc[u] = mfma16(vf(buf, r, u), p[r], oacc[u]);
+      for (int u = 0; u < TU; ++u) oacc[u] = mfma16(vf(buf, r, u), p[r], oacc[u]);
   };
 #pragma unroll
   for (int b = 0; b < NB; ++b) load(b, wave + b * NWV);
@@ -516,20 +539,55 @@ __global__ __launch_bounds__(kTinyThreads) void fwd_f32_tiny_kernel(FwdArgs a, i
   l_w = half_swap_sum(l_w);
   float* om = lds;                                // [wave][row][D]
   float* st = lds + NWV * kTinyRows * D;          // [wave][row]: m, then l
-  // output column of oacc[u][r]: g DQ + TD r + u
+  // output column of oacc[u][r]: g DQ + TD r + u0 + u
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < 4; ++r) {
+    float* dst = om + (wave * kTinyRows + j) * D + g * DQ + TD * r + u0;
+    if constexpr (TU % 4 == 0) {
 #pragma unroll
-    for (int u0 = 0; u0 < TD; u0 += 4) {
-      const f32x4 w = {oacc[u0][r], oacc[u0 + 1][r], oacc[u0 + 2][r], oacc[u0 + 3][r]};
-      *(f32x4*)(om + (wave * kTinyRows + j) * D + g * DQ + TD * r + u0) = w;
+      for (int u = 0; u < TU; u += 4) {
+        const f32x4 w = {oacc[u][r], oacc[u + 1][r], oacc[u + 2][r], oacc[u + 3][r]};
+        *(f32x4*)(dst + u) = w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < TU; ++u) dst[u] = oacc[u][r];
     }
+  }
   if (g == 0) {
     st[wave * kTinyRows + j] = m_run;
     st[NWV * kTinyRows + wave * kTinyRows + j] = l_w;
   }
   __syncthreads();
 
+  if constexpr (CG > 1) {
+    // thread -> (row, one of this workgroup's 16 TU columns): the sum below,
+    // column by column
+    constexpr int kCols = 16 * TU;
+    for (int u = tid; u < kTinyRows * kCols; u += kTinyThreads) {
+      const int row = u / kCols, lc = u % kCols;
+      const int col = (lc / (4 * TU)) * DQ + TD * ((lc / TU) % 4) + u0 + lc % TU;
+      float m = kNegInf;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) m = fmaxf(m, st[w * kTinyRows + row]);
+      float ltot = 0.f, o = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) {
+        const float mw = st[w * kTinyRows + row];
+        const float wt = mw == kNegInf ? 0.f : fast_exp2((mw - m) * c);
+        ltot += wt * st[NWV * kTinyRows + w * kTinyRows + row];
+        o += wt * om[(w * kTinyRows + row) * D + col];
+      }
+      const int q = q0 + row;
+      if (q < NQ) {
+        const float inv = ltot > 0.f ? __builtin_amdgcn_rcpf(ltot) : 0.f;
+        ((float*)a.o)[((int64_t)prob * NQ + q) * D + col] = o * inv;
+        if (cgi == 0 && lc == 0 && a.lse)
+          a.lse[(int64_t)prob * NQ + q] = ltot > 0.f ? (m * c + fast_log2(ltot)) * kLn2 : kNegInf;
+      }
+    }
+    return;
+  }
   // thread -> (row, 4-column group)
   constexpr int kGroups = D / 4;
   for (int u = tid; u < kTinyRows * kGroups; u += kTinyThreads) {
@@ -556,14 +614,26 @@ __global__ __launch_bounds__(kTinyThreads) void fwd_f32_tiny_kernel(FwdArgs a, i
   }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_tiny(const FwdArgs& a, hipStream_t s) {
+// Column groups of the small-problem kernel: when its 16-row blocks number
+// at most a quarter of kTinyFill, each block's output tiles are shared out
+// among four workgroups.
+constexpr int kTinyFill = 256;
+
+template <int D, bool CAUSAL, int TU>
+hipError_t launch_tiny_tu(const FwdArgs& a, hipStream_t s) {
   int n_qt = (a.nq + kTinyRows - 1) / kTinyRows;
-  int total = (int)((int64_t)n_qt * a.problems);
+  int total = (int)((int64_t)n_qt * a.problems * (D / 16 / TU));
   FwdArgs args = a;
   void* params[] = {&args, &n_qt, &total};
-  return hipLaunchKernel((const void*)&fwd_f32_tiny_kernel<D, CAUSAL>, dim3(total),
+  return hipLaunchKernel((const void*)&fwd_f32_tiny_kernel<D, CAUSAL, TU>, dim3(total),
                          dim3(kTinyThreads), params, 0, s);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_tiny(const FwdArgs& a, hipStream_t s) {
+  const int64_t blocks = (a.nq + kTinyRows - 1) / kTinyRows * (int64_t)a.problems;
+  if (blocks * 4 <= kTinyFill) return launch_tiny_tu<D, CAUSAL, D / 64>(a, s);
+  return launch_tiny_tu<D, CAUSAL, D / 16>(a, s);
 }
 
 template <int D>
