@@ -19,8 +19,11 @@ visible pair).  Prints ONE JSON line with:
                         when causal) from a wall clock around K steps,
                         bracketed by stream synchronisation;
   roofline              the kernel's own average duration from HIP events
-                        recorded on the launch stream around every timed
-                        launch, against the MI355X dense MFMA peak of the
+                        recorded on the launch stream around each of K more
+                        launches, queued behind a delay kernel of the probe
+                        library (libfa_probe.so) so that they run back to back
+                        and the host's launch gap stays out of the events,
+                        against the MI355X dense MFMA peak of the
                         input dtype, or against HBM bandwidth (8 TB/s)
                         when the workload's FLOP per algorithmic byte is
                         below the ridge point; ``hbm_gbs`` is the algorithmic
@@ -355,20 +358,38 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Kernel duration: events on the launch stream around every launch.
+    # Whole-job throughput: K steps between two synchronisations.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    enqueue_s = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # Kernel duration: HIP events on the launch stream around each of K more
+    # launches.  They are queued behind a delay kernel that holds the stream
+    # for longer than the host takes to enqueue them, so they run back to
+    # back and each event pair brackets its launch rather than the host's
+    # launch gap, which is longer than the shortest calls.  W untimed
+    # launches between the delay and the timed ones bring the clock back up
+    # after the near-idle delay.
+    from exact_attention_13_amd import probe
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    per_launch_s = enqueue_s / max(1, args.steps)
+    probe.delay(min(1000000, int(3e6 * per_launch_s * (args.steps + args.warmup)) + 2000), stream)
+    for _ in range(args.warmup):
+        step()
     for i in range(args.steps):
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     kernel_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     avg_kernel_ms = sum(kernel_ms) / len(kernel_ms)
-    ms_per_step = wall * 1e3 / args.steps
 
     # Cold caches: reading a 512 MiB buffer between calls evicts the L2s and
     # the MALL (a read leaves no dirty lines to write back during the next
@@ -394,7 +415,6 @@ def main():
     # after the attention calls (same warm chip), for the FLOP-bound lines.
     mfma_loop = None
     if not args.no_mfma_loop:
-        from exact_attention_13_amd import probe
         mfma_loop = probe.mfma_tflops(w.dtype, stream=stream)
 
     flops = w.flops * (2.5 if args.which == "bwd" else 1.0)

@@ -6,7 +6,8 @@
 // (the published peaks assume 2.4 GHz).  The loop is what the attention
 // kernels' MFMAs would achieve with no softmax, no memory traffic and no
 // waits: every wave issues independent 32x32 MFMAs back to back, two waves
-// per SIMD, every SIMD of the chip busy.
+// per SIMD, every SIMD of the chip busy.  It also holds a delay kernel, which
+// the benchmark queues its timed launches behind.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,6 +53,13 @@ __global__ __launch_bounds__(kThreads) void mfma_loop(float* out, int iters) {
 }
 
 constexpr double kFlopsPerMfma[3] = {32.0 * 32 * 2 * 2, 32.0 * 32 * 16 * 2, 32.0 * 32 * 16 * 2};
+
+// One wave that waits until `ticks` of the constant-rate real-time counter
+// have passed since it started, then exits.
+__global__ __launch_bounds__(64) void delay_kernel(uint64_t ticks) {
+  const uint64_t t0 = wall_clock64();
+  while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+}
 
 }  // namespace
 
@@ -103,6 +111,24 @@ int fa_probe_mfma_tflops(int dtype, int iters, int launches, void* stream, doubl
   if (e != hipSuccess) return (int)e;
   *tflops = best;
   return 0;
+}
+
+// Occupies `stream` (a hipStream_t; null = the default stream) for about
+// `microseconds` (0 .. 1000000) with a one-wave kernel that waits on the
+// GPU's real-time counter, so that launches the host makes next queue up
+// behind it and then run back to back.  Asynchronous.  Returns 0, or a
+// hipError_t code (hipErrorInvalidValue for an out-of-range time).
+int fa_probe_delay(int microseconds, void* stream) {
+  if (microseconds < 0 || microseconds > 1000000) return (int)hipErrorInvalidValue;
+  int dev = 0, khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return (int)e;
+  if (khz <= 0) return (int)hipErrorInvalidValue;
+  uint64_t ticks = (uint64_t)microseconds * (uint64_t)khz / 1000u;
+  void* params[] = {&ticks};
+  return (int)hipLaunchKernel((const void*)&delay_kernel, dim3(1), dim3(64), params, 0,
+                              (hipStream_t)stream);
 }
 
 }  // extern "C"

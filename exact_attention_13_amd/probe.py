@@ -4,7 +4,8 @@ The benchmark reports an attention kernel's FLOP rate against MI355X's
 published dense peak and, beside it, against this measured rate of a plain
 MFMA loop (independent 32x32 MFMAs back to back on every SIMD, two waves per
 SIMD), which runs at the clock the chip holds under MFMA load.  The probe is
-not part of libfa and computes nothing of the attention path.
+not part of libfa and computes nothing of the attention path.  Its delay
+kernel lets the benchmark queue timed launches so that they run back to back.
 """
 from __future__ import annotations
 
@@ -25,6 +26,8 @@ def load() -> ctypes.CDLL:
         lib.fa_probe_mfma_tflops.restype = ctypes.c_int
         lib.fa_probe_mfma_tflops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                              ctypes.POINTER(ctypes.c_double)]
+        lib.fa_probe_delay.restype = ctypes.c_int
+        lib.fa_probe_delay.argtypes = [ctypes.c_int, ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -39,3 +42,13 @@ def mfma_tflops(dtype: str, iters: int = 4000, launches: int = 5, stream=None) -
     if st != 0:
         raise RuntimeError(f"fa_probe_mfma_tflops failed with HIP error {st}")
     return float(out.value)
+
+
+def delay(microseconds: int, stream=None) -> None:
+    """Occupy `stream` (a torch.cuda.Stream or None) for about `microseconds`
+    (0 .. 1e6) with a kernel that waits on the GPU's real-time counter, so that
+    the launches made next queue up behind it.  Asynchronous."""
+    handle = stream.cuda_stream if stream is not None else None
+    st = load().fa_probe_delay(int(microseconds), handle)
+    if st != 0:
+        raise RuntimeError(f"fa_probe_delay failed with HIP error {st}")
