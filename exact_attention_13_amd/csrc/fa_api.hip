@@ -288,6 +288,14 @@ extern "C" int64_t fa_fwd_ex_default_splits(int64_t B, int64_t H, int64_t H_kv, 
   if (B <= 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || N_q <= 0 || N_kv <= 0) return 1;
   if ((d != 64 && d != 128) || !valid_dtype(dtype)) return 1;
   const Plan p = make_plan(B, H, H_kv, N_q, d, causal, dtype);
+  // fp32 problems that the unsplit launch hands to the small-problem kernel
+  // stay unsplit while each 16-row block's key chain is short: measured on
+  // MI355X, up to N_kv d = 64 Ki the one kernel beats the split call and its
+  // combine (one 512-row head, d = 64: 11.0 against 15.1 us with 8 ranges;
+  // 2 x 4 heads of 256 rows: 9.4 against 15.4), beyond it splitting gains
+  // (2048 keys at d = 64: 22.8 against 25.1 us; d = 128: 30.4 against 47.5).
+  if (dtype == FA_F32 && fa_impl::f32_small_kernel(p.nq, p.problems) && N_kv * d <= 65536)
+    return 1;
   // Aim for two workgroups per compute unit (256 CUs).  More ranges do not
   // stream K/V faster (a decoding step already reads at the rate a plain
   // streaming read reaches) but cost partial results and a longer combine.

@@ -185,5 +185,8 @@ int64_t combine_grid_blocks(int64_t rows, int d);
 // sizes grids and split counts with it).
 int h16_rows_per_block(int d, bool causal, int64_t nq);
 int f32_rows_per_block();
+// Whether an unsplit fp32 launch over `problems` problems of `nq` query rows
+// takes the small-problem kernel (16-row blocks spread over the chip).
+bool f32_small_kernel(int64_t nq, int64_t problems);
 
 }  // namespace fa_impl

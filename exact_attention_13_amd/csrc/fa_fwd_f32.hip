@@ -638,7 +638,7 @@ hipError_t launch_tiny(const FwdArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t launch_d(bool causal, bool split, const FwdArgs& a, hipStream_t s) {
-  if (!split && (int64_t)((a.nq + kBM - 1) / kBM) * a.problems < kShortGrid)
+  if (!split && f32_small_kernel(a.nq, a.problems))
     return causal ? launch_tiny<D, true>(a, s) : launch_tiny<D, false>(a, s);
   if (causal) return split ? launch<D, true, true>(a, s) : launch<D, true, false>(a, s);
   return split ? launch<D, false, true>(a, s) : launch<D, false, false>(a, s);
@@ -651,5 +651,9 @@ hipError_t launch_fwd_f32(int d, bool causal, bool split, const FwdArgs& a, hipS
 }
 
 int f32_rows_per_block() { return kBM; }
+
+bool f32_small_kernel(int64_t nq, int64_t problems) {
+  return (nq + kBM - 1) / kBM * problems < kShortGrid;
+}
 
 }  // namespace fa_impl

@@ -91,7 +91,7 @@ class Workload:
 # The five workloads (plus the ragged variant of the second) that the parity
 # tests and the benchmark use, and the shapes of the split-KV / grouped-head
 # entry point:
-#   C1s  the one-head fp32 workload run with its keys split (short grid);
+#   C1s  the one-head fp32 workload run with its keys split into 8 ranges;
 #   D1   one decoding step: one query row per head against 16384 cached keys,
 #        32 query heads sharing 8 K/V heads, head size 128, bf16;
 #   G1   the headline bf16 shape with 16 query heads on 4 K/V heads;
@@ -103,7 +103,7 @@ WORKLOADS = {
     "C3": Workload("C3", "bf16", 8, 16, 4096, 128, True, 2),
     "C4": Workload("C4", "bf16", 1, 16, 16384, 64, False, 3),
     "C5": Workload("C5", "f16", 2, 32, 8191, 128, True, 4, "large_logit"),
-    "C1s": Workload("C1s", "f32", 1, 1, 512, 64, False, 0, splits=0),
+    "C1s": Workload("C1s", "f32", 1, 1, 512, 64, False, 0, splits=8),
     "D1": Workload("D1", "bf16", 8, 32, 1, 128, False, 5, Hkv=8, Nkv=16384, splits=0),
     "G1": Workload("G1", "bf16", 1, 16, 16384, 64, False, 6, Hkv=4),
     "G2": Workload("G2", "bf16", 8, 16, 4096, 128, True, 7, Hkv=2),

@@ -215,8 +215,16 @@ def test_default_splits():
     bf16, f32 = libfa.FA_BF16, libfa.FA_F32
     # a full grid is not split (the headline bf16 shape)
     assert libfa.default_splits(1, 16, 16, 16384, 16384, 64, False, bf16) == 1
-    # one fp32 head of 512 rows: four workgroups, split to one 64-key tile each
-    assert libfa.default_splits(1, 1, 1, 512, 512, 64, False, f32) == 8
+    # one fp32 head of 512 rows: the small-problem kernel, unsplit, is faster
+    assert libfa.default_splits(1, 1, 1, 512, 512, 64, False, f32) == 1
+    assert libfa.default_splits(1, 1, 1, 512, 512, 128, True, f32) == 1
+    assert libfa.default_splits(2, 4, 4, 256, 256, 64, False, f32) == 1
+    # its longer key chains are split: 2048 keys at d = 64, 1024 at d = 128
+    assert libfa.default_splits(1, 1, 1, 512, 2048, 64, False, f32) == 32
+    assert libfa.default_splits(4, 1, 1, 256, 1024, 128, False, f32) == 16
+    assert libfa.default_splits(1, 1, 1, 1, 16384, 64, False, f32) >= 64
+    # a full fp32 grid is not split
+    assert libfa.default_splits(4, 8, 8, 2048, 2048, 64, False, f32) == 1
     # decoding against a long cache is split into many ranges
     s = libfa.default_splits(8, 32, 8, 1, 16384, 128, False, bf16)
     assert 8 <= s <= 256
