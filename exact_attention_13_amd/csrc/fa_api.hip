@@ -296,15 +296,24 @@ extern "C" int64_t fa_fwd_ex_default_splits(int64_t B, int64_t H, int64_t H_kv, 
   // (2048 keys at d = 64: 22.8 against 25.1 us; d = 128: 30.4 against 47.5).
   if (dtype == FA_F32 && fa_impl::f32_small_kernel(p.nq, p.problems) && N_kv * d <= 65536)
     return 1;
-  // Aim for two workgroups per compute unit (256 CUs).  More ranges do not
-  // stream K/V faster (a decoding step already reads at the rate a plain
-  // streaming read reaches) but cost partial results and a longer combine.
-  // Each range keeps enough keys that its fixed costs (Q load, partial
-  // write) stay small.
-  const int64_t target = 512;
+  // Aim for about two workgroups per compute unit (256 CUs) where several
+  // fit on one (fp32, and the one-wave workgroups of short bf16/fp16 rows,
+  // which stream K/V), one per compute unit for the multi-wave bf16/fp16
+  // tiles (eight-wave d = 64 tiles fill a compute unit; the split call's
+  // partial results and combine then cost more than the rest of the chip
+  // gains).  More ranges do not stream K/V faster (a decoding step already
+  // reads at the rate a plain streaming read reaches) but cost partial
+  // results and a longer combine.  Each range keeps enough keys that its
+  // fixed costs (Q load, partial write) stay small; short key sequences
+  // of grids of a few row blocks take shorter ranges.  (Measured on MI355X over 1-32 heads, N_q 1-2048,
+  // N_kv 512-65536: one 512-row bf16 head at d = 64 21.2 -> 18.3 us,
+  // 16 heads of 2048 rows 59.7 -> 45.2 us, d = 128 with 128 row blocks
+  // 34.5 -> 28.6 us unsplit; decoding shapes unchanged.)
+  const bool multi_wave = dtype != FA_F32 && p.rpb > 32;
+  const int64_t target = multi_wave ? 256 : 512;
   if (p.blocks >= target / 2) return 1;
   int64_t want = (target + p.blocks - 1) / p.blocks;
-  const int64_t min_keys = dtype == FA_F32 ? 64 : 256;
+  const int64_t min_keys = dtype == FA_F32 ? 64 : (N_kv <= 1024 && p.blocks <= 8 ? 128 : 256);
   int64_t most = N_kv / min_keys;
   if (most < 1) most = 1;
   if (want > most) want = most;

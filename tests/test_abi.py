@@ -229,6 +229,15 @@ def test_default_splits():
     s = libfa.default_splits(8, 32, 8, 1, 16384, 128, False, bf16)
     assert 8 <= s <= 256
     assert libfa.default_splits(1, 4, 3, 1, 100, 64, False, bf16) == 1  # invalid grouping
+    # eight-wave d = 64 tiles: one workgroup per compute unit is the target
+    assert libfa.default_splits(1, 16, 16, 2048, 2048, 64, False, bf16) == 4
+    # d = 128 grids of 128 row blocks run unsplit
+    assert libfa.default_splits(2, 8, 8, 1024, 1024, 128, False, bf16) == 1
+    # a few row blocks over a short key sequence: 128-key ranges
+    assert libfa.default_splits(1, 1, 1, 512, 512, 64, False, bf16) == 4
+    assert libfa.default_splits(4, 1, 1, 256, 1024, 128, False, bf16) == 8
+    # ... but not once the grid has more blocks
+    assert libfa.default_splits(2, 8, 8, 1024, 1024, 64, False, bf16) == 4
 
 
 @pytest.mark.parametrize("kw,status", [
