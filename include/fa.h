@@ -184,9 +184,10 @@ int64_t fa_fwd_ex_workspace_bytes(int64_t B, int64_t H, int64_t N_q, int64_t N_k
 /* A split count for fa_fwd_ex that gives MI355X's 256 compute units enough
  * workgroups when the unsplit grid is short (1 when it is already full or
  * the arguments are invalid): about one multi-wave bf16/fp16 workgroup or
- * two fp32 or one-wave workgroups per compute unit.  Small fp32 problems with N_kv * d <= 65536
- * are not split: their unsplit kernel already spreads 16-row blocks over the
- * chip and is faster than a split call with its combine step. */
+ * two fp32 or one-wave workgroups per compute unit.  Small fp32 problems
+ * with N_kv * d <= 65536 are not split: their unsplit kernel already spreads
+ * 16-row blocks over the chip and is faster than a split call with its
+ * combine step. */
 int64_t fa_fwd_ex_default_splits(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_kv,
                                  int64_t d, int causal, fa_dtype dtype);
 
