@@ -61,7 +61,7 @@ Plan make_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t d, int c
   p.grp = packed ? 1 : g;
   p.rows = B * H * N_q;
   p.rpb = dtype == FA_F32 ? fa_impl::f32_rows_per_block()
-                          : fa_impl::h16_rows_per_block((int)d, p.causal, p.nq);
+                          : fa_impl::h16_rows_per_block((int)d, p.causal, p.nq, p.problems);
   p.blocks = p.problems * ((p.nq + p.rpb - 1) / p.rpb);
   return p;
 }
@@ -305,7 +305,7 @@ extern "C" int64_t fa_fwd_ex_default_splits(int64_t B, int64_t H, int64_t H_kv, 
   // reads at the rate a plain streaming read reaches) but cost partial
   // results and a longer combine.  Each range keeps enough keys that its
   // fixed costs (Q load, partial write) stay small; short key sequences
-  // of grids of a few row blocks take shorter ranges.  (Measured on MI355X over 1-32 heads, N_q 1-2048,
+  // of problems of at most 2048 query rows in all take shorter ranges.  (Measured on MI355X over 1-32 heads, N_q 1-2048,
   // N_kv 512-65536: one 512-row bf16 head at d = 64 21.2 -> 18.3 us,
   // 16 heads of 2048 rows 59.7 -> 45.2 us, d = 128 with 128 row blocks
   // 34.5 -> 28.6 us unsplit; decoding shapes unchanged.)
@@ -313,7 +313,7 @@ extern "C" int64_t fa_fwd_ex_default_splits(int64_t B, int64_t H, int64_t H_kv, 
   const int64_t target = multi_wave ? 256 : 512;
   if (p.blocks >= target / 2) return 1;
   int64_t want = (target + p.blocks - 1) / p.blocks;
-  const int64_t min_keys = dtype == FA_F32 ? 64 : (N_kv <= 1024 && p.blocks <= 8 ? 128 : 256);
+  const int64_t min_keys = dtype == FA_F32 ? 64 : (N_kv <= 1024 && p.rows <= 2048 ? 128 : 256);
   int64_t most = N_kv / min_keys;
   if (most < 1) most = 1;
   if (want > most) want = most;

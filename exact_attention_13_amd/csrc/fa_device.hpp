@@ -183,7 +183,7 @@ int64_t combine_grid_blocks(int64_t rows, int d);
 
 // Query rows per workgroup of the instance a launch would use (the host
 // sizes grids and split counts with it).
-int h16_rows_per_block(int d, bool causal, int64_t nq);
+int h16_rows_per_block(int d, bool causal, int64_t nq, int64_t problems);
 int f32_rows_per_block();
 // Whether an unsplit fp32 launch over `problems` problems of `nq` query rows
 // takes the small-problem kernel (16-row blocks spread over the chip).

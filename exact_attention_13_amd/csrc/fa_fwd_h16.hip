@@ -80,6 +80,9 @@ constexpr int kStreamAux = 2;  // buffer-load cache policy bit: nt
 template <int D_, int QB_, int BN_, int NW_>
 struct Cfg {
   static constexpr int D = D_, QB = QB_, BN = BN_, NW = NW_;
+  // K/V loads carry the non-temporal hint: one-wave workgroups of a decoding
+  // step, which read every K/V byte once
+  static constexpr bool kStream = NW == 1;
   static constexpr int kThreads = NW * 64;
   static constexpr int kQPerWave = 32 * QB;
   static constexpr int kBM = NW * kQPerWave;        // queries per workgroup
@@ -104,6 +107,13 @@ struct Cfg {
   static constexpr int kKPer = (kKUnits + kThreads - 1) / kThreads;
   static constexpr int kVPer = (kVUnits + kThreads - 1) / kThreads;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+};
+
+// The one-wave 32-row tile for short d = 64 grids, where each row block of a
+// problem reads its K/V again and the default cache policy keeps them.
+template <int D_, int BN_>
+struct CfgShort : Cfg<D_, 1, BN_, 1> {
+  static constexpr bool kStream = false;
 };
 
 template <bool BF16, bool CAUSAL, bool SPLIT, class C>
@@ -197,7 +207,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
       const int u = tid + i * C::kThreads;
       if (C::kKUnits % C::kThreads == 0 || u < C::kKUnits) {
         const int row = u / (D / 8), cc = u % (D / 8);
-        kst[i] = buf_load16<C::NW == 1 ? kStreamAux : 0>(kr, ((k0 + row) * D + cc * 8) * 2);
+        kst[i] = buf_load16<C::kStream ? kStreamAux : 0>(kr, ((k0 + row) * D + cc * 8) * 2);
       }
     }
 #pragma unroll
@@ -207,7 +217,7 @@ __global__ __launch_bounds__(C::kThreads) void fwd_h16_kernel(FwdArgs a, int n_q
         const int pr = u % (BN / 2), cc = u / (BN / 2);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          vst[i][h] = buf_load16<C::NW == 1 ? kStreamAux : 0>(vr, ((k0 + 2 * pr + h) * D + cc * 8) * 2);
+          vst[i][h] = buf_load16<C::kStream ? kStreamAux : 0>(vr, ((k0 + 2 * pr + h) * D + cc * 8) * 2);
       }
     }
   };
@@ -611,7 +621,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
 // Overridable at build time (FA_H16_D64_CFG / FA_H16_D128_CFG = QB, BN, NW).
 // Problems with at most 32 query rows (decoding, grouped heads packed into
 // rows) take a one-wave workgroup instead, so that the grid is made of key
-// ranges rather than of idle query rows.
+// ranges rather than of idle query rows; so do d = 64 grids too short to
+// fill the chip with the eight-wave tiles (see pick below).
 #ifndef FA_H16_D64_CFG
 #define FA_H16_D64_CFG 2, 128, 8
 #endif
@@ -622,15 +633,44 @@ using CfgD64 = Cfg<64, FA_H16_D64_CFG>;
 using CfgD128 = Cfg<128, FA_H16_D128_CFG>;
 using CfgD64Small = Cfg<64, 1, 64, 1>;
 using CfgD128Small = Cfg<128, 1, 32, 1>;
+// The same one-wave 32-row workgroups for short grids, where the K/V of a
+// problem are read by each of its row blocks and stay cached.
+using CfgD64Short = CfgShort<64, 64>;
 
-bool use_small(bool causal, int64_t nq) { return !causal && nq <= 32; }
+// d = 64 grids of fewer than kShortBlocks eight-wave workgroups leave most
+// of the 256 compute units idle: they take 32-row one-wave workgroups
+// instead, 16x as many, with half of a wave's rows each, so each wave's
+// chain over the keys is half as long (measured on MI355X: one 512-row
+// head 25.0 -> 12.6 us, 8 heads of 2048 rows 67.6 -> 39.9 us, 2 causal
+// heads of 8192 rows 231 -> 141 us).  d = 128 keeps its tile there: its
+// waves already hold 32 rows each, so one-wave workgroups would only spread
+// the same waves thinner without its direct-to-LDS staging (one causal
+// 2048-row head: 48.8 -> 63.0 us).
+constexpr int64_t kShortBlocks = 64;
+
+enum class Pick { kBig, kSmall, kShort };
+
+Pick pick(int d, bool causal, int64_t nq, int64_t problems) {
+  if (!causal && nq <= 32) return Pick::kSmall;
+  if (d == 64 && (nq + CfgD64::kBM - 1) / CfgD64::kBM * problems < kShortBlocks) return Pick::kShort;
+  return Pick::kBig;
+}
 
 template <bool BF16, int D>
 hipError_t launch_d(bool causal, bool split, const FwdArgs& a, hipStream_t s) {
   using Big = typename std::conditional<D == 64, CfgD64, CfgD128>::type;
   using Small = typename std::conditional<D == 64, CfgD64Small, CfgD128Small>::type;
-  if (use_small(causal, a.nq))
+  const Pick k = pick(D, causal, a.nq, a.problems);
+  if (k == Pick::kSmall)
     return split ? launch<BF16, false, true, Small>(a, s) : launch<BF16, false, false, Small>(a, s);
+  if constexpr (D == 64) {
+    using Short = CfgD64Short;
+    if (k == Pick::kShort) {
+      if (causal)
+        return split ? launch<BF16, true, true, Short>(a, s) : launch<BF16, true, false, Short>(a, s);
+      return split ? launch<BF16, false, true, Short>(a, s) : launch<BF16, false, false, Short>(a, s);
+    }
+  }
   if (causal)
     return split ? launch<BF16, true, true, Big>(a, s) : launch<BF16, true, false, Big>(a, s);
   return split ? launch<BF16, false, true, Big>(a, s) : launch<BF16, false, false, Big>(a, s);
@@ -647,8 +687,8 @@ hipError_t launch_fwd_h16(bool bf16, int d, bool causal, bool split, const FwdAr
                  : launch_d<false, 128>(causal, split, a, s);
 }
 
-int h16_rows_per_block(int d, bool causal, int64_t nq) {
-  if (use_small(causal, nq)) return 32;
+int h16_rows_per_block(int d, bool causal, int64_t nq, int64_t problems) {
+  if (pick(d, causal, nq, problems) != Pick::kBig) return 32;
   return d == 64 ? CfgD64::kBM : CfgD128::kBM;
 }
 

@@ -233,11 +233,13 @@ def test_default_splits():
     assert libfa.default_splits(1, 16, 16, 2048, 2048, 64, False, bf16) == 4
     # d = 128 grids of 128 row blocks run unsplit
     assert libfa.default_splits(2, 8, 8, 1024, 1024, 128, False, bf16) == 1
-    # a few row blocks over a short key sequence: 128-key ranges
+    # a few query rows over a short key sequence: 128-key ranges
     assert libfa.default_splits(1, 1, 1, 512, 512, 64, False, bf16) == 4
     assert libfa.default_splits(4, 1, 1, 256, 1024, 128, False, bf16) == 8
-    # ... but not once the grid has more blocks
-    assert libfa.default_splits(2, 8, 8, 1024, 1024, 64, False, bf16) == 4
+    # ... but not with more rows; short d = 64 grids of 32-row workgroups
+    # that fill the chip are not split
+    assert libfa.default_splits(1, 8, 8, 512, 512, 64, False, bf16) == 2
+    assert libfa.default_splits(2, 8, 8, 1024, 1024, 64, False, bf16) == 1
 
 
 @pytest.mark.parametrize("kw,status", [
