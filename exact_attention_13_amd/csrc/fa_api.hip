@@ -294,7 +294,8 @@ extern "C" int64_t fa_fwd_ex_default_splits(int64_t B, int64_t H, int64_t H_kv, 
   // combine (one 512-row head, d = 64: 11.0 against 15.1 us with 8 ranges;
   // 2 x 4 heads of 256 rows: 9.4 against 15.4), beyond it splitting gains
   // (2048 keys at d = 64: 22.8 against 25.1 us; d = 128: 30.4 against 47.5).
-  if (dtype == FA_F32 && fa_impl::f32_small_kernel(p.nq, p.problems) && N_kv * d <= 65536)
+  if (dtype == FA_F32 && fa_impl::f32_small_kernel(p.nq, p.problems, p.causal, (int)d) &&
+      N_kv * d <= 65536)
     return 1;
   // Aim for about two workgroups per compute unit (256 CUs) where several
   // fit on one (fp32, and the one-wave workgroups of short bf16/fp16 rows,

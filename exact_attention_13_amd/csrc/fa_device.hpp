@@ -187,6 +187,6 @@ int h16_rows_per_block(int d, bool causal, int64_t nq, int64_t problems);
 int f32_rows_per_block();
 // Whether an unsplit fp32 launch over `problems` problems of `nq` query rows
 // takes the small-problem kernel (16-row blocks spread over the chip).
-bool f32_small_kernel(int64_t nq, int64_t problems);
+bool f32_small_kernel(int64_t nq, int64_t problems, bool causal, int d);
 
 }  // namespace fa_impl

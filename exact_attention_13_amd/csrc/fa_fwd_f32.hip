@@ -259,12 +259,24 @@ hipError_t launch(const FwdArgs& a, hipStream_t s) {
                          dim3(kThreads), params, 0, s);
 }
 
-// Grids of fewer than kShortGrid workgroups of 128 rows take the small-problem
-// kernel below.
+// Grids of at most kShortGrid workgroups of 128 rows take the small-problem
+// kernel below; causal grids of at most kShortGridCausal, whose 128-row
+// workgroups also differ in length, so that a grid of one or two per compute
+// unit ends with a long tail.  Measured on MI355X (median of 30 queued
+// calls): 32 heads of 512 rows (128 workgroups) 44.0 -> 36.4 us, causal
+// 43.4 -> 30.8; 24 causal heads of 1024 rows (192) 80.8 -> 59.6 us; while
+// non-causal grids from about 192 workgroups and causal ones of 256 run
+// faster on the 128-row kernel (48 heads of 512 rows: 45.8 against 51.9 us;
+// 16 causal heads of 512 rows x 4: 45.7 against 55.6).  Causal d = 64
+// problems of at least 2048 rows gain up to kShortGridLong workgroups (8
+// heads of 4096 rows, 256 workgroups: 298 -> 204 us; 6 of 8192, 384: 808 ->
+// 614 us; one d = 128 case of 384 lost 5 %, so d = 128 stays out).
 constexpr int kShortGrid = 128;
+constexpr int kShortGridCausal = 255;
+constexpr int kShortGridLong = 511;
 
 // ---------------------------------------------------------------------------
-// Small fp32 problems (fewer than kShortGrid workgroups of 128 rows, e.g. one
+// Small fp32 problems (at most kShortGrid workgroups of 128 rows, e.g. one
 // 512-row head).  There the time is set by the serial MFMA chain of each
 // compute unit, not by the chip's throughput, so the work is cut finer:
 //   * 16 query rows per workgroup on v_mfma_f32_16x16x4_f32 (half the rows
@@ -638,7 +650,7 @@ hipError_t launch_tiny(const FwdArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t launch_d(bool causal, bool split, const FwdArgs& a, hipStream_t s) {
-  if (!split && f32_small_kernel(a.nq, a.problems))
+  if (!split && f32_small_kernel(a.nq, a.problems, causal, D))
     return causal ? launch_tiny<D, true>(a, s) : launch_tiny<D, false>(a, s);
   if (causal) return split ? launch<D, true, true>(a, s) : launch<D, true, false>(a, s);
   return split ? launch<D, false, true>(a, s) : launch<D, false, false>(a, s);
@@ -652,8 +664,10 @@ hipError_t launch_fwd_f32(int d, bool causal, bool split, const FwdArgs& a, hipS
 
 int f32_rows_per_block() { return kBM; }
 
-bool f32_small_kernel(int64_t nq, int64_t problems) {
-  return (nq + kBM - 1) / kBM * problems < kShortGrid;
+bool f32_small_kernel(int64_t nq, int64_t problems, bool causal, int d) {
+  const int64_t blocks = (nq + kBM - 1) / kBM * problems;
+  if (!causal) return blocks <= kShortGrid;
+  return blocks <= (d == 64 && nq >= 2048 ? kShortGridLong : kShortGridCausal);
 }
 
 }  // namespace fa_impl

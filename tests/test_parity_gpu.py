@@ -86,12 +86,15 @@ def test_small_shapes(dtype, d, causal):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_f32_grid_sizes(d, causal):
-    # fp32 problems of fewer than 128 workgroups of 128 rows take the
-    # small-problem kernel (16 rows per workgroup, eight waves splitting the
-    # keys in 16-key tiles); larger ones the 128-row kernel.  Both sides of
-    # the switch, ragged tails, key counts that leave waves without tiles.
+    # fp32 problems of at most 128 workgroups of 128 rows (255 causal) take
+    # the small-problem kernel (16 rows per workgroup, eight waves splitting
+    # the keys in 16-key tiles); larger ones the 128-row kernel.  Both sides
+    # of both switches, ragged tails, key counts that leave waves without
+    # tiles.
     for B, H, N, seed in ((1, 1, 700, 1600), (2, 16, 1000, 1601), (1, 31, 513, 1602),
-                          (1, 3, 100, 1603), (1, 2, 17, 1604)):
+                          (1, 3, 100, 1603), (1, 2, 17, 1604), (1, 128, 100, 1605),
+                          (1, 129, 100, 1606), (5, 51, 70, 1607), (1, 256, 90, 1608),
+                          (1, 2, 2100, 1609), (1, 16, 2048, 1610)):
         w, (q, k, v) = small_case("f32", B, H, N, d, causal, seed=seed)
         _note(f"f32 grid d={d} causal={causal} B={B} H={H} N={N}")
         o, lse = run_gpu(q, k, v, w.scale, causal)
