@@ -637,22 +637,24 @@ using CfgD128Small = Cfg<128, 1, 32, 1>;
 // problem are read by each of its row blocks and stay cached.
 using CfgD64Short = CfgShort<64, 64>;
 
-// d = 64 grids of fewer than kShortBlocks eight-wave workgroups leave most
-// of the 256 compute units idle: they take 32-row one-wave workgroups
-// instead, 16x as many, with half of a wave's rows each, so each wave's
-// chain over the keys is half as long (measured on MI355X: one 512-row
-// head 25.0 -> 12.6 us, 8 heads of 2048 rows 67.6 -> 39.9 us, 2 causal
-// heads of 8192 rows 231 -> 141 us).  d = 128 keeps its tile there: its
+// d = 64 grids of at most kShortBlocks eight-wave workgroups leave most of
+// the 256 compute units idle: they take 32-row one-wave workgroups instead,
+// 16x as many, with half of a wave's rows each, so each wave's chain over
+// the keys is half as long (measured on MI355X: one 512-row head 25.0 ->
+// 12.6 us, 8 heads of 2048 rows 67.6 -> 39.9 us, 2 causal heads of 8192
+// rows 231 -> 141 us, 64 heads of 512 rows 26.1 -> 16.9 us; at 192
+// workgroups the eight-wave tile is ahead: 24 heads of 4096 rows 148 against
+// 251 us).  d = 128 keeps its tile there: its
 // waves already hold 32 rows each, so one-wave workgroups would only spread
 // the same waves thinner without its direct-to-LDS staging (one causal
 // 2048-row head: 48.8 -> 63.0 us).
-constexpr int64_t kShortBlocks = 64;
+constexpr int64_t kShortBlocks = 64;  // at most
 
 enum class Pick { kBig, kSmall, kShort };
 
 Pick pick(int d, bool causal, int64_t nq, int64_t problems) {
   if (!causal && nq <= 32) return Pick::kSmall;
-  if (d == 64 && (nq + CfgD64::kBM - 1) / CfgD64::kBM * problems < kShortBlocks) return Pick::kShort;
+  if (d == 64 && (nq + CfgD64::kBM - 1) / CfgD64::kBM * problems <= kShortBlocks) return Pick::kShort;
   return Pick::kBig;
 }
 

@@ -229,8 +229,10 @@ def test_default_splits():
     s = libfa.default_splits(8, 32, 8, 1, 16384, 128, False, bf16)
     assert 8 <= s <= 256
     assert libfa.default_splits(1, 4, 3, 1, 100, 64, False, bf16) == 1  # invalid grouping
-    # eight-wave d = 64 tiles: one workgroup per compute unit is the target
-    assert libfa.default_splits(1, 16, 16, 2048, 2048, 64, False, bf16) == 4
+    # a short d = 64 grid runs 32-row workgroups that fill the chip unsplit
+    assert libfa.default_splits(1, 16, 16, 2048, 2048, 64, False, bf16) == 1
+    # eight-wave d = 64 tiles (96 of them): one workgroup per compute unit
+    assert libfa.default_splits(1, 24, 24, 2048, 2048, 64, False, bf16) == 3
     # d = 128 grids of 128 row blocks run unsplit
     assert libfa.default_splits(2, 8, 8, 1024, 1024, 128, False, bf16) == 1
     # a few query rows over a short key sequence: 128-key ranges

@@ -105,11 +105,11 @@ def test_f32_grid_sizes(d, causal):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_h16_d64_short_grid_switch(dtype, causal):
-    # d = 64 grids of fewer than 64 eight-wave workgroups of 512 rows take
-    # one-wave 32-row workgroups.  Both sides of the switch (63 and 64
+    # d = 64 grids of at most 64 eight-wave workgroups of 512 rows take
+    # one-wave 32-row workgroups.  Both sides of the switch (64 and 65
     # problems of one block), a multi-block head on the short side, ragged
     # tails, and rows past the last key block of a causal wave.
-    for B, H, N, seed in ((1, 63, 100, 1650), (1, 64, 100, 1651), (3, 21, 97, 1652),
+    for B, H, N, seed in ((1, 64, 100, 1650), (1, 65, 100, 1651), (3, 21, 97, 1652),
                           (2, 4, 1500, 1653), (1, 1, 33, 1654)):
         w, (q, k, v) = small_case(dtype, B, H, N, 64, causal, seed=seed)
         _note(f"h16 short grid {dtype} causal={causal} B={B} H={H} N={N}")
