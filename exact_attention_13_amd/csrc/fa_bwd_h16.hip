@@ -78,6 +78,10 @@ template <int D> constexpr int kDqWaves = 2;
 // instead of three: 1-1.5 % faster backward (C4, G1).
 template <int D> constexpr int kDqBlocks = D == 64 ? 2 : 1;
 template <int D> constexpr int kDqRows = 32 * kBwdWaves * kDqBlocks<D>;
+#ifndef FA_BWD_DQ_SHORT_GRID
+#define FA_BWD_DQ_SHORT_GRID 256
+#endif
+constexpr int64_t kDqShortGrid = FA_BWD_DQ_SHORT_GRID;
 
 // logsumexp in exp2 units; a row without a visible key (LSE = -inf) gets +inf
 // so that every weight exp2(s c - lse2) is 0 instead of inf.
@@ -490,11 +494,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDk
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (query head, kDqRows queries)
 // ---------------------------------------------------------------------------
-template <bool BF16, bool CAUSAL, int D>
+// QB_: 32-row query blocks per wave (kDqBlocks by default; one for the short
+// d = 64 grids below).
+template <bool BF16, bool CAUSAL, int D, int QB_ = kDqBlocks<D>>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(kDqWaves<D>))) void bwd_dq_kernel(BwdArgs a, int n_qt, int total) {
   using HH = Half<BF16>;
-  constexpr int QB = kDqBlocks<D>;
-  constexpr int kRows = kDqRows<D>;
+  constexpr int QB = QB_;
+  constexpr int kRows = 32 * kBwdWaves * QB;
   // K and V tiles loaded HBM -> LDS directly into three stages of unpadded
   // swizzled rows (row_swz)
   constexpr int kTileElems = kBT * D;
@@ -823,13 +829,21 @@ hipError_t launch_bwd(const BwdArgs& a, const void* o, float* delta, hipStream_t
       if (e != hipSuccess) return e;
     }
   }
-  // dQ over the query heads' row tiles (zero when there are no keys)
+  // dQ over the query heads' row tiles (zero when there are no keys).  A
+  // d = 64 grid of fewer than kDqShortGrid 256-row workgroups takes 128-row
+  // ones (one block per wave), twice as many.
   int n_qt = (a.nq + kDqRows<D> - 1) / kDqRows<D>;
+  const void* dq_fn = (const void*)&bwd_dq_kernel<BF16, CAUSAL, D>;
+  if constexpr (D == 64 && kDqBlocks<D> == 2) {
+    if ((int64_t)n_qt * a.bh < kDqShortGrid) {
+      n_qt = (a.nq + 32 * kBwdWaves - 1) / (32 * kBwdWaves);
+      dq_fn = (const void*)&bwd_dq_kernel<BF16, CAUSAL, D, 1>;
+    }
+  }
   int total_q = (int)((int64_t)n_qt * a.bh);
   if (total_q > 0) {
     void* p2[] = {&args, &n_qt, &total_q};
-    e = hipLaunchKernel((const void*)&bwd_dq_kernel<BF16, CAUSAL, D>, dim3(total_q),
-                        dim3(kBwdThreads), p2, 0, s);
+    e = hipLaunchKernel(dq_fn, dim3(total_q), dim3(kBwdThreads), p2, 0, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
