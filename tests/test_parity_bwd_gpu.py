@@ -137,6 +137,24 @@ def test_bwd_small_shapes(dtype, d, causal):
             assert_grad_close(got, ref, dtype, f"N={n} {name}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_d64_dq_short_grid_switch(dtype, causal):
+    # d = 64 dQ grids of fewer than 256 workgroups of 256 rows take 128-row
+    # workgroups (one 32-row block per wave).  Both sides of the switch
+    # (255 and 256 problems of one block), multi-block heads on the short
+    # side, ragged tails.
+    for i, (B, H, n) in enumerate(((1, 255, 40), (1, 256, 40), (3, 5, 700), (1, 1, 129))):
+        w = Workload("case", dtype, B, H, n, 64, causal, 1350 + i)
+        q, k, v = make_inputs(w)
+        dout = upstream(w, 1360 + i)
+        _note(f"bwd dQ short grid {dtype} causal={causal} B={B} H={H} N={n}")
+        dq, dk, dv = run_bwd(w, q, k, v, dout)
+        rq, rk, rv = oracle.bwd(q, k, v, dout, w.scale, causal)
+        for got, ref, name in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+            assert_grad_close(got, ref, dtype, f"B={B} H={H} N={n} {name}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_bwd_large_logits(dtype):
     # scores with std ~ 9: most weights are tiny, a few dominate each row
