@@ -1,6 +1,6 @@
 """Seeded random shapes through the extended entry points (MI355X only).
 
-Forty cases drawn from a fixed seed over everything the extended calls
+Eighty cases drawn from two fixed seeds over everything the extended calls
 combine: element type, head size, causal mask, batch, grouped K/V heads,
 query and key lengths (one query row, more queries than keys, lengths off
 every tile size), key ranges of the forward split and head parts of the
@@ -44,7 +44,9 @@ def draw_cases(count=40, seed=20240611):
     return cases
 
 
-CASES = draw_cases()
+# Two fixed draws of forty: the second spans the same space with other
+# shapes (among them the short-grid tiles' switches).
+CASES = draw_cases() + [(40 + c[0],) + c[1:] for c in draw_cases(40, seed=777001)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"case{c[0]}" for c in CASES])
